@@ -1,0 +1,119 @@
+"""The C-ABI library loads, exports every declared symbol, and its pure host
+functions and argument validation behave as declared (no GPU needed: every
+call here returns before any device work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from trellis_quantized_linear_had_amd import _lib as X
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "exl3.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    decl = declared_functions()
+    assert set(decl) == set(X.EXPORTS), decl
+    L = X.lib()
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_padded_width_rule():
+    assert X.lib().logits_padded_width(248077, 248320) == 248192
+    assert X.lib().logits_padded_width(256, 1000) == 256
+    assert X.lib().logits_padded_width(257, 300) == 300
+    assert X.lib().logits_padded_width(0, 10) == -1
+    assert X.lib().logits_padded_width(11, 10) == -1
+
+
+def test_scratch_sizes():
+    L = X.lib()
+    # Wide projection: fp16 rotated input (M x K) + one 32768-column fp16 slice of W.
+    wide = L.exl3_linear_scratch_bytes(5120, 32768, 2048, 128)
+    assert wide == 2048 * 5120 * 2 + 5120 * 32768 * 2
+    assert 5120 * 32768 * 2 == 335544320  # the 336 MB bound of the pages' 32768-column slicing
+    # N above one slice still holds a single slice
+    assert L.exl3_linear_scratch_bytes(128, 33024, 128, 128) == 128 * 128 * 2 + 32768 * 128 * 2
+    # decode path is used below the threshold and when the threshold is 0
+    d = L.exl3_linear_scratch_bytes(5120, 17408, 16, 128)
+    assert d == L.exl3_linear_scratch_bytes(5120, 17408, 16, 0)
+    assert d > 16 * 5120 * 2
+    # M at the threshold takes the prefill path: rotated input + the whole 17408-column slice
+    assert L.exl3_linear_scratch_bytes(5120, 17408, 16, 16) == 16 * 5120 * 2 + 17408 * 5120 * 2
+    assert L.exl3_linear_scratch_bytes(100, 128, 1, 128) == 0
+    assert L.exl3_linear_scratch_bytes(128, 128, 0, 128) == 0
+    assert L.logits_scratch_bytes(16, 248077, 248320) > 0
+    assert L.logits_scratch_bytes(16, 0, 10) == 0
+
+
+def _layer(K=256, N=256, bits=4, codes=0x1000, cb=0x2000, scale=0x3000):
+    return X.Exl3Layer(codes, cb, scale, None, None, K, N, bits)
+
+
+def _linear(layer, x=0x4000, M=1, y=0x5000, scratch=0x6000, nbytes=1 << 30, pm=128):
+    return X.lib().exl3_linear(ctypes.byref(layer), x, M, y, scratch, nbytes, pm, None)
+
+
+@pytest.mark.parametrize("layer,status", [
+    (_layer(K=100), X.EXL3_ESHAPE),
+    (_layer(N=130), X.EXL3_ESHAPE),
+    (_layer(bits=3), X.EXL3_ESHAPE),
+    (_layer(codes=0), X.EXL3_EINVAL),
+    (_layer(cb=0), X.EXL3_EINVAL),
+    (_layer(codes=0x1004), X.EXL3_EINVAL),
+])
+def test_linear_rejects_bad_layers(layer, status):
+    assert _linear(layer) == status
+    assert X.lib().exl3_strerror(status)
+
+
+def test_linear_rejects_bad_calls():
+    good = _layer()
+    assert _linear(good, M=-1) == X.EXL3_EINVAL
+    assert _linear(good, M=0) == X.EXL3_OK            # no-op
+    assert _linear(good, x=0) == X.EXL3_EINVAL
+    assert _linear(good, scratch=0) == X.EXL3_EINVAL
+    assert _linear(good, scratch=0x6010) == X.EXL3_EINVAL   # scratch must be 256-byte aligned
+    need = X.lib().exl3_linear_scratch_bytes(256, 256, 1, 128)
+    assert _linear(good, nbytes=need - 1) == X.EXL3_ESCRATCH
+    assert b"needs" in X.lib().exl3_strerror(X.EXL3_ESCRATCH)
+    assert _linear(good, pm=-1) == X.EXL3_EINVAL
+
+
+def test_reconstruct_and_had_validation():
+    L = X.lib()
+    lay = _layer()
+    assert L.exl3_reconstruct(ctypes.byref(lay), 8, 16, 0x7000, 16, 0, None) == X.EXL3_ESHAPE   # misaligned slice
+    assert L.exl3_reconstruct(ctypes.byref(lay), 0, 272, 0x7000, 272, 0, None) == X.EXL3_ESHAPE  # beyond N
+    assert L.exl3_reconstruct(ctypes.byref(lay), 0, 16, 0x7000, 8, 0, None) == X.EXL3_ESHAPE    # ldw < n_count
+    assert L.exl3_reconstruct(ctypes.byref(lay), 0, 16, 0x7000, 128, 1, None) == X.EXL3_ESHAPE  # NK: ldw < K
+    assert L.exl3_reconstruct(ctypes.byref(lay), 0, 16, 0x7000, 16, 5, None) == X.EXL3_EINVAL   # layout
+    assert L.exl3_reconstruct(ctypes.byref(lay), 0, 0, 0x7000, 16, 0, None) == X.EXL3_OK        # empty slice
+    assert L.had_r_128(0x1000, 0x2000, 4, 100, None, None, None) == X.EXL3_ESHAPE
+    assert L.had_r_128(0x1000, 0x2000, -1, 128, None, None, None) == X.EXL3_EINVAL
+    assert L.had_r_128(0, 0x2000, 4, 128, None, None, None) == X.EXL3_EINVAL
+    assert L.had_r_128(0x1000, 0x2000, 0, 128, None, None, None) == X.EXL3_OK
+
+
+def test_logits_validation():
+    L = X.lib()
+
+    def call(M=1, K=256, w_rows=300, n_valid=257, ld=300, nbytes=1 << 20, x=0x1000):
+        return L.logits_pad_mask_argmax(x, M, K, 0x2000, w_rows, n_valid, 0x3000, ld, 0x4000, 0x5000, nbytes, None)
+
+    assert call(n_valid=0) == X.EXL3_EWIDTH
+    assert call(n_valid=301) == X.EXL3_EWIDTH
+    assert call(ld=299) == X.EXL3_EWIDTH
+    assert call(K=200) == X.EXL3_ESHAPE
+    assert call(M=-1) == X.EXL3_EINVAL
+    assert call(x=0) == X.EXL3_EINVAL
+    assert call(nbytes=0) == X.EXL3_ESCRATCH
+    assert call(M=0) == X.EXL3_OK

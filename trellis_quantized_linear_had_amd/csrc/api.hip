@@ -1,0 +1,355 @@
+// Host side of libexl3: argument validation (fail closed, before any launch),
+// the row-count dispatch between the fused decode path and the prefill path
+// (vLLM PR #316, "Change": the branch sits inside the op and is taken at call
+// time; threshold 128 by default, 0 disables the prefill path), the
+// <= 32768-column slice loop over one caller-owned scratch buffer, and status
+// reporting. No allocation, host synchronisation, environment read or timing
+// search happens in any call (vLLM PR #314, "Problem": a lazily allocated
+// buffer on first call breaks graph capture).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/exl3.h"
+#include "decode_plan.h"
+
+namespace exl3 {
+hipError_t launch_had128(const uint16_t* in, uint16_t* out, int64_t rows, int64_t cols, const uint16_t* sign_pre,
+                         const uint16_t* sign_post, hipStream_t stream);
+hipError_t launch_reconstruct_nk(const uint32_t* codes, const uint16_t* cb, const uint16_t* scale, int32_t K,
+                                 int32_t N, int32_t n0, int32_t n_count, uint16_t* wt, int64_t ldw, hipStream_t stream);
+hipError_t launch_reconstruct_kn(const uint32_t* codes, const uint16_t* cb, const uint16_t* scale, int32_t K,
+                                 int32_t N, int32_t n0, int32_t n_count, uint16_t* w, int64_t ldw, bool states,
+                                 hipStream_t stream);
+hipError_t launch_decode_gemm(const uint16_t* xr, const uint32_t* codes, const uint16_t* cb, float* partials,
+                              int32_t K, int32_t N, int32_t M, const DecodePlan& plan, hipStream_t stream);
+hipError_t launch_decode_finalize(const float* partials, int32_t ks_count, const uint16_t* scale,
+                                  const uint16_t* sign_n, uint16_t* y, int32_t M, int32_t N, hipStream_t stream);
+hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
+                           int64_t ldy, int32_t n0, const uint16_t* sign_n, hipStream_t stream);
+hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int64_t n_valid, int64_t n_pad,
+                         uint16_t* logits, int64_t ld, int64_t* argmax, float* pv, int32_t* pi, hipStream_t stream);
+int64_t logits_items(int64_t n_pad);
+}  // namespace exl3
+
+using namespace exl3;
+
+namespace {
+
+thread_local char g_msg[512];
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(EXL3_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define EXL3_TRY(call, where)                  \
+  do {                                         \
+    hipError_t e_ = (call);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+// Device architecture check, cached per device (a result, not tuning state).
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(EXL3_EARCH, "device index %d out of range", dev);
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(EXL3_EARCH, "device %d is not gfx950", dev);
+  return EXL3_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int validate_layer(const exl3_layer* L) {
+  if (!L) return fail(EXL3_EINVAL, "layer is NULL");
+  if (!L->codes || !L->codebook || !L->scale) return fail(EXL3_EINVAL, "layer codes, codebook or scale is NULL");
+  if (L->bits != 4) return fail(EXL3_ESHAPE, "bits = %d; only 4 bits per weight is supported", L->bits);
+  if (L->K <= 0 || L->N <= 0 || L->K % 128 || L->N % 128)
+    return fail(EXL3_ESHAPE, "K = %d and N = %d must be positive multiples of 128", L->K, L->N);
+  if (!aligned16(L->codes) || !aligned16(L->codebook) || !aligned16(L->scale) || !aligned16(L->sign_k) ||
+      !aligned16(L->sign_n))
+    return fail(EXL3_EINVAL, "layer tensors must be 16-byte aligned");
+  return EXL3_OK;
+}
+
+bool use_prefill(int64_t M, int32_t prefill_min_m) { return prefill_min_m > 0 && M >= prefill_min_m; }
+
+// Work decomposition of the fused decode path: choose workgroup and wave
+// grids that give every workgroup the same number of tiles and keep the
+// split-K partial traffic small. Cost model in GPU clocks: a 16-column x
+// 32-row tile costs ~60 clocks of the LDS gather pipe per CU; the slowest
+// wave sets the time of its workgroup; partials are written and read once.
+DecodePlan plan_decode(int32_t K, int32_t N, int64_t M) {
+  const int ksteps = K / 32, ntiles = N / 16;
+  const int64_t mgroups = (M + 15) / 16;
+  DecodePlan best{1, 1, ksteps, 1, 1, 8};
+  double best_cost = 1e300;
+  const int wns[4] = {1, 2, 4, 8};
+  for (int wi = 0; wi < 4; ++wi) {
+    const int wn = wns[wi], wk = 8 / wn;
+    for (int ks = 1; ks <= std::min(ksteps, 64); ++ks) {
+      const int kpw = (ksteps + ks - 1) / ks;
+      if ((int64_t)(ks - 1) * kpw >= ksteps) continue;
+      const int kpw_wave = (kpw + wk - 1) / wk;
+      for (int npw = 1; npw * wn <= DEC_NT_MAX; ++npw) {
+        const int ntpw = npw * wn;
+        const int ns = (ntiles + ntpw - 1) / ntpw;
+        const int ntpw_real = (ntiles + ns - 1) / ns;
+        const int per_wave_n = (ntpw_real + wn - 1) / wn;
+        const int64_t wgs = (int64_t)ks * ns;
+        const int64_t rounds = (wgs + 255) / 256;
+        const double decode = (double)rounds * 8.0 * kpw_wave * per_wave_n * 60.0 * mgroups;
+        const double partial = (double)ks * M * N * 8.0 / 2083.0;
+        const double cost = decode + partial;
+        if (cost < best_cost - 1e-9) {
+          best_cost = cost;
+          best = DecodePlan{ks, ns, kpw, ntpw_real, wn, wk};
+        }
+      }
+    }
+  }
+  return best;
+}
+
+struct PrefillLayout {
+  size_t xr_off, w_off, total;
+  int32_t chunk;
+};
+struct DecodeLayout {
+  size_t xr_off, part_off, total;
+  DecodePlan plan;
+};
+
+PrefillLayout prefill_layout(int32_t K, int32_t N, int64_t M) {
+  PrefillLayout l;
+  l.chunk = std::min<int32_t>(N, EXL3_MAX_CHUNK_COLS);
+  l.xr_off = 0;
+  l.w_off = align256((size_t)M * K * 2);
+  l.total = l.w_off + align256((size_t)l.chunk * K * 2);
+  return l;
+}
+
+// plan_decode is a pure function of (K, N, M); a small per-thread memo keeps
+// its search off the per-call host path.
+DecodePlan plan_decode_cached(int32_t K, int32_t N, int64_t M) {
+  struct Entry {
+    int32_t K, N;
+    int64_t M;
+    DecodePlan plan;
+  };
+  thread_local Entry memo[16];
+  thread_local int used = 0, next = 0;
+  for (int i = 0; i < used; ++i)
+    if (memo[i].K == K && memo[i].N == N && memo[i].M == M) return memo[i].plan;
+  const DecodePlan p = plan_decode(K, N, M);
+  memo[next] = Entry{K, N, M, p};
+  next = (next + 1) % 16;
+  if (used < 16) ++used;
+  return p;
+}
+
+DecodeLayout decode_layout(int32_t K, int32_t N, int64_t M) {
+  DecodeLayout l;
+  l.plan = plan_decode_cached(K, N, M);
+  l.xr_off = 0;
+  l.part_off = align256((size_t)M * K * 2);
+  l.total = l.part_off + align256((size_t)l.plan.ks_count * M * N * 4);
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* exl3_strerror(int status) {
+  switch (status) {
+    case EXL3_OK:
+      return "ok";
+    case EXL3_EINVAL:
+    case EXL3_ESHAPE:
+    case EXL3_ESCRATCH:
+    case EXL3_EWIDTH:
+    case EXL3_EHIP:
+    case EXL3_EARCH:
+      return g_msg[0] ? g_msg : "error";
+    default:
+      return "unknown status";
+  }
+}
+
+size_t exl3_linear_scratch_bytes(int32_t K, int32_t N, int64_t M, int32_t prefill_min_m) {
+  if (K <= 0 || N <= 0 || K % 128 || N % 128 || M < 0) return 0;
+  if (M == 0) return 0;
+  return use_prefill(M, prefill_min_m) ? prefill_layout(K, N, M).total : decode_layout(K, N, M).total;
+}
+
+int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* scratch, size_t scratch_bytes,
+                int32_t prefill_min_m, void* stream_) {
+  g_msg[0] = 0;
+  int st = validate_layer(L);
+  if (st) return st;
+  if (M < 0) return fail(EXL3_EINVAL, "M = %lld is negative", (long long)M);
+  if (prefill_min_m < 0) return fail(EXL3_EINVAL, "prefill_min_m = %d is negative", prefill_min_m);
+  if (M > 0x7FFFFFFF) return fail(EXL3_EINVAL, "M = %lld is too large", (long long)M);
+  if (M == 0) return EXL3_OK;
+  if (!x || !y) return fail(EXL3_EINVAL, "x or y is NULL");
+  if (!scratch) return fail(EXL3_EINVAL, "scratch is NULL");
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)scratch & 255u))
+    return fail(EXL3_EINVAL, "x and y must be 16-byte aligned and scratch 256-byte aligned");
+  const int32_t K = L->K, N = L->N;
+  const size_t need = exl3_linear_scratch_bytes(K, N, M, prefill_min_m);
+  if (scratch_bytes < need)
+    return fail(EXL3_ESCRATCH, "scratch has %zu bytes; this call needs %zu", scratch_bytes, need);
+  st = check_device();
+  if (st) return st;
+  hipStream_t stream = (hipStream_t)stream_;
+  char* sb = (char*)scratch;
+
+  if (use_prefill(M, prefill_min_m)) {
+    const PrefillLayout l = prefill_layout(K, N, M);
+    uint16_t* xr = (uint16_t*)(sb + l.xr_off);
+    uint16_t* wt = (uint16_t*)(sb + l.w_off);
+    EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
+    for (int32_t n0 = 0; n0 < N; n0 += l.chunk) {
+      const int32_t nc = std::min(l.chunk, N - n0);
+      EXL3_TRY(launch_reconstruct_nk(L->codes, L->codebook, L->scale, K, N, n0, nc, wt, K, stream), "reconstruct");
+      EXL3_TRY(launch_gemm_had(wt, xr, y, nc, (int32_t)M, K, N, n0, L->sign_n, stream), "gemm");
+    }
+  } else {
+    const DecodeLayout l = decode_layout(K, N, M);
+    uint16_t* xr = (uint16_t*)(sb + l.xr_off);
+    float* part = (float*)(sb + l.part_off);
+    EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
+    EXL3_TRY(launch_decode_gemm(xr, L->codes, L->codebook, part, K, N, (int32_t)M, l.plan, stream), "decode gemm");
+    EXL3_TRY(launch_decode_finalize(part, l.plan.ks_count, L->scale, L->sign_n, y, (int32_t)M, N, stream),
+             "decode finalize");
+  }
+  return EXL3_OK;
+}
+
+int exl3_reconstruct(const exl3_layer* L, int32_t n0, int32_t n_count, uint16_t* w, int64_t ldw, int32_t layout,
+                     void* stream_) {
+  g_msg[0] = 0;
+  int st = validate_layer(L);
+  if (st) return st;
+  if (!w) return fail(EXL3_EINVAL, "w is NULL");
+  if (n0 < 0 || n_count < 0 || n0 % 16 || n_count % 16 || (int64_t)n0 + n_count > L->N)
+    return fail(EXL3_ESHAPE, "slice [%d, %d + %d) must be 16-aligned and inside N = %d", n0, n0, n_count, L->N);
+  if (layout != EXL3_LAYOUT_KN && layout != EXL3_LAYOUT_NK) return fail(EXL3_EINVAL, "unknown layout %d", layout);
+  const int64_t minld = layout == EXL3_LAYOUT_KN ? n_count : L->K;
+  if (ldw < minld || ldw % 8) return fail(EXL3_ESHAPE, "ldw = %lld must be >= %lld and a multiple of 8",
+                                          (long long)ldw, (long long)minld);
+  if (!aligned16(w)) return fail(EXL3_EINVAL, "w must be 16-byte aligned");
+  if (n_count == 0) return EXL3_OK;
+  st = check_device();
+  if (st) return st;
+  hipStream_t stream = (hipStream_t)stream_;
+  if (layout == EXL3_LAYOUT_NK)
+    EXL3_TRY(launch_reconstruct_nk(L->codes, L->codebook, L->scale, L->K, L->N, n0, n_count, w, ldw, stream),
+             "reconstruct");
+  else
+    EXL3_TRY(launch_reconstruct_kn(L->codes, L->codebook, L->scale, L->K, L->N, n0, n_count, w, ldw, false, stream),
+             "reconstruct");
+  return EXL3_OK;
+}
+
+int exl3_decode_states(const exl3_layer* L, uint16_t* states, void* stream_) {
+  g_msg[0] = 0;
+  if (!L || !L->codes) return fail(EXL3_EINVAL, "layer or codes is NULL");
+  if (L->K <= 0 || L->N <= 0 || L->K % 128 || L->N % 128)
+    return fail(EXL3_ESHAPE, "K = %d and N = %d must be positive multiples of 128", L->K, L->N);
+  if (!states || !aligned16(states) || !aligned16(L->codes)) return fail(EXL3_EINVAL, "states NULL or misaligned");
+  int st = check_device();
+  if (st) return st;
+  EXL3_TRY(launch_reconstruct_kn(L->codes, nullptr, nullptr, L->K, L->N, 0, L->N, states, L->N, true,
+                                 (hipStream_t)stream_),
+           "decode states");
+  return EXL3_OK;
+}
+
+int had_r_128(const uint16_t* in, uint16_t* out, int64_t rows, int64_t cols, const uint16_t* sign_pre,
+              const uint16_t* sign_post, void* stream_) {
+  g_msg[0] = 0;
+  if (rows < 0 || cols < 0) return fail(EXL3_EINVAL, "rows = %lld, cols = %lld", (long long)rows, (long long)cols);
+  if (cols % 128) return fail(EXL3_ESHAPE, "cols = %lld is not a multiple of 128", (long long)cols);
+  if (rows == 0 || cols == 0) return EXL3_OK;
+  if (!in || !out) return fail(EXL3_EINVAL, "in or out is NULL");
+  if (!aligned16(in) || !aligned16(out) || !aligned16(sign_pre) || !aligned16(sign_post))
+    return fail(EXL3_EINVAL, "tensors must be 16-byte aligned");
+  int st = check_device();
+  if (st) return st;
+  EXL3_TRY(launch_had128(in, out, rows, cols, sign_pre, sign_post, (hipStream_t)stream_), "had_r_128");
+  return EXL3_OK;
+}
+
+int64_t logits_padded_width(int64_t n_valid, int64_t w_rows) {
+  if (n_valid < 1 || n_valid > w_rows) return -1;
+  const int64_t aligned = (n_valid + 127) / 128 * 128;
+  return std::min(aligned, w_rows);
+}
+
+size_t logits_scratch_bytes(int64_t M, int64_t n_valid, int64_t w_rows) {
+  const int64_t n_pad = logits_padded_width(n_valid, w_rows);
+  if (n_pad < 0 || M < 0) return 0;
+  const int64_t items = logits_items(n_pad);
+  return align256((size_t)items * M * 4) * 2;
+}
+
+int logits_pad_mask_argmax(const uint16_t* x, int64_t M, int32_t K, const uint16_t* w, int64_t w_rows,
+                           int64_t n_valid, uint16_t* logits, int64_t ld_logits, int64_t* argmax, void* scratch,
+                           size_t scratch_bytes, void* stream_) {
+  g_msg[0] = 0;
+  if (M < 0 || w_rows < 0) return fail(EXL3_EINVAL, "M = %lld, w_rows = %lld", (long long)M, (long long)w_rows);
+  if (M > 0x7FFFFFFF || w_rows > 0x7FFFFFFF) return fail(EXL3_EINVAL, "M or w_rows too large");
+  if (K <= 0 || K % 128) return fail(EXL3_ESHAPE, "K = %d must be a positive multiple of 128", K);
+  const int64_t n_pad = logits_padded_width(n_valid, w_rows);
+  if (n_pad < 0)
+    return fail(EXL3_EWIDTH, "n_valid = %lld must be in [1, w_rows = %lld]", (long long)n_valid, (long long)w_rows);
+  if (ld_logits < n_pad)
+    return fail(EXL3_EWIDTH, "ld_logits = %lld is below the padded width %lld", (long long)ld_logits,
+                (long long)n_pad);
+  if (M == 0) return EXL3_OK;
+  if (!x || !w || !logits || !argmax || !scratch) return fail(EXL3_EINVAL, "a required pointer is NULL");
+  if (!aligned16(x) || !aligned16(w) || ((uintptr_t)logits & 1) || ((uintptr_t)argmax & 7) ||
+      ((uintptr_t)scratch & 255u))
+    return fail(EXL3_EINVAL, "misaligned pointer");
+  const size_t need = logits_scratch_bytes(M, n_valid, w_rows);
+  if (scratch_bytes < need)
+    return fail(EXL3_ESCRATCH, "scratch has %zu bytes; this call needs %zu", scratch_bytes, need);
+  int st = check_device();
+  if (st) return st;
+  const int64_t items = logits_items(n_pad);
+  float* pv = (float*)scratch;
+  int32_t* pi = (int32_t*)((char*)scratch + align256((size_t)items * M * 4));
+  EXL3_TRY(launch_logits(x, (int32_t)M, K, w, n_valid, n_pad, logits, ld_logits, argmax, pv, pi,
+                         (hipStream_t)stream_),
+           "logits");
+  return EXL3_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,189 @@
+// Fused trellis decode-GEMM for decode-shaped calls (vLLM PR #316, summary and
+// "Problem": the fused kernel decodes the trellis once per output tile, so its
+// cost grows with the row count; it serves every call below the threshold).
+//
+// Yr = Xr . W with W decoded on the fly. One workgroup per CU (the 128 KiB
+// codebook fills most of the 160 KiB LDS); the K x N weight grid is cut into
+// ks_count x ns_count rectangles, one per workgroup, so every workgroup decodes
+// the same number of tiles. Inside a workgroup the 8 waves form a wn x wk grid
+// over (n-tiles, k-steps). Each lane decodes 8 consecutive k of one column and
+// feeds them straight into v_mfma_f32_16x16x32_f16 as the B operand (the rows
+// of Xr are the A operand, padded to 16). Waves that share n-tiles are summed
+// in LDS in a fixed order; each workgroup writes one fp32 partial per output,
+// and the finalize kernel sums the ks_count partials in order, applies the
+// column scale and the output rotation. No float atomics: bit-identical
+// results run to run.
+//
+// The bound is the codebook gather rate of the LDS (one random 16-bit read
+// per weight), not HBM: the packed codes are 0.5 byte per weight.
+#include "common.h"
+#include "decode_plan.h"
+#include "trellis.h"
+
+namespace exl3 {
+
+#define DEC_THREADS 512
+#define DEC_WAVES 8
+
+__global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t* __restrict__ xr,
+                                                                  const uint32_t* __restrict__ codes,
+                                                                  const uint16_t* __restrict__ cb,
+                                                                  float* __restrict__ partials, int32_t K,
+                                                                  int32_t N, int32_t M, DecodePlan plan) {
+  __shared__ uint16_t cb_lds[65536];
+  __shared__ float red[DEC_NT_MAX * 256];
+
+  const int ksteps_total = K / 32, ntiles_total = N / 16;
+  const int ks = blockIdx.x / plan.ns_count, ns = blockIdx.x % plan.ns_count;
+  const int s_begin = ks * plan.ksteps_per_wg;
+  const int s_end = min(s_begin + plan.ksteps_per_wg, ksteps_total);
+  const int t_begin = ns * plan.ntiles_per_wg;
+  const int t_end = min(t_begin + plan.ntiles_per_wg, ntiles_total);
+  if (s_begin >= s_end || t_begin >= t_end) return;  // whole workgroup idle (uniform)
+
+  load_codebook<DEC_THREADS>(cb_lds, cb);
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wn_idx = wave % plan.wn, wk_idx = wave / plan.wn;
+  const int tw = t_end - t_begin;
+  const int per_n = (tw + plan.wn - 1) / plan.wn;
+  const int wt_begin = t_begin + min(wn_idx * per_n, tw);
+  const int nt_w = min(wt_begin + per_n, t_end) - wt_begin;
+  const int sw = s_end - s_begin;
+  const int per_k = (sw + plan.wk - 1) / plan.wk;
+  const int ws_begin = s_begin + min(wk_idx * per_k, sw);
+  const int ws_end = min(ws_begin + per_k, s_end);
+
+  // Lane roles in the 16x16x32 MFMA: A row (= x row) and B column (= n) are
+  // lane & 15; the 8-element k slice is lane >> 4: k-tile (lane >> 5) of the
+  // step, half (lane >> 4) & 1 of that tile's 16 rows.
+  const int c = lane & 15;
+  const int ktile_in_step = lane >> 5;
+  const int d = 2 * c + ((lane >> 4) & 1);  // first code word of the lane's windows
+  const int d1 = (d + 1) & 31;
+
+  for (int m0 = 0; m0 < M; m0 += 16) {
+    f32x4 acc[DEC_NT_MAX];
+#pragma unroll
+    for (int t = 0; t < DEC_NT_MAX; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    const int mrow = m0 + c;
+    const uint16_t* xrow = xr + (int64_t)mrow * K + 8 * (lane >> 4);
+    for (int step = ws_begin; step < ws_end; ++step) {
+      f16x8 a = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+      if (mrow < M) a = *reinterpret_cast<const f16x8*>(xrow + 32 * step);
+      const uint32_t* trow = codes + ((int64_t)(2 * step + ktile_in_step) * ntiles_total + wt_begin) * 32;
+#pragma unroll
+      for (int t = 0; t < DEC_NT_MAX; ++t) {
+        if (t < nt_w) {
+          const uint32_t lo = trow[32 * t + d], hi = trow[32 * t + d1];
+          uint32_t off[8];
+          window_offsets8(lo, hi, off);
+          f16x8 b;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) b[j] = __builtin_bit_cast(f16, lds_cb(cb_lds, off[j]));
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+        }
+      }
+    }
+
+    // Fixed-order reduction over the wk waves that share these n-tiles.
+    // D layout of the MFMA: lane holds rows 4*(lane>>4) + r, column lane & 15.
+    const int rbase = (wt_begin - t_begin) * 256 + 4 * (lane >> 4) * 16 + c;
+    for (int j = 0; j < plan.wk; ++j) {
+      if (wk_idx == j) {
+#pragma unroll
+        for (int t = 0; t < DEC_NT_MAX; ++t) {
+          if (t < nt_w) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float* p = &red[rbase + t * 256 + r * 16];
+              *p = (j == 0) ? acc[t][r] : *p + acc[t][r];
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+    // partials[ks][m][n]
+    for (int idx = threadIdx.x; idx < tw * 256; idx += DEC_THREADS) {
+      const int t = idx >> 8, e = idx & 255, m = m0 + (e >> 4), n = (t_begin + t) * 16 + (e & 15);
+      if (m < M) partials[((int64_t)ks * M + m) * N + n] = red[idx];
+    }
+    __syncthreads();
+  }
+}
+
+// y[m][128b + i] = fp16(sign_n * (1/sqrt128) * sum_j H[i][j] * scale[n_j] *
+//                       sum_ks partials[ks][m][n_j]); an aligned quad of lanes
+// per 128-column block, as in the Hadamard kernel.
+__global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __restrict__ partials, int32_t ks_count,
+                                                              const uint16_t* __restrict__ scale,
+                                                              const uint16_t* __restrict__ sign_n,
+                                                              uint16_t* __restrict__ y, int32_t M, int32_t N) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q = (int)(gid & 3);
+  const int64_t nblocks = (int64_t)M * (N / 128);
+  const int64_t blk_raw = gid >> 2;
+  const int64_t blk = blk_raw < nblocks ? blk_raw : nblocks - 1;
+  const int64_t m = blk / (N / 128);
+  const int64_t n0 = (blk % (N / 128)) * 128 + 32 * q;
+
+  float v[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) v[e] = 0.f;
+  for (int ks = 0; ks < ks_count; ++ks) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(partials + ((int64_t)ks * M + m) * N + n0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 p = src[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * i + j] += p[j];
+    }
+  }
+  const u32x4* sc = reinterpret_cast<const u32x4*>(scale + n0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 s = sc[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] *= bits_lo_f16(s[j]);
+      v[8 * i + 2 * j + 1] *= bits_hi_f16(s[j]);
+    }
+  }
+  wht128_quad(v, q);
+  u32x4 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[i][j] = pack_f16x2(v[8 * i + 2 * j] * EXL3_INV_SQRT128, v[8 * i + 2 * j + 1] * EXL3_INV_SQRT128);
+  if (sign_n) {
+    const u32x4* sq = reinterpret_cast<const u32x4*>(sign_n + n0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] ^= (sq[i] & 0x80008000u);
+  }
+  if (blk_raw < nblocks) {
+    u32x4* dst = reinterpret_cast<u32x4*>(y + m * N + n0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = o[i];
+  }
+}
+
+hipError_t launch_decode_gemm(const uint16_t* xr, const uint32_t* codes, const uint16_t* cb, float* partials,
+                              int32_t K, int32_t N, int32_t M, const DecodePlan& plan, hipStream_t stream) {
+  decode_gemm_kernel<<<plan.ks_count * plan.ns_count, DEC_THREADS, 0, stream>>>(xr, codes, cb, partials, K, N, M,
+                                                                               plan);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_finalize(const float* partials, int32_t ks_count, const uint16_t* scale,
+                                  const uint16_t* sign_n, uint16_t* y, int32_t M, int32_t N, hipStream_t stream) {
+  const int64_t threads = (int64_t)M * (N / 128) * 4;
+  decode_finalize_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(partials, ks_count, scale, sign_n,
+                                                                                y, M, N);
+  return hipGetLastError();
+}
+
+}  // namespace exl3
