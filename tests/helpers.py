@@ -38,6 +38,25 @@ def ulp_diff(a_u16, b_u16) -> np.ndarray:
     return np.abs(ordered(a) - ordered(b))
 
 
+def ulp16(ref_u16) -> np.ndarray:
+    """Spacing of fp16 values at |ref| (2^-24 in the subnormal range)."""
+    v = np.abs(val(ref_u16))
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -14)))
+    return np.exp2(e - 10)
+
+
+def assert_logits_close(lg_u16, ref_u16, K: int):
+    """fp16 logits from fp32 accumulation against the fp64 oracle: one fp16
+    rounding step plus the worst-case fp32 accumulation error over K terms,
+    with partial sums bounded by the row's largest logit."""
+    g, r = val(lg_u16), val(ref_u16)
+    assert np.all(np.isfinite(g))
+    rowmax = np.max(np.abs(r), axis=1, keepdims=True)
+    tol = ulp16(ref_u16) + K * 2.0 ** -24 * rowmax
+    bad = np.abs(g - r) > tol
+    assert not np.any(bad), (np.argwhere(bad)[:5], g[bad][:5], r[bad][:5])
+
+
 def require_gpu():
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():

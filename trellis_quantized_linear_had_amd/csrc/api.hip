@@ -14,7 +14,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/exl3.h"
+#include "exl3.h"
 #include "decode_plan.h"
 
 namespace exl3 {
@@ -100,18 +100,20 @@ int validate_layer(const exl3_layer* L) {
 bool use_prefill(int64_t M, int32_t prefill_min_m) { return prefill_min_m > 0 && M >= prefill_min_m; }
 
 // Work decomposition of the fused decode path: choose workgroup and wave
-// grids that give every workgroup the same number of tiles and keep the
-// split-K partial traffic small. Cost model in GPU clocks: a 16-column x
-// 32-row tile costs ~60 clocks of the LDS gather pipe per CU; the slowest
-// wave sets the time of its workgroup; partials are written and read once.
+// grids (16 waves per workgroup) that give every workgroup the same number of
+// tiles and keep the split-K partial traffic small. Cost model in GPU clocks:
+// a 16-column x 32-row tile costs ~60 clocks of the LDS gather pipe per CU;
+// the slowest wave sets the time of its workgroup; every round of workgroups
+// pays the 128 KiB codebook copy into LDS (~3000 clocks); partials are
+// written and read once.
 DecodePlan plan_decode(int32_t K, int32_t N, int64_t M) {
   const int ksteps = K / 32, ntiles = N / 16;
   const int64_t mgroups = (M + 15) / 16;
-  DecodePlan best{1, 1, ksteps, 1, 1, 8};
+  DecodePlan best{1, 1, ksteps, 1, 1, 16, 1};
   double best_cost = 1e300;
-  const int wns[4] = {1, 2, 4, 8};
-  for (int wi = 0; wi < 4; ++wi) {
-    const int wn = wns[wi], wk = 8 / wn;
+  const int wns[5] = {1, 2, 4, 8, 16};
+  for (int wi = 0; wi < 5; ++wi) {
+    const int wn = wns[wi], wk = 16 / wn;
     for (int ks = 1; ks <= std::min(ksteps, 64); ++ks) {
       const int kpw = (ksteps + ks - 1) / ks;
       if ((int64_t)(ks - 1) * kpw >= ksteps) continue;
@@ -121,14 +123,21 @@ DecodePlan plan_decode(int32_t K, int32_t N, int64_t M) {
         const int ns = (ntiles + ntpw - 1) / ntpw;
         const int ntpw_real = (ntiles + ns - 1) / ns;
         const int per_wave_n = (ntpw_real + wn - 1) / wn;
+        int nt_inst = 0;
+        for (int32_t v : kDecodeNtInstances)
+          if (v >= per_wave_n) {
+            nt_inst = v;
+            break;
+          }
+        if (nt_inst == 0) continue;
         const int64_t wgs = (int64_t)ks * ns;
         const int64_t rounds = (wgs + 255) / 256;
-        const double decode = (double)rounds * 8.0 * kpw_wave * per_wave_n * 60.0 * mgroups;
+        const double decode = (double)rounds * (16.0 * kpw_wave * nt_inst * 30.0 * mgroups + 3000.0);
         const double partial = (double)ks * M * N * 8.0 / 2083.0;
         const double cost = decode + partial;
         if (cost < best_cost - 1e-9) {
           best_cost = cost;
-          best = DecodePlan{ks, ns, kpw, ntpw_real, wn, wk};
+          best = DecodePlan{ks, ns, kpw, ntpw_real, wn, wk, nt_inst};
         }
       }
     }

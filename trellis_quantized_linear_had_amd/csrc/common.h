@@ -18,6 +18,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 namespace exl3 {
 
+// Buffer resource descriptor over [p, p + bytes): raw (untyped) 32-bit loads
+// with a wave-uniform scalar offset and a per-lane 32-bit offset. Third word:
+// the raw-buffer data format for gfx9-family parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t buffer_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff_bytes, uint32_t soff_bytes) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff_bytes, soff_bytes, 0);
+}
+
 __device__ __forceinline__ float bits_lo_f16(uint32_t w) {
   return (float)__builtin_bit_cast(f16, (uint16_t)(w & 0xFFFFu));
 }
@@ -67,6 +77,33 @@ __device__ __forceinline__ void wht128_quad(float (&v)[32], int q) {
     float p = quad_perm<EXL3_DPP_XOR2>(v[j]);
     v[j] = __builtin_fmaf(s2, v[j], p);
   }
+}
+
+// The same transform with 16 lanes per block: lane q (= lane & 15) holds
+// elements 8q .. 8q + 7. Index bits 0..2 live in registers, bits 3..6 in the
+// lane (partners q ^ 1, q ^ 2 by DPP, q ^ 4, q ^ 8 by swizzle).
+__device__ __forceinline__ void wht128_16(float (&v)[8], int q) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if ((j & h) == 0) {
+        float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+    }
+  }
+  const float s1 = (q & 1) ? -1.0f : 1.0f, s2 = (q & 2) ? -1.0f : 1.0f;
+  const float s4 = (q & 4) ? -1.0f : 1.0f, s8 = (q & 8) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s1, v[j], quad_perm<EXL3_DPP_XOR1>(v[j]));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s2, v[j], quad_perm<EXL3_DPP_XOR2>(v[j]));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s4, v[j], __shfl_xor(v[j], 4, 16));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s8, v[j], __shfl_xor(v[j], 8, 16));
 }
 
 }  // namespace exl3

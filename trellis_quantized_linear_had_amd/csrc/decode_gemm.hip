@@ -5,7 +5,7 @@
 // Yr = Xr . W with W decoded on the fly. One workgroup per CU (the 128 KiB
 // codebook fills most of the 160 KiB LDS); the K x N weight grid is cut into
 // ks_count x ns_count rectangles, one per workgroup, so every workgroup decodes
-// the same number of tiles. Inside a workgroup the 8 waves form a wn x wk grid
+// the same number of tiles. Inside a workgroup the 16 waves form a wn x wk grid
 // over (n-tiles, k-steps). Each lane decodes 8 consecutive k of one column and
 // feeds them straight into v_mfma_f32_16x16x32_f16 as the B operand (the rows
 // of Xr are the A operand, padded to 16). Waves that share n-tiles are summed
@@ -22,9 +22,65 @@
 
 namespace exl3 {
 
-#define DEC_THREADS 512
-#define DEC_WAVES 8
+#define DEC_THREADS 1024
+#define DEC_WAVES 16
 
+// Loads the code words of NT tiles of one k-step (two per lane: the lane's
+// windows start in word d and end in word d + 1, mod 32) and the A fragment.
+// The tile bases are wave-uniform (scalar registers); each lane adds a 32-bit
+// offset (its k-tile row and word).
+template <int NT>
+__device__ __forceinline__ void decode_load_step(__amdgpu_buffer_rsrc_t codes, int ntiles_total, int step,
+                                                 const int (&tbase)[NT], int loff, int loff1,
+                                                 const uint16_t* xrow, bool mok, uint32_t (&lo)[NT],
+                                                 uint32_t (&hi)[NT], f16x8& a) {
+  // The A fragment goes first: loads retire in order, so the MFMAs of the
+  // previous step (which need only that step's A fragment) never wait for
+  // this step's code words.
+  a = mok ? *reinterpret_cast<const f16x8*>(xrow + 32 * step) : (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+  const uint32_t row = (uint32_t)(2 * step) * ntiles_total * 128u;  // bytes
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    lo[t] = buffer_load_u32(codes, loff, row + tbase[t]);
+    hi[t] = buffer_load_u32(codes, loff1, row + tbase[t]);
+  }
+}
+
+// Issues the 8 codebook gathers of one tile; the halves stay unpacked until
+// the MFMA that consumes them, so the wait for them can sit right before it.
+__device__ __forceinline__ void gather_tile(const uint16_t* cb_lds, uint32_t lo, uint32_t hi, uint32_t (&g)[8]) {
+  uint32_t off[8];
+  window_offsets8(lo, hi, off);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) g[j] = lds_cb(cb_lds, off[j]);
+}
+
+__device__ __forceinline__ f16x8 pack_tile(const uint32_t (&g)[8]) {
+  u32x4 p;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_perm(g[2 * j + 1], g[2 * j], 0x05040100u);
+  return __builtin_bit_cast(f16x8, p);
+}
+
+// The gathers of tile t + 1 are issued before the MFMA of tile t consumes
+// tile t, so two tiles' gathers (up to the 15 outstanding LDS reads a wave can
+// track) are in flight per wave.
+template <int NT>
+__device__ __forceinline__ void decode_mfma_step(const uint16_t* cb_lds, const uint32_t (&lo)[NT],
+                                                 const uint32_t (&hi)[NT], const f16x8& a, f32x4 (&acc)[NT]) {
+  uint32_t cur[8], nxt[8];
+  gather_tile(cb_lds, lo[0], hi[0], cur);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t + 1 < NT) gather_tile(cb_lds, lo[t + 1], hi[t + 1], nxt);
+    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pack_tile(cur), acc[t], 0, 0, 0);
+    if (t + 1 < NT)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cur[j] = nxt[j];
+  }
+}
+
+template <int NT>
 __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t* __restrict__ xr,
                                                                   const uint32_t* __restrict__ codes,
                                                                   const uint16_t* __restrict__ cb,
@@ -44,16 +100,17 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
   load_codebook<DEC_THREADS>(cb_lds, cb);
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wn_idx = wave % plan.wn, wk_idx = wave / plan.wn;
   const int tw = t_end - t_begin;
   const int per_n = (tw + plan.wn - 1) / plan.wn;
   const int wt_begin = t_begin + min(wn_idx * per_n, tw);
-  const int nt_w = min(wt_begin + per_n, t_end) - wt_begin;
+  const int nt_w = min(wt_begin + per_n, t_end) - wt_begin;  // <= NT
   const int sw = s_end - s_begin;
   const int per_k = (sw + plan.wk - 1) / plan.wk;
   const int ws_begin = s_begin + min(wk_idx * per_k, sw);
   const int ws_end = min(ws_begin + per_k, s_end);
+  const bool busy = nt_w > 0 && ws_begin < ws_end;  // wave-uniform
 
   // Lane roles in the 16x16x32 MFMA: A row (= x row) and B column (= n) are
   // lane & 15; the 8-element k slice is lane >> 4: k-tile (lane >> 5) of the
@@ -62,28 +119,35 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
   const int ktile_in_step = lane >> 5;
   const int d = 2 * c + ((lane >> 4) & 1);  // first code word of the lane's windows
   const int d1 = (d + 1) & 31;
+  const int loff = (ktile_in_step * ntiles_total * 32 + d) * 4;  // bytes
+  const int loff1 = (ktile_in_step * ntiles_total * 32 + d1) * 4;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((int64_t)K * N / 2));
+  // Tiles past the wave's range re-read its last tile (no branches in the
+  // hot loop); their sums are never stored.
+  int tbase[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) tbase[t] = (wt_begin + min(t, max(nt_w, 1) - 1)) * 128;  // bytes
 
   for (int m0 = 0; m0 < M; m0 += 16) {
-    f32x4 acc[DEC_NT_MAX];
+    f32x4 acc[NT];
 #pragma unroll
-    for (int t = 0; t < DEC_NT_MAX; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     const int mrow = m0 + c;
-    const uint16_t* xrow = xr + (int64_t)mrow * K + 8 * (lane >> 4);
-    for (int step = ws_begin; step < ws_end; ++step) {
-      f16x8 a = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
-      if (mrow < M) a = *reinterpret_cast<const f16x8*>(xrow + 32 * step);
-      const uint32_t* trow = codes + ((int64_t)(2 * step + ktile_in_step) * ntiles_total + wt_begin) * 32;
-#pragma unroll
-      for (int t = 0; t < DEC_NT_MAX; ++t) {
-        if (t < nt_w) {
-          const uint32_t lo = trow[32 * t + d], hi = trow[32 * t + d1];
-          uint32_t off[8];
-          window_offsets8(lo, hi, off);
-          f16x8 b;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) b[j] = __builtin_bit_cast(f16, lds_cb(cb_lds, off[j]));
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+    const bool mok = mrow < M;
+    const uint16_t* xrow = xr + (int64_t)(mok ? mrow : 0) * K + 8 * (lane >> 4);
+    if (busy) {
+      uint32_t lo0[NT], hi0[NT], lo1[NT], hi1[NT];
+      f16x8 a0, a1;
+      const int last = ws_end - 1;
+      decode_load_step<NT>(crs, ntiles_total, ws_begin, tbase, loff, loff1, xrow, mok, lo0, hi0, a0);
+      for (int step = ws_begin; step < ws_end; step += 2) {
+        decode_load_step<NT>(crs, ntiles_total, min(step + 1, last), tbase, loff, loff1, xrow, mok, lo1, hi1, a1);
+        decode_mfma_step<NT>(cb_lds, lo0, hi0, a0, acc);
+        if (step + 1 < ws_end) {
+          decode_load_step<NT>(crs, ntiles_total, min(step + 2, last), tbase, loff, loff1, xrow, mok, lo0, hi0,
+                               a0);
+          decode_mfma_step<NT>(cb_lds, lo1, hi1, a1, acc);
         }
       }
     }
@@ -94,7 +158,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
     for (int j = 0; j < plan.wk; ++j) {
       if (wk_idx == j) {
 #pragma unroll
-        for (int t = 0; t < DEC_NT_MAX; ++t) {
+        for (int t = 0; t < NT; ++t) {
           if (t < nt_w) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -116,71 +180,74 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
 }
 
 // y[m][128b + i] = fp16(sign_n * (1/sqrt128) * sum_j H[i][j] * scale[n_j] *
-//                       sum_ks partials[ks][m][n_j]); an aligned quad of lanes
-// per 128-column block, as in the Hadamard kernel.
+//                       sum_ks partials[ks][m][n_j]); 16 lanes per 128-column
+// block, 8 columns per lane.
 __global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __restrict__ partials, int32_t ks_count,
                                                               const uint16_t* __restrict__ scale,
                                                               const uint16_t* __restrict__ sign_n,
                                                               uint16_t* __restrict__ y, int32_t M, int32_t N) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int q = (int)(gid & 3);
+  const int q = (int)(gid & 15);
   const int64_t nblocks = (int64_t)M * (N / 128);
-  const int64_t blk_raw = gid >> 2;
+  const int64_t blk_raw = gid >> 4;
   const int64_t blk = blk_raw < nblocks ? blk_raw : nblocks - 1;
   const int64_t m = blk / (N / 128);
-  const int64_t n0 = (blk % (N / 128)) * 128 + 32 * q;
+  const int64_t n0 = (blk % (N / 128)) * 128 + 8 * q;
 
-  float v[32];
+  float v[8];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) v[e] = 0.f;
+  for (int e = 0; e < 8; ++e) v[e] = 0.f;
   for (int ks = 0; ks < ks_count; ++ks) {
     const f32x4* src = reinterpret_cast<const f32x4*>(partials + ((int64_t)ks * M + m) * N + n0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const f32x4 p = src[i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[4 * i + j] += p[j];
-    }
-  }
-  const u32x4* sc = reinterpret_cast<const u32x4*>(scale + n0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x4 s = sc[i];
+    const f32x4 p0 = src[0], p1 = src[1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[8 * i + 2 * j] *= bits_lo_f16(s[j]);
-      v[8 * i + 2 * j + 1] *= bits_hi_f16(s[j]);
+      v[j] += p0[j];
+      v[4 + j] += p1[j];
     }
   }
-  wht128_quad(v, q);
-  u32x4 o[4];
+  const u32x4 sc = *reinterpret_cast<const u32x4*>(scale + n0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o[i][j] = pack_f16x2(v[8 * i + 2 * j] * EXL3_INV_SQRT128, v[8 * i + 2 * j + 1] * EXL3_INV_SQRT128);
-  if (sign_n) {
-    const u32x4* sq = reinterpret_cast<const u32x4*>(sign_n + n0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] ^= (sq[i] & 0x80008000u);
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] *= bits_lo_f16(sc[j]);
+    v[2 * j + 1] *= bits_hi_f16(sc[j]);
   }
-  if (blk_raw < nblocks) {
-    u32x4* dst = reinterpret_cast<u32x4*>(y + m * N + n0);
+  wht128_16(v, q);
+  u32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = o[i];
-  }
+  for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * EXL3_INV_SQRT128, v[2 * j + 1] * EXL3_INV_SQRT128);
+  if (sign_n) o ^= (*reinterpret_cast<const u32x4*>(sign_n + n0) & 0x80008000u);
+  if (blk_raw < nblocks) *reinterpret_cast<u32x4*>(y + m * N + n0) = o;
 }
 
 hipError_t launch_decode_gemm(const uint16_t* xr, const uint32_t* codes, const uint16_t* cb, float* partials,
                               int32_t K, int32_t N, int32_t M, const DecodePlan& plan, hipStream_t stream) {
-  decode_gemm_kernel<<<plan.ks_count * plan.ns_count, DEC_THREADS, 0, stream>>>(xr, codes, cb, partials, K, N, M,
-                                                                               plan);
+  const int grid = plan.ks_count * plan.ns_count;
+#define EXL3_DEC_CASE(nt)                                                                                  \
+  case nt:                                                                                                 \
+    decode_gemm_kernel<nt><<<grid, DEC_THREADS, 0, stream>>>(xr, codes, cb, partials, K, N, M, plan);      \
+    break;
+  switch (plan.nt_wave) {
+    EXL3_DEC_CASE(1)
+    EXL3_DEC_CASE(2)
+    EXL3_DEC_CASE(3)
+    EXL3_DEC_CASE(4)
+    EXL3_DEC_CASE(5)
+    EXL3_DEC_CASE(6)
+    EXL3_DEC_CASE(8)
+    EXL3_DEC_CASE(10)
+    EXL3_DEC_CASE(12)
+    EXL3_DEC_CASE(9)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef EXL3_DEC_CASE
   return hipGetLastError();
 }
 
 hipError_t launch_decode_finalize(const float* partials, int32_t ks_count, const uint16_t* scale,
                                   const uint16_t* sign_n, uint16_t* y, int32_t M, int32_t N, hipStream_t stream) {
-  const int64_t threads = (int64_t)M * (N / 128) * 4;
+  const int64_t threads = (int64_t)M * (N / 128) * 16;
   decode_finalize_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(partials, ks_count, scale, sign_n,
                                                                                 y, M, N);
   return hipGetLastError();

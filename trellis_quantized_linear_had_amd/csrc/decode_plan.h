@@ -15,7 +15,12 @@ struct DecodePlan {
   int32_t ksteps_per_wg;  // 32-wide k-steps per workgroup (last may be short)
   int32_t ntiles_per_wg;  // 16-wide n-tiles per workgroup (last may be short), <= DEC_NT_MAX
   int32_t wn;             // waves along N inside a workgroup
-  int32_t wk;             // waves along K inside a workgroup (wn * wk = 8)
+  int32_t wk;             // waves along K inside a workgroup (wn * wk = 16)
+  int32_t nt_wave;        // compiled n-tiles per wave (>= the largest wave share)
 };
+
+// Per-wave n-tile counts the decode kernel is compiled for (16 waves of at
+// most 128 VGPRs: accumulators and two code-word sets grow with the count).
+static const int32_t kDecodeNtInstances[] = {1, 2, 3, 4, 5, 6, 8, 9, 10, 12};
 
 }  // namespace exl3

@@ -6,11 +6,12 @@
 // decodable vocabulary).
 //
 // HBM-bound: each weight row is streamed once (2 bytes per element). A wave
-// owns 64 consecutive weight rows (four 16-row MFMA tiles) over all of K; each
-// lane loads 64 contiguous bytes of a row per 128-wide k chunk and feeds them
-// to v_mfma_f32_16x16x32_f16 as the A operand, with up to 16 rows of x as the
-// B operand. The k order inside a chunk is permuted identically on both
-// operands, which leaves the dot products unchanged.
+// owns 64 consecutive weight rows (four 16-row MFMA tiles) over all of K and
+// feeds them to v_mfma_f32_16x16x32_f16 as the A operand, with up to 16 rows of
+// x as the B operand. Inside a 128-wide k chunk, MFMA step s takes the k slice
+// 32 s + 8 g .. + 8 in lane group g on both operands (a permutation of k, which
+// leaves the dot products unchanged), so each 16-byte load instruction reads
+// 64 contiguous bytes of each of 16 rows.
 #include "common.h"
 
 namespace exl3 {
@@ -46,10 +47,10 @@ __global__ __launch_bounds__(64 * LG_WAVES) void logits_kernel(const uint16_t* _
   for (int t = 0; t < 4; ++t) {
     const int64_t row = p0 + 16 * t + pl;
     wok[t] = row < n_pad;
-    wrow[t] = w + (wok[t] ? row : 0) * (int64_t)K + 32 * g;
+    wrow[t] = w + (wok[t] ? row : 0) * (int64_t)K + 8 * g;
   }
   const bool qok = q < M;
-  const uint16_t* xrow = x + (int64_t)(qok ? q : 0) * K + 32 * g;
+  const uint16_t* xrow = x + (int64_t)(qok ? q : 0) * K + 8 * g;
 
   for (int kc = 0; kc < K; kc += 128) {
     u32x4 av[4][4], bv[4];
@@ -57,10 +58,10 @@ __global__ __launch_bounds__(64 * LG_WAVES) void logits_kernel(const uint16_t* _
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        av[t][s] = wok[t] ? *reinterpret_cast<const u32x4*>(wrow[t] + kc + 8 * s) : (u32x4){0, 0, 0, 0};
+        av[t][s] = wok[t] ? *reinterpret_cast<const u32x4*>(wrow[t] + kc + 32 * s) : (u32x4){0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      bv[s] = qok ? *reinterpret_cast<const u32x4*>(xrow + kc + 8 * s) : (u32x4){0, 0, 0, 0};
+      bv[s] = qok ? *reinterpret_cast<const u32x4*>(xrow + kc + 32 * s) : (u32x4){0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll

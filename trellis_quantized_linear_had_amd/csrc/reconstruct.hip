@@ -28,6 +28,17 @@ __device__ __forceinline__ void tile_column_offsets(const uint32_t* __restrict__
 }
 
 // Writes W^T: wt[j * ldw + k] = W[k][16 nt0 + j], j < 16 n_nt.
+// A unit is 4 k-tiles x 1 n-tile: lane (dk = lane >> 4, c = lane & 15) decodes
+// column c of k-tile 4 kg + dk. A wave walks its units (stride = all waves) in
+// groups of RC_GROUP; the code words of the next group load into a second
+// register set while the current group decodes, which keeps ~2 KB of codes
+// per wave in flight.
+#define RC_GROUP 4
+
+struct RcRegs {
+  uint32_t w0[RC_GROUP], w1[RC_GROUP], w2[RC_GROUP], sc[RC_GROUP];
+};
+
 __global__ __launch_bounds__(1024) void reconstruct_nk_kernel(const uint32_t* __restrict__ codes,
                                                               const uint16_t* __restrict__ cb,
                                                               const uint16_t* __restrict__ scale, int32_t K,
@@ -40,26 +51,68 @@ __global__ __launch_bounds__(1024) void reconstruct_nk_kernel(const uint32_t* __
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, dk = lane >> 4;
   const int tiles_n = N / 16;
-  const int64_t units = (int64_t)(K / 64) * n_nt;  // a unit: 4 k-tiles x 1 n-tile
-  const int64_t nwaves = (int64_t)gridDim.x * 16;
-  for (int64_t u = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 6); u < units; u += nwaves) {
-    const int kg = (int)(u / n_nt), ntl = (int)(u % n_nt);
-    const int kt = 4 * kg + dk, nt = nt0 + ntl;
-    const uint32_t* tile = codes + ((int64_t)kt * tiles_n + nt) * 32;
-    uint32_t off[16];
-    tile_column_offsets(tile, c, off);
-    const f16 s = __builtin_bit_cast(f16, scale[16 * nt + c]);
-    const f16x2 s2 = {s, s};
-    u32x4 o[2];
+  // Unit indices are wave-uniform 32-bit values (K / 64 * n_nt < 2^31 for any
+  // K, N the layer accepts), so their arithmetic stays on the scalar unit.
+  const int units = (K / 64) * n_nt;
+  const int nwaves = gridDim.x * 16;
+  int u = blockIdx.x * 16 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (u >= units) return;  // no workgroup barrier follows
+  const int last = u + (units - 1 - u) / nwaves * nwaves;  // this wave's last unit
+
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((int64_t)K * N / 2));
+  const uint32_t vrow = (uint32_t)dk * tiles_n * 128u;  // bytes from k-tile 4 kg to 4 kg + dk
+  const uint32_t v0 = vrow + 8u * c, v1 = v0 + 4u, v2 = vrow + 4u * ((2 * c + 2) & 31);
+  // scales: the aligned dword holding column 16 nt + c, then its half
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(scale, (uint32_t)N * 2);
+  const uint32_t vsc = 4u * (c >> 1), sc_shift = 16u * (c & 1);
+
+  auto load_group = [&](int ug, RcRegs& R) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      f16x2 v = {__builtin_bit_cast(f16, lds_cb(cb_lds, off[2 * j])), __builtin_bit_cast(f16, lds_cb(cb_lds, off[2 * j + 1]))};
-      v = v * s2;  // one fp16 rounding of the exact product
-      o[j >> 2][j & 3] = __builtin_bit_cast(uint32_t, v);
+    for (int i = 0; i < RC_GROUP; ++i) {
+      const int uu = min(ug + i * nwaves, last);  // past the end: reload the last unit
+      const int kg = uu / n_nt, ntl = uu % n_nt;
+      const uint32_t so = (uint32_t)((4 * kg * tiles_n + nt0 + ntl) * 128);
+      R.w0[i] = buffer_load_u32(crs, v0, so);
+      R.w1[i] = buffer_load_u32(crs, v1, so);
+      R.w2[i] = buffer_load_u32(crs, v2, so);
+      R.sc[i] = buffer_load_u32(srs, vsc, (uint32_t)(32 * (nt0 + ntl)));
     }
-    u32x4* dst = reinterpret_cast<u32x4*>(wt + (int64_t)(16 * ntl + c) * ldw + 16 * kt);
-    dst[0] = o[0];
-    dst[1] = o[1];
+  };
+  auto decode_group = [&](int ug, const RcRegs& R) {
+#pragma unroll
+    for (int i = 0; i < RC_GROUP; ++i) {
+      const int uu = ug + i * nwaves;
+      if (uu > last) break;  // wave-uniform
+      const int kg = uu / n_nt, ntl = uu % n_nt;
+      const int kt = 4 * kg + dk;
+      uint32_t a[8], b[8];
+      window_offsets8(R.w0[i], R.w1[i], a);
+      window_offsets8(R.w1[i], R.w2[i], b);
+      const f16 s = __builtin_bit_cast(f16, (uint16_t)(R.sc[i] >> sc_shift));
+      const f16x2 s2 = {s, s};
+      u32x4 o[2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t o0 = j < 4 ? a[2 * j] : b[2 * j - 8], o1 = j < 4 ? a[2 * j + 1] : b[2 * j - 7];
+        f16x2 v = {__builtin_bit_cast(f16, lds_cb(cb_lds, o0)), __builtin_bit_cast(f16, lds_cb(cb_lds, o1))};
+        v = v * s2;  // one fp16 rounding of the exact product
+        o[j >> 2][j & 3] = __builtin_bit_cast(uint32_t, v);
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(wt + (int64_t)(16 * ntl + c) * ldw + 16 * kt);
+      dst[0] = o[0];
+      dst[1] = o[1];
+    }
+  };
+
+  const int gstride = RC_GROUP * nwaves;
+  RcRegs ra, rb;
+  load_group(u, ra);
+  for (; u <= last; u += 2 * gstride) {
+    load_group(u + gstride, rb);
+    decode_group(u, ra);
+    if (u + gstride > last) break;
+    load_group(u + 2 * gstride, ra);
+    decode_group(u + gstride, rb);
   }
 }
 

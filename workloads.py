@@ -85,13 +85,22 @@ def activations(config_seed: int, M: int, K: int, *extra: int) -> np.ndarray:
     return x.astype(np.float16).view(np.uint16)
 
 
-def logits_weights(config_seed: int, w_rows: int, K: int) -> np.ndarray:
-    """w_rows x K fp16 output-projection rows drawn as 0.02 * N(0,1), in 8192-row chunks."""
+def logits_weights(config_seed: int, w_rows: int, K: int, threads: int = 8) -> np.ndarray:
+    """w_rows x K fp16 output-projection rows drawn as 0.02 * N(0,1) (float32
+    draws), in 8192-row chunks, each chunk from its own stream."""
+    from concurrent.futures import ThreadPoolExecutor
+
     out = np.empty((w_rows, K), dtype=np.uint16)
-    for c, r0 in enumerate(range(0, w_rows, LOGITS_CHUNK_ROWS)):
+
+    def fill(c):
+        r0 = c * LOGITS_CHUNK_ROWS
         r1 = min(w_rows, r0 + LOGITS_CHUNK_ROWS)
-        block = 0.02 * rng(config_seed, T_LOGITS_W, c).standard_normal((r1 - r0, K))
-        out[r0:r1] = block.astype(np.float16).view(np.uint16)
+        block = rng(config_seed, T_LOGITS_W, c).standard_normal((r1 - r0, K), dtype=np.float32)
+        out[r0:r1] = (np.float32(0.02) * block).astype(np.float16).view(np.uint16)
+
+    n_chunks = (w_rows + LOGITS_CHUNK_ROWS - 1) // LOGITS_CHUNK_ROWS
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(fill, range(n_chunks)))
     return out
 
 
