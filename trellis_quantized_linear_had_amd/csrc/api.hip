@@ -30,7 +30,8 @@ hipError_t launch_decode_gemm(const uint16_t* xr, const uint32_t* codes, const u
 hipError_t launch_decode_finalize(const float* partials, int32_t ks_count, const uint16_t* scale,
                                   const uint16_t* sign_n, uint16_t* y, int32_t M, int32_t N, hipStream_t stream);
 hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
-                           int64_t ldy, int32_t n0, const uint16_t* sign_n, hipStream_t stream);
+                           int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream);
+size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K);
 hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int64_t n_valid, int64_t n_pad,
                          uint16_t* logits, int64_t ld, int64_t* argmax, float* pv, int32_t* pi, hipStream_t stream);
 int64_t logits_items(int64_t n_pad);
@@ -146,7 +147,7 @@ DecodePlan plan_decode(int32_t K, int32_t N, int64_t M) {
 }
 
 struct PrefillLayout {
-  size_t xr_off, w_off, total;
+  size_t xr_off, w_off, part_off, total;
   int32_t chunk;
 };
 struct DecodeLayout {
@@ -159,7 +160,12 @@ PrefillLayout prefill_layout(int32_t K, int32_t N, int64_t M) {
   l.chunk = std::min<int32_t>(N, EXL3_MAX_CHUNK_COLS);
   l.xr_off = 0;
   l.w_off = align256((size_t)M * K * 2);
-  l.total = l.w_off + align256((size_t)l.chunk * K * 2);
+  l.part_off = l.w_off + align256((size_t)l.chunk * K * 2);
+  // fp32 k-piece tiles of the GEMM's last round, for the widest slice and the
+  // trailing one (the only two widths the slice loop uses)
+  const int32_t last = N - (N - 1) / l.chunk * l.chunk;
+  const size_t part = std::max(gemm_partial_bytes(l.chunk, (int32_t)M, K), gemm_partial_bytes(last, (int32_t)M, K));
+  l.total = l.part_off + align256(part);
   return l;
 }
 
@@ -247,7 +253,8 @@ int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
     for (int32_t n0 = 0; n0 < N; n0 += l.chunk) {
       const int32_t nc = std::min(l.chunk, N - n0);
       EXL3_TRY(launch_reconstruct_nk(L->codes, L->codebook, L->scale, K, N, n0, nc, wt, K, stream), "reconstruct");
-      EXL3_TRY(launch_gemm_had(wt, xr, y, nc, (int32_t)M, K, N, n0, L->sign_n, stream), "gemm");
+      EXL3_TRY(launch_gemm_had(wt, xr, y, nc, (int32_t)M, K, N, n0, L->sign_n, (float*)(sb + l.part_off), stream),
+               "gemm");
     }
   } else {
     const DecodeLayout l = decode_layout(K, N, M);

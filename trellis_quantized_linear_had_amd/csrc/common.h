@@ -47,41 +47,12 @@ __device__ __forceinline__ float quad_perm(float v) {
 #define EXL3_DPP_XOR1 0xB1  // quad_perm [1,0,3,2]
 #define EXL3_DPP_XOR2 0x4E  // quad_perm [2,3,0,1]
 
-// Unnormalised 128-point Walsh-Hadamard transform of one block held by an
-// aligned quad of lanes: lane q (= lane & 3) holds elements 32q .. 32q + 31 in
-// v[0..31]. Index bits 0..4 live in registers, bits 5 and 6 in the lane.
-// Butterfly convention: (a, b) -> (a + b, a - b) with a the lower index, which
-// yields the natural (Sylvester) order H[i][j] = (-1)^popcount(i & j).
-__device__ __forceinline__ void wht128_quad(float (&v)[32], int q) {
-#pragma unroll
-  for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if ((j & h) == 0) {
-        float a = v[j], b = v[j + h];
-        v[j] = a + b;
-        v[j + h] = a - b;
-      }
-    }
-  }
-  // bit 5: partner lane q ^ 1; lower lane keeps a + b, upper keeps a - b
-  const float s1 = (q & 1) ? -1.0f : 1.0f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    float p = quad_perm<EXL3_DPP_XOR1>(v[j]);
-    v[j] = __builtin_fmaf(s1, v[j], p);
-  }
-  const float s2 = (q & 2) ? -1.0f : 1.0f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    float p = quad_perm<EXL3_DPP_XOR2>(v[j]);
-    v[j] = __builtin_fmaf(s2, v[j], p);
-  }
-}
-
-// The same transform with 16 lanes per block: lane q (= lane & 15) holds
-// elements 8q .. 8q + 7. Index bits 0..2 live in registers, bits 3..6 in the
-// lane (partners q ^ 1, q ^ 2 by DPP, q ^ 4, q ^ 8 by swizzle).
+// Unnormalised 128-point Walsh-Hadamard transform of one block held by 16
+// consecutive lanes: lane q (= lane & 15) holds elements 8q .. 8q + 7 in
+// v[0..7]. Index bits 0..2 live in registers, bits 3..6 in the lane (partners
+// q ^ 1, q ^ 2 by DPP, q ^ 4, q ^ 8 by swizzle). Butterfly convention:
+// (a, b) -> (a + b, a - b) with a the lower index, which yields the natural
+// (Sylvester) order H[i][j] = (-1)^popcount(i & j).
 __device__ __forceinline__ void wht128_16(float (&v)[8], int q) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {

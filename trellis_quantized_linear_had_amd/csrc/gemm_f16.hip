@@ -14,12 +14,20 @@
 // Tiling: 256 (p) x 256 (q) per workgroup, 64-wide k steps. Operands go from
 // global memory straight into LDS (global_load_lds_dwordx4, no register
 // staging), two stages, one barrier per k step. Inside a stage each 128-byte
-// row is cut in 16-byte chunks XOR-swizzled by (row & 7), so the fragment
-// reads (32 rows at one chunk) are bank-conflict free; the swizzle is applied
-// on the global side, because a direct-to-LDS load writes lane i's 16 bytes at
-// base + 16 i. 8 waves as 2 (p) x 4 (q), each 128 x 64 = 4 x 2
-// v_mfma_f32_32x32x16_f16 tiles; two waves per SIMD hide each other's LDS and
-// barrier waits.
+// row is cut in 16-byte chunks XOR-swizzled by ((row >> 1) & 7): the LDS
+// serves a 16-byte read 16 lanes at a time over 64 banks, and this key makes
+// every group of 16 consecutive rows hit 16 distinct bank groups (measured:
+// zero bank-conflict cycles). The swizzle is applied on the global side,
+// because a direct-to-LDS load writes lane i's 16 bytes at base + 16 i. 8
+// waves form 2 (p) x 4 (q); each owns 128 p-rows (one rotation block, 4
+// v_mfma_f32_32x32x16_f16 row tiles) and 2 32-wide q tiles; two waves per
+// SIMD.
+//
+// Tail balance: tiles are dealt to the 256 CUs in rounds. The largest
+// multiple of 256 tiles runs whole; the remaining tiles are cut along K into
+// S = floor(256 / rem) pieces so the last round is full, each piece writes its
+// fp32 accumulator tile (in register order) to scratch, and a fixup kernel
+// sums the S pieces in a fixed order and runs the same rotation epilogue.
 //
 // Workgroup order is XCD-aware: workgroups are dispatched round-robin over
 // the 8 XCDs, so workgroup w is given tile (w % 8) * ceil(T / 8) + w / 8. Each
@@ -33,23 +41,28 @@ namespace exl3 {
 #define G_BP 256
 #define G_BQ 256
 #define G_BK 64
+#define G_WQ 4
+#define G_QT 2
 #define G_THREADS 512
-#define G_STAGE (G_BP * G_BK + G_BQ * G_BK)  // halves per stage
+#define G_STAGE ((G_BP + G_BQ) * G_BK)  // halves per stage
+#define G_LPS 8                         // load instructions per wave per stage
+#define G_CUS 256
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * G_BK + ((chunk ^ (row & 7)) << 3); }
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * G_BK + ((chunk ^ swz_key(row)) << 3); }
 
-// Per-lane byte offsets of the 4 x 16 bytes one wave loads per k step from
-// 32 rows of a row-major operand (8 rows, 1 KB per instruction): row
-// wave_row0 + 8 i + lane / 8, source chunk (lane % 8) ^ (row % 8). Rows past
-// the end re-read the last row (never stored).
+// Per-lane byte offsets of the 16-byte pieces one wave loads per k step from
+// 32 consecutive rows of a row-major operand (8 rows, 1 KB per instruction):
+// row wave_row0 + 8 i + lane / 8, source chunk (lane % 8) ^ key(row). Rows
+// past the end re-read the last row (never stored).
 __device__ __forceinline__ void lane_offsets(int64_t ld, int row_base, int rows_valid, int wave_row0, int lane,
                                              uint32_t (&off)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wave_row0 + 8 * i + (lane >> 3);
-    const int chunk = (lane & 7) ^ (r & 7);
+    const int chunk = (lane & 7) ^ swz_key(r);
     const int gr = min(row_base + r, rows_valid - 1);
     off[i] = (uint32_t)(((int64_t)gr * ld + 8 * chunk) * 2);
   }
@@ -64,101 +77,16 @@ __device__ __forceinline__ void load_rows_lds(const uint16_t* __restrict__ g, in
                                      16, 0, 0);
 }
 
-__global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __restrict__ A,
-                                                             const uint16_t* __restrict__ B,
-                                                             uint16_t* __restrict__ y, int32_t P, int32_t Q,
-                                                             int32_t K, int64_t ldy, int32_t n0,
-                                                             const uint16_t* __restrict__ sign_n) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * G_STAGE];
-
-  const int tiles_q = (Q + G_BQ - 1) / G_BQ;
-  const int tiles = ((P + G_BP - 1) / G_BP) * tiles_q;
-  const int per_xcd = (tiles + 7) / 8;
-  const int t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (t >= tiles) return;  // whole workgroup (uniform)
-  const int p_base = (t / tiles_q) * G_BP, q_base = (t % tiles_q) * G_BQ;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wp = wave & 1, wq = wave >> 1;
-
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  uint32_t offa[4], offb[4];
-  lane_offsets(K, p_base, P, 32 * wave, lane, offa);
-  lane_offsets(K, q_base, Q, 32 * wave, lane, offb);
-  auto issue_loads = [&](int stage, int k0) {
-    uint16_t* st = smem + stage * G_STAGE;
-    load_rows_lds(A, k0, offa, st, 32 * wave);
-    load_rows_lds(B, k0, offb, st + G_BP * G_BK, 32 * wave);
-  };
-
-  const int nk = K / G_BK;
+// Output rotation + signs + fp16 store of one wave's 128 x 64 block.
+// acc[i][j][r] holds D[p][q] with (inside the wave's 128-row rotation block)
+// p = 32 i + 8 (r >> 2) + 4 lhalf + (r & 3), q = 32 j + lrow. Index bits of p:
+// 0,1 <- r&3; 2 <- lhalf; 3,4 <- r>>2; 5,6 <- i.
+__device__ __forceinline__ void rotate_store(f32x16 (&acc)[4][G_QT], int lane, int pw, int qw, int P, int Q,
+                                             uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
+                                             const uint16_t* __restrict__ sign_n) {
   const int lrow = lane & 31, lhalf = lane >> 5;
-  // fragments of one k16 sub-step: 4 A tiles and 2 B tiles, two register sets
-  f16x8 af[2][4], bf[2][2];
-  auto read_frags = [&](int stage, int s, int buf) {
-    const uint16_t* As = smem + stage * G_STAGE;
-    const uint16_t* Bs = As + G_BP * G_BK;
-    const int ch = 2 * s + lhalf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[buf][i] = *reinterpret_cast<const f16x8*>(&As[swz(128 * wp + 32 * i + lrow, ch)]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) bf[buf][j] = *reinterpret_cast<const f16x8*>(&Bs[swz(64 * wq + 32 * j + lrow, ch)]);
-  };
-  auto mfmas = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[buf][i], bf[buf][j], acc[i][j], 0, 0, 0);
-  };
-
-  // Schedule per k step kb (stage buffer b = kb & 1):
-  //   sub-steps 0..2: read the next sub-step's fragments, then MFMAs;
-  //   sub-step 3: its fragments are in registers; wait for this wave's loads of
-  //   stage kb+1, barrier (every wave is done reading buffer b and stage kb+1
-  //   has landed), issue the loads of stage kb+2 into buffer b, read sub-step 0
-  //   of stage kb+1, and only then run sub-step 3's MFMAs, which cover the
-  //   barrier and the fragment-read latency.
-  issue_loads(0, 0);
-  if (nk > 1) issue_loads(1, G_BK);
-  if (nk > 1)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 0 (8 loads per wave per stage)
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  read_frags(0, 0, 0);
-  for (int kb = 0; kb < nk; ++kb) {
-    const int b = kb & 1;
-    read_frags(b, 1, 1);
-    mfmas(0);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(b, 2, 0);
-    mfmas(1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(b, 3, 1);
-    mfmas(0);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kb + 2 < nk) issue_loads(b, (kb + 2) * G_BK);
-    if (kb + 1 < nk) read_frags(b ^ 1, 0, 0);
-    mfmas(1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // Epilogue. acc[i][j][r] holds D[p][q] with (inside the wave's 128-row
-  // rotation block) p = 32 i + 8 (r >> 2) + 4 lhalf + (r & 3), q = 32 j + lrow.
-  // Index bits of p: 0,1 <- r&3; 2 <- lhalf; 3,4 <- r>>2; 5,6 <- i.
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < G_QT; ++j) {
 #pragma unroll
     for (int h = 1; h <= 8; h <<= 1) {  // register bits r&1, r&2, r&4, r&8
 #pragma unroll
@@ -192,35 +120,265 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
         acc[i][j][r] = __builtin_fmaf(s, acc[i][j][r], partner);
       }
   }
-
-  const int pw = p_base + 128 * wp;  // first output column of this wave's block
-  if (pw < P) {
+  if (pw >= P) return;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int q = q_base + 64 * wq + 32 * j + lrow;
-      if (q < Q) {
-        uint16_t* yrow = y + (int64_t)q * ldy + n0 + pw;
+  for (int j = 0; j < G_QT; ++j) {
+    const int q = qw + 32 * j + lrow;
+    if (q < Q) {
+      uint16_t* yrow = y + (int64_t)q * ldy + n0 + pw;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int p = 32 * i + 8 * g + 4 * lhalf;
-            u32x2 o;
-            o[0] = pack_f16x2(acc[i][j][4 * g] * EXL3_INV_SQRT128, acc[i][j][4 * g + 1] * EXL3_INV_SQRT128);
-            o[1] = pack_f16x2(acc[i][j][4 * g + 2] * EXL3_INV_SQRT128, acc[i][j][4 * g + 3] * EXL3_INV_SQRT128);
-            if (sign_n) o ^= (*reinterpret_cast<const u32x2*>(sign_n + n0 + pw + p) & 0x80008000u);
-            *reinterpret_cast<u32x2*>(yrow + p) = o;
-          }
-      }
+        for (int g = 0; g < 4; ++g) {
+          const int p = 32 * i + 8 * g + 4 * lhalf;
+          u32x2 o;
+          o[0] = pack_f16x2(acc[i][j][4 * g] * EXL3_INV_SQRT128, acc[i][j][4 * g + 1] * EXL3_INV_SQRT128);
+          o[1] = pack_f16x2(acc[i][j][4 * g + 2] * EXL3_INV_SQRT128, acc[i][j][4 * g + 3] * EXL3_INV_SQRT128);
+          if (sign_n) o ^= (*reinterpret_cast<const u32x2*>(sign_n + n0 + pw + p) & 0x80008000u);
+          *reinterpret_cast<u32x2*>(yrow + p) = o;
+        }
     }
   }
 }
 
+// One accumulator tile in scratch: 512 threads x 128 floats, stored as 32
+// float4 columns of 512 (coalesced in both the writer and the fixup).
+__device__ __forceinline__ void store_partial(const f32x16 (&acc)[4][G_QT], f32x4* __restrict__ dst) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < G_QT; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 v = {acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+        dst[((i * G_QT + j) * 4 + c) * G_THREADS + threadIdx.x] = v;
+      }
+}
+
+// MODE 0: workgroup w computes tile tile_base + t (t in XCD order, t < count)
+// over all of K and runs the rotation epilogue. MODE 1: workgroup w computes
+// k-piece w % splits of tile tile_base + w / splits and writes the partial.
+template <int MODE>
+__global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __restrict__ A,
+                                                             const uint16_t* __restrict__ B,
+                                                             uint16_t* __restrict__ y, int32_t P, int32_t Q,
+                                                             int32_t K, int64_t ldy, int32_t n0,
+                                                             const uint16_t* __restrict__ sign_n, int32_t tile_base,
+                                                             int32_t count, int32_t splits,
+                                                             f32x4* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * G_STAGE];
+
+  const int tiles_q = (Q + G_BQ - 1) / G_BQ;
+  int t, kb0, kb1;
+  const int nk_all = K / G_BK;
+  if (MODE == 0) {
+    const int per_xcd = (count + 7) / 8;
+    t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (t >= count) return;  // whole workgroup (uniform)
+    kb0 = 0;
+    kb1 = nk_all;
+  } else {
+    t = blockIdx.x / splits;
+    const int sp = blockIdx.x % splits, per = (nk_all + splits - 1) / splits;
+    kb0 = min(sp * per, nk_all);
+    kb1 = min(kb0 + per, nk_all);
+  }
+  const int tile = tile_base + t;
+  const int p_base = (tile / tiles_q) * G_BP, q_base = (tile % tiles_q) * G_BQ;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wp = wave & 1, wq = wave >> 1;
+
+  f32x16 acc[4][G_QT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < G_QT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  uint32_t offa[4], offb[4];
+  lane_offsets(K, p_base, P, 32 * wave, lane, offa);
+  lane_offsets(K, q_base, Q, 32 * wave, lane, offb);
+  auto issue_loads = [&](int stage, int k0) {
+    uint16_t* st = smem + stage * G_STAGE;
+    load_rows_lds(A, k0, offa, st, 32 * wave);
+    load_rows_lds(B, k0, offb, st + G_BP * G_BK, 32 * wave);
+  };
+
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  // fragments of one k16 sub-step: 4 A tiles and 2 B tiles, two register sets
+  f16x8 af[2][4], bf[2][G_QT];
+  auto read_frags = [&](int stage, int s, int buf) {
+    const uint16_t* As = smem + stage * G_STAGE;
+    const uint16_t* Bs = As + G_BP * G_BK;
+    const int ch = 2 * s + lhalf;
+    // B first: the first MFMAs of a sub-step use both B tiles and A tile 0
+#pragma unroll
+    for (int j = 0; j < G_QT; ++j)
+      bf[buf][j] = *reinterpret_cast<const f16x8*>(&Bs[swz(32 * G_QT * wq + 32 * j + lrow, ch)]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[buf][i] = *reinterpret_cast<const f16x8*>(&As[swz(128 * wp + 32 * i + lrow, ch)]);
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < G_QT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[buf][i], bf[buf][j], acc[i][j], 0, 0, 0);
+  };
+  // Pins the order inside one sub-step: the 6 fragment reads of the next
+  // sub-step are all issued in its first half (read, MFMA three times, then
+  // three reads), so they land under the remaining five MFMAs instead of
+  // after them.
+#ifndef EXL3_GEMM_SCHED
+#define EXL3_GEMM_SCHED 2
+#endif
+  auto interleave = [&]() {
+#if EXL3_GEMM_SCHED == 2
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
+#elif EXL3_GEMM_SCHED == 1
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#endif
+  };
+
+  // Schedule per k step kb (stage buffer b = (kb - kb0) & 1):
+  //   sub-steps 0..2: read the next sub-step's fragments, then MFMAs;
+  //   sub-step 3: its fragments are in registers; wait for this wave's loads of
+  //   stage kb+1, barrier (every wave is done reading buffer b and stage kb+1
+  //   has landed), issue the loads of stage kb+2 into buffer b, read sub-step 0
+  //   of stage kb+1, and only then run sub-step 3's MFMAs, which cover the
+  //   barrier and the fragment-read latency.
+  const int nk = kb1 - kb0;
+  if (nk > 0) {
+    issue_loads(0, kb0 * G_BK);
+    if (nk > 1) issue_loads(1, (kb0 + 1) * G_BK);
+    if (nk > 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G_LPS) : "memory");  // stage 0 landed, stage 1 may not have
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    read_frags(0, 0, 0);
+    for (int kk = 0; kk < nk; ++kk) {
+      const int b = kk & 1;
+      read_frags(b, 1, 1);
+      mfmas(0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(b, 2, 0);
+      mfmas(1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(b, 3, 1);
+      mfmas(0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kk + 2 < nk) issue_loads(b, (kb0 + kk + 2) * G_BK);
+      if (kk + 1 < nk) read_frags(b ^ 1, 0, 0);
+      mfmas(1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  if (MODE == 0)
+    rotate_store(acc, lane, p_base + 128 * wp, q_base + 32 * G_QT * wq, P, Q, y, ldy, n0, sign_n);
+  else
+    store_partial(acc, partial + (int64_t)blockIdx.x * (G_BP * G_BQ / 4));
+}
+
+// Sums the k-pieces of one wave's 128 x 64 block in piece order and runs the
+// rotation epilogue. One single-wave workgroup per (tail tile, wave) spreads
+// the partial reads over the CUs.
+__global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict__ partial, int32_t splits,
+                                                        int32_t tile_base, int32_t P, int32_t Q,
+                                                        uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
+                                                        const uint16_t* __restrict__ sign_n) {
+  const int item = blockIdx.x / 8, wave = blockIdx.x % 8;
+  const int tiles_q = (Q + G_BQ - 1) / G_BQ;
+  const int tile = tile_base + item;
+  const int p_base = (tile / tiles_q) * G_BP, q_base = (tile % tiles_q) * G_BQ;
+  const int lane = threadIdx.x;
+  const int tid = 64 * wave + lane;  // the thread of the k-piece workgroup this lane stands for
+  const int wp = wave & 1, wq = wave >> 1;
+  f32x16 acc[4][G_QT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < G_QT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const f32x4* src = partial + ((int64_t)item * splits + sp) * (G_BP * G_BQ / 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < G_QT; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 v = src[((i * G_QT + j) * 4 + c) * G_THREADS + tid];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * c + e] += v[e];
+        }
+  }
+  rotate_store(acc, lane, p_base + 128 * wp, q_base + 32 * G_QT * wq, P, Q, y, ldy, n0, sign_n);
+}
+
+// Round plan: `full` tiles run whole; the `rem` tiles after them are cut into
+// `splits` k-pieces (one round of pieces).
+struct GemmPlan {
+  int tiles, full, rem, splits;
+};
+
+static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
+  GemmPlan g;
+  g.tiles = ((P + G_BP - 1) / G_BP) * ((Q + G_BQ - 1) / G_BQ);
+  g.full = g.tiles / G_CUS * G_CUS;
+  g.rem = g.tiles - g.full;
+  g.splits = 1;
+  if (g.rem > 0) {
+    g.splits = G_CUS / g.rem;
+    const int nk = K / G_BK;
+    if (g.splits > nk) g.splits = nk;
+    if (g.splits < 2) g.splits = 1;
+  }
+  if (g.splits == 1) {  // no split: every tile runs whole
+    g.full = g.tiles;
+    g.rem = 0;
+  }
+  return g;
+}
+
+size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K) {
+  const GemmPlan g = gemm_plan(P, Q, K);
+  return (size_t)g.rem * g.splits * G_BP * G_BQ * sizeof(float);
+}
+
 hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
-                           int64_t ldy, int32_t n0, const uint16_t* sign_n, hipStream_t stream) {
-  const int tiles = ((P + G_BP - 1) / G_BP) * ((Q + G_BQ - 1) / G_BQ);
-  const int grid = 8 * ((tiles + 7) / 8);
-  gemm_had_kernel<<<grid, G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n);
+                           int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream) {
+  const GemmPlan g = gemm_plan(P, Q, K);
+  f32x4* part = reinterpret_cast<f32x4*>(partial);
+  if (g.full > 0)
+    gemm_had_kernel<0><<<8 * ((g.full + 7) / 8), G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, 0, g.full,
+                                                                         1, part);
+  if (g.rem > 0) {
+    gemm_had_kernel<1><<<g.rem * g.splits, G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, g.full, g.rem,
+                                                                   g.splits, part);
+    gemm_fixup_kernel<<<g.rem * 8, 64, 0, stream>>>(part, g.splits, g.full, P, Q, y, ldy, n0, sign_n);
+  }
   return hipGetLastError();
 }
 
