@@ -25,8 +25,9 @@ hipError_t launch_reconstruct_nk(const uint32_t* codes, const uint16_t* cb, cons
 hipError_t launch_reconstruct_kn(const uint32_t* codes, const uint16_t* cb, const uint16_t* scale, int32_t K,
                                  int32_t N, int32_t n0, int32_t n_count, uint16_t* w, int64_t ldw, bool states,
                                  hipStream_t stream);
-hipError_t launch_decode_gemm(const uint16_t* xr, const uint32_t* codes, const uint16_t* cb, float* partials,
-                              int32_t K, int32_t N, int32_t M, const DecodePlan& plan, hipStream_t stream);
+hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const uint32_t* codes, const uint16_t* cb,
+                              float* partials, int32_t K, int32_t N, int32_t M, const DecodePlan& plan,
+                              hipStream_t stream);
 hipError_t launch_decode_finalize(const float* partials, int32_t ks_count, const uint16_t* scale,
                                   const uint16_t* sign_n, uint16_t* y, int32_t M, int32_t N, hipStream_t stream);
 hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
@@ -107,20 +108,29 @@ bool use_prefill(int64_t M, int32_t prefill_min_m) { return prefill_min_m > 0 &&
 // the slowest wave sets the time of its workgroup; every round of workgroups
 // pays the 128 KiB codebook copy into LDS (~3000 clocks); partials are
 // written and read once.
-DecodePlan plan_decode(int32_t K, int32_t N, int64_t M) {
+// Chooses (ks, ns, wn, wk, NT) for the decode kernel: every workgroup gets
+// the same work, the grid fills at most whole rounds of 256 CUs, and the
+// modelled cost (per round: the workgroup's tile-steps, the padded per-wave
+// share and a codebook load; plus the fp32 partial traffic) is least. With x_in_lds the workgroup's k
+// range is a whole number of 128-element blocks and its rotated slice of the
+// M rows fits DEC_XS_BYTES.
+static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, DecodePlan& best) {
   const int ksteps = K / 32, ntiles = N / 16;
   const int64_t mgroups = (M + 15) / 16;
-  DecodePlan best{1, 1, ksteps, 1, 1, 16, 1};
   double best_cost = 1e300;
+  bool found = false;
   const int wns[5] = {1, 2, 4, 8, 16};
   for (int wi = 0; wi < 5; ++wi) {
     const int wn = wns[wi], wk = 16 / wn;
     for (int ks = 1; ks <= std::min(ksteps, 64); ++ks) {
-      const int kpw = (ksteps + ks - 1) / ks;
+      int kpw = (ksteps + ks - 1) / ks;
+      if (x_in_lds) {
+        kpw = (kpw + 3) / 4 * 4;
+        if (M * kpw * 32 * 2 > DEC_XS_BYTES) continue;
+      }
       if ((int64_t)(ks - 1) * kpw >= ksteps) continue;
       const int kpw_wave = (kpw + wk - 1) / wk;
-      for (int npw = 1; npw * wn <= DEC_NT_MAX; ++npw) {
-        const int ntpw = npw * wn;
+      for (int ntpw = 1; ntpw <= DEC_NT_MAX; ++ntpw) {
         const int ns = (ntiles + ntpw - 1) / ntpw;
         const int ntpw_real = (ntiles + ns - 1) / ns;
         const int per_wave_n = (ntpw_real + wn - 1) / wn;
@@ -133,17 +143,28 @@ DecodePlan plan_decode(int32_t K, int32_t N, int64_t M) {
         if (nt_inst == 0) continue;
         const int64_t wgs = (int64_t)ks * ns;
         const int64_t rounds = (wgs + 255) / 256;
-        const double decode = (double)rounds * (16.0 * kpw_wave * nt_inst * 30.0 * mgroups + 3000.0);
+        // the CU's LDS gathers cover the workgroup's real tile-steps; the
+        // padded per-wave share bounds the slowest wave
+        const double decode =
+            (double)rounds * (30.0 * mgroups * ((double)ntpw_real * kpw + 16.0 * kpw_wave * nt_inst) + 3000.0);
         const double partial = (double)ks * M * N * 8.0 / 2083.0;
         const double cost = decode + partial;
         if (cost < best_cost - 1e-9) {
           best_cost = cost;
-          best = DecodePlan{ks, ns, kpw, ntpw_real, wn, wk, nt_inst};
+          best = DecodePlan{ks, ns, kpw, ntpw_real, wn, wk, nt_inst, x_in_lds ? 1 : 0};
+          found = true;
         }
       }
     }
   }
-  return best;
+  return found;
+}
+
+DecodePlan plan_decode(int32_t K, int32_t N, int64_t M) {
+  DecodePlan p{1, 1, K / 32, 1, 1, 16, 1, 0};
+  if (M <= 16 && plan_decode_search(K, N, M, true, p)) return p;
+  plan_decode_search(K, N, M, false, p);
+  return p;
 }
 
 struct PrefillLayout {
@@ -260,8 +281,14 @@ int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
     const DecodeLayout l = decode_layout(K, N, M);
     uint16_t* xr = (uint16_t*)(sb + l.xr_off);
     float* part = (float*)(sb + l.part_off);
-    EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
-    EXL3_TRY(launch_decode_gemm(xr, L->codes, L->codebook, part, K, N, (int32_t)M, l.plan, stream), "decode gemm");
+    if (l.plan.x_in_lds) {
+      EXL3_TRY(launch_decode_gemm(x, L->sign_k, L->codes, L->codebook, part, K, N, (int32_t)M, l.plan, stream),
+               "decode gemm");
+    } else {
+      EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
+      EXL3_TRY(launch_decode_gemm(xr, nullptr, L->codes, L->codebook, part, K, N, (int32_t)M, l.plan, stream),
+               "decode gemm");
+    }
     EXL3_TRY(launch_decode_finalize(part, l.plan.ks_count, L->scale, L->sign_n, y, (int32_t)M, N, stream),
              "decode finalize");
   }

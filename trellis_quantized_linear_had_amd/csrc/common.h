@@ -39,18 +39,32 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Lane exchange inside an aligned quad of lanes via DPP quad_perm.
+// Lane exchange by one DPP move; CTRL is the DPP control word (quad_perm,
+// row_mirror, row_half_mirror, ...), all rows and banks enabled.
 template <int CTRL>
-__device__ __forceinline__ float quad_perm(float v) {
+__device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 #define EXL3_DPP_XOR1 0xB1  // quad_perm [1,0,3,2]
 #define EXL3_DPP_XOR2 0x4E  // quad_perm [2,3,0,1]
+#define EXL3_DPP_REV4 0x1B  // quad_perm [3,2,1,0]: lane ^ 3
+#define EXL3_DPP_HALF_MIRROR 0x141  // lane ^ 7 within 8 lanes
+#define EXL3_DPP_MIRROR 0x140       // lane ^ 15 within 16 lanes
+
+// Value of lane ^ 4 and lane ^ 8 (within 16 lanes) by two DPP moves each,
+// on the VALU rather than the LDS crossbar: (l ^ 7) ^ 3 = l ^ 4 and
+// (l ^ 15) ^ 7 = l ^ 8.
+__device__ __forceinline__ float lane_xor4(float v) {
+  return dpp_mov<EXL3_DPP_REV4>(dpp_mov<EXL3_DPP_HALF_MIRROR>(v));
+}
+__device__ __forceinline__ float lane_xor8(float v) {
+  return dpp_mov<EXL3_DPP_HALF_MIRROR>(dpp_mov<EXL3_DPP_MIRROR>(v));
+}
 
 // Unnormalised 128-point Walsh-Hadamard transform of one block held by 16
 // consecutive lanes: lane q (= lane & 15) holds elements 8q .. 8q + 7 in
-// v[0..7]. Index bits 0..2 live in registers, bits 3..6 in the lane (partners
-// q ^ 1, q ^ 2 by DPP, q ^ 4, q ^ 8 by swizzle). Butterfly convention:
+// v[0..7]. Index bits 0..2 live in registers, bits 3..6 in the lane (all four
+// partners q ^ 1, q ^ 2, q ^ 4, q ^ 8 by DPP). Butterfly convention:
 // (a, b) -> (a + b, a - b) with a the lower index, which yields the natural
 // (Sylvester) order H[i][j] = (-1)^popcount(i & j).
 __device__ __forceinline__ void wht128_16(float (&v)[8], int q) {
@@ -68,13 +82,13 @@ __device__ __forceinline__ void wht128_16(float (&v)[8], int q) {
   const float s1 = (q & 1) ? -1.0f : 1.0f, s2 = (q & 2) ? -1.0f : 1.0f;
   const float s4 = (q & 4) ? -1.0f : 1.0f, s8 = (q & 8) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s1, v[j], quad_perm<EXL3_DPP_XOR1>(v[j]));
+  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s1, v[j], dpp_mov<EXL3_DPP_XOR1>(v[j]));
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s2, v[j], quad_perm<EXL3_DPP_XOR2>(v[j]));
+  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s2, v[j], dpp_mov<EXL3_DPP_XOR2>(v[j]));
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s4, v[j], __shfl_xor(v[j], 4, 16));
+  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s4, v[j], lane_xor4(v[j]));
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s8, v[j], __shfl_xor(v[j], 8, 16));
+  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s8, v[j], lane_xor8(v[j]));
 }
 
 }  // namespace exl3

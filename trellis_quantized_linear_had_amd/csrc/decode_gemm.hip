@@ -25,25 +25,42 @@ namespace exl3 {
 #define DEC_THREADS 1024
 #define DEC_WAVES 16
 
-// Loads the code words of NT tiles of one k-step (two per lane: the lane's
-// windows start in word d and end in word d + 1, mod 32) and the A fragment.
-// The tile bases are wave-uniform (scalar registers); each lane adds a 32-bit
-// offset (its k-tile row and word).
+// Loads the code words of NT tiles of one k-step: two per lane (the lane's
+// windows start in word d and end in word d + 1, mod 32). The tile bases are
+// wave-uniform (scalar registers); each lane adds a 32-bit offset (its k-tile
+// row and word).
 template <int NT>
-__device__ __forceinline__ void decode_load_step(__amdgpu_buffer_rsrc_t codes, int ntiles_total, int step,
-                                                 const int (&tbase)[NT], int loff, int loff1,
-                                                 const uint16_t* xrow, bool mok, uint32_t (&lo)[NT],
-                                                 uint32_t (&hi)[NT], f16x8& a) {
-  // The A fragment goes first: loads retire in order, so the MFMAs of the
-  // previous step (which need only that step's A fragment) never wait for
-  // this step's code words.
-  a = mok ? *reinterpret_cast<const f16x8*>(xrow + 32 * step) : (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+__device__ __forceinline__ void decode_load_codes(__amdgpu_buffer_rsrc_t codes, int ntiles_total, int step,
+                                                  const int (&tbase)[NT], int loff, int loff1, uint32_t (&lo)[NT],
+                                                  uint32_t (&hi)[NT]) {
   const uint32_t row = (uint32_t)(2 * step) * ntiles_total * 128u;  // bytes
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     lo[t] = buffer_load_u32(codes, loff, row + tbase[t]);
     hi[t] = buffer_load_u32(codes, loff1, row + tbase[t]);
   }
+}
+
+// The A fragment of one k-step (8 consecutive k of one row of Xr) and the
+// step's code words. The A fragment goes first: loads of one kind retire in
+// order, so the MFMAs of the previous step (which need only that step's A
+// fragment) never wait for this step's code words. XL: the fragment comes
+// from the workgroup's rotated slice in LDS (16-byte chunk j of row m stored
+// at chunk j ^ (m & 15), so the 16 rows one read instruction touches fall on
+// distinct banks); otherwise from Xr in global memory.
+template <int NT, bool XL>
+__device__ __forceinline__ void decode_load_step(__amdgpu_buffer_rsrc_t codes, int ntiles_total, int step,
+                                                 const int (&tbase)[NT], int loff, int loff1, const uint16_t* xsrc,
+                                                 int xstep0, bool mok, uint32_t (&lo)[NT], uint32_t (&hi)[NT],
+                                                 f16x8& a) {
+  if (XL) {
+    const int j = 4 * (step - xstep0) + (threadIdx.x & 63) / 16;  // chunk in the row
+    a = mok ? *reinterpret_cast<const f16x8*>(xsrc + 8 * (j ^ (threadIdx.x & 15)))
+            : (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+  } else {
+    a = mok ? *reinterpret_cast<const f16x8*>(xsrc + 32 * step) : (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  decode_load_codes<NT>(codes, ntiles_total, step, tbase, loff, loff1, lo, hi);
 }
 
 // Issues the 8 codebook gathers of one tile; the halves stay unpacked until
@@ -80,14 +97,20 @@ __device__ __forceinline__ void decode_mfma_step(const uint16_t* cb_lds, const u
   }
 }
 
-template <int NT>
-__global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t* __restrict__ xr,
+template <int NT, bool XL>
+__global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t* __restrict__ xin,
+                                                                  const uint16_t* __restrict__ sign_k,
                                                                   const uint32_t* __restrict__ codes,
                                                                   const uint16_t* __restrict__ cb,
                                                                   float* __restrict__ partials, int32_t K,
                                                                   int32_t N, int32_t M, DecodePlan plan) {
-  __shared__ uint16_t cb_lds[65536];
-  __shared__ float red[DEC_NT_MAX * 256];
+  // One 160 KiB block: the codebook (128 KiB), then either the rotated x
+  // slice (XL) or the reduction buffer of the multi-group path. After the
+  // last gather the whole block serves as reduction slots.
+  __shared__ __align__(16) float lds[40960];
+  uint16_t* cb_lds = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds + 32768);
+  float* red = lds + 32768;
 
   const int ksteps_total = K / 32, ntiles_total = N / 16;
   const int ks = blockIdx.x / plan.ns_count, ns = blockIdx.x % plan.ns_count;
@@ -96,9 +119,6 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
   const int t_begin = ns * plan.ntiles_per_wg;
   const int t_end = min(t_begin + plan.ntiles_per_wg, ntiles_total);
   if (s_begin >= s_end || t_begin >= t_end) return;  // whole workgroup idle (uniform)
-
-  load_codebook<DEC_THREADS>(cb_lds, cb);
-  __syncthreads();
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wn_idx = wave % plan.wn, wk_idx = wave / plan.wn;
@@ -128,6 +148,64 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
 #pragma unroll
   for (int t = 0; t < NT; ++t) tbase[t] = (wt_begin + min(t, max(nt_w, 1) - 1)) * 128;  // bytes
 
+  // Prologue. The codebook copy is in flight while (XL) the workgroup
+  // rotates its x slice: rows < M, k in [32 s_begin, 32 s_end), 16 lanes per
+  // 128-element block, the same arithmetic as the stand-alone rotation pass
+  // (sign bit flip, fp32 butterflies, one scaling, one fp16 rounding).
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(cb);
+    u32x4* dst = reinterpret_cast<u32x4*>(cb_lds);
+    constexpr int kPer = 65536 * 2 / 16 / DEC_THREADS;
+    u32x4 tmp[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) tmp[i] = src[threadIdx.x + i * DEC_THREADS];
+    if (XL) {
+      // M * kslice <= DEC_XS_BYTES / 2 elements, so each 16-lane group has
+      // at most two (row, block) tasks; both loads go out before any math.
+      static_assert(DEC_XS_BYTES / 2 / 128 <= 2 * (DEC_THREADS / 16), "more than two rotation tasks per group");
+      const int kslice = sw * 32, nblk = sw / 4, ntask = M * nblk;
+      const int q = threadIdx.x & 15;
+      // Without signs the mask is zero (the second load then re-reads x).
+      const uint16_t* sgn = sign_k ? sign_k : xin;
+      const uint32_t smask = sign_k ? 0x80008000u : 0u;
+      u32x4 xv[2], sv[2];
+      int xoff[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int task = (threadIdx.x >> 4) + i * (DEC_THREADS / 16);
+        const int tk = task < ntask ? task : 0;
+        const int m = tk / nblk, b = tk - m * nblk;
+        const int64_t kg = (int64_t)s_begin * 32 + 128 * b + 8 * q;
+        xv[i] = *reinterpret_cast<const u32x4*>(xin + (int64_t)m * K + kg);
+        sv[i] = *reinterpret_cast<const u32x4*>(sgn + kg);
+        xoff[i] = task < ntask ? m * kslice + 8 * (16 * b + (q ^ (m & 15))) : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (xoff[i] >= 0) {  // uniform over the 16 lanes of the block
+          xv[i] ^= sv[i] & smask;  // +-1: flip the sign bit
+          float v[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[2 * j] = bits_lo_f16(xv[i][j]);
+            v[2 * j + 1] = bits_hi_f16(xv[i][j]);
+          }
+          wht128_16(v, q);
+          u32x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            o[j] = pack_f16x2(v[2 * j] * EXL3_INV_SQRT128, v[2 * j + 1] * EXL3_INV_SQRT128);
+          *reinterpret_cast<u32x4*>(xs + xoff[i]) = o;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) dst[threadIdx.x + i * DEC_THREADS] = tmp[i];
+  }
+  // (The first step's code words are not requested before this barrier: its
+  // release fence would wait for them.)
+  __syncthreads();
+
   for (int m0 = 0; m0 < M; m0 += 16) {
     f32x4 acc[NT];
 #pragma unroll
@@ -135,53 +213,92 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
 
     const int mrow = m0 + c;
     const bool mok = mrow < M;
-    const uint16_t* xrow = xr + (int64_t)(mok ? mrow : 0) * K + 8 * (lane >> 4);
+    // XL: the row of the LDS slice; otherwise the row of Xr in global memory
+    // at this lane's 8-element k offset.
+    const uint16_t* xsrc = XL ? xs + (mok ? mrow : 0) * (sw * 32)
+                              : xin + (int64_t)(mok ? mrow : 0) * K + 8 * (lane >> 4);
     if (busy) {
       uint32_t lo0[NT], hi0[NT], lo1[NT], hi1[NT];
       f16x8 a0, a1;
       const int last = ws_end - 1;
-      decode_load_step<NT>(crs, ntiles_total, ws_begin, tbase, loff, loff1, xrow, mok, lo0, hi0, a0);
+      decode_load_step<NT, XL>(crs, ntiles_total, ws_begin, tbase, loff, loff1, xsrc, s_begin, mok, lo0, hi0, a0);
       for (int step = ws_begin; step < ws_end; step += 2) {
-        decode_load_step<NT>(crs, ntiles_total, min(step + 1, last), tbase, loff, loff1, xrow, mok, lo1, hi1, a1);
+        decode_load_step<NT, XL>(crs, ntiles_total, min(step + 1, last), tbase, loff, loff1, xsrc, s_begin, mok,
+                                 lo1, hi1, a1);
         decode_mfma_step<NT>(cb_lds, lo0, hi0, a0, acc);
         if (step + 1 < ws_end) {
-          decode_load_step<NT>(crs, ntiles_total, min(step + 2, last), tbase, loff, loff1, xrow, mok, lo0, hi0,
-                               a0);
+          decode_load_step<NT, XL>(crs, ntiles_total, min(step + 2, last), tbase, loff, loff1, xsrc, s_begin, mok,
+                                   lo0, hi0, a0);
           decode_mfma_step<NT>(cb_lds, lo1, hi1, a1, acc);
         }
       }
     }
 
-    // Fixed-order reduction over the wk waves that share these n-tiles.
-    // D layout of the MFMA: lane holds rows 4*(lane>>4) + r, column lane & 15.
-    const int rbase = (wt_begin - t_begin) * 256 + 4 * (lane >> 4) * 16 + c;
-    for (int j = 0; j < plan.wk; ++j) {
-      if (wk_idx == j) {
+    // Fixed-order reduction over the wk waves that share these n-tiles:
+    // sum = ((w_0 + w_1) + w_2) + ... over the waves' k order, for every
+    // output. D layout of the MFMA: lane holds rows 4*(lane>>4) + r, column
+    // lane & 15.
+    const int eoff = 4 * (lane >> 4) * 16 + c;
+    const int wt_off = wt_begin - t_begin;
+    if (m0 + 16 >= M) {
+      // Last row group: no gather follows, so the whole LDS block holds one
+      // slot per (wave, tile) and all waves store at once, in passes of
+      // `chunk` tiles.
+      float* slots = lds;
+      const int chunk = 40960 / 256 / plan.wk;
+      __syncthreads();
+      for (int t0 = 0; t0 < tw; t0 += chunk) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          if (t < nt_w) {
+          const int tt = wt_off + t - t0;
+          if (t < nt_w && tt >= 0 && tt < chunk)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              float* p = &red[rbase + t * 256 + r * 16];
-              *p = (j == 0) ? acc[t][r] : *p + acc[t][r];
+            for (int r = 0; r < 4; ++r) slots[(wk_idx * chunk + tt) * 256 + eoff + r * 16] = acc[t][r];
+        }
+        __syncthreads();
+        const int nout = min(chunk, tw - t0) * 256;
+        for (int idx = threadIdx.x; idx < nout; idx += DEC_THREADS) {
+          float sum = slots[idx];
+          for (int j = 1; j < plan.wk; ++j) sum += slots[j * chunk * 256 + idx];
+          const int t = t0 + (idx >> 8), e = idx & 255, m = m0 + (e >> 4), n = (t_begin + t) * 16 + (e & 15);
+          if (m < M) partials[((int64_t)ks * M + m) * N + n] = sum;
+        }
+        __syncthreads();
+      }
+    } else {
+      // More row groups follow and need the codebook: accumulate through the
+      // small reduction buffer one wave at a time, in the same order.
+      const int rbase = wt_off * 256 + eoff;
+      for (int j = 0; j < plan.wk; ++j) {
+        if (wk_idx == j) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            if (t < nt_w) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                float* p = &red[rbase + t * 256 + r * 16];
+                *p = (j == 0) ? acc[t][r] : *p + acc[t][r];
+              }
             }
           }
         }
+        __syncthreads();
+      }
+      // partials[ks][m][n]
+      for (int idx = threadIdx.x; idx < tw * 256; idx += DEC_THREADS) {
+        const int t = idx >> 8, e = idx & 255, m = m0 + (e >> 4), n = (t_begin + t) * 16 + (e & 15);
+        if (m < M) partials[((int64_t)ks * M + m) * N + n] = red[idx];
       }
       __syncthreads();
     }
-    // partials[ks][m][n]
-    for (int idx = threadIdx.x; idx < tw * 256; idx += DEC_THREADS) {
-      const int t = idx >> 8, e = idx & 255, m = m0 + (e >> 4), n = (t_begin + t) * 16 + (e & 15);
-      if (m < M) partials[((int64_t)ks * M + m) * N + n] = red[idx];
-    }
-    __syncthreads();
   }
 }
 
-// y[m][128b + i] = fp16(sign_n * (1/sqrt128) * sum_j H[i][j] * scale[n_j] *
-//                       sum_ks partials[ks][m][n_j]); 16 lanes per 128-column
-// block, 8 columns per lane.
+// Output stage: y[m][128b + i] = fp16(s_N * (1/sqrt128) * sum_j H[i][j] *
+// scale[n_j] * sum_ks partials[ks][m][n_j]); 16 lanes per (row, 128-column
+// block), 8 columns per lane. The partials are summed in ks order; the loads
+// of up to 8 slices are issued before their sums so one memory round trip
+// serves them.
 __global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __restrict__ partials, int32_t ks_count,
                                                               const uint16_t* __restrict__ scale,
                                                               const uint16_t* __restrict__ sign_n,
@@ -193,17 +310,35 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __res
   const int64_t blk = blk_raw < nblocks ? blk_raw : nblocks - 1;
   const int64_t m = blk / (N / 128);
   const int64_t n0 = (blk % (N / 128)) * 128 + 8 * q;
+  const int64_t slice = (int64_t)M * N;
 
   float v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = 0.f;
-  for (int ks = 0; ks < ks_count; ++ks) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(partials + ((int64_t)ks * M + m) * N + n0);
+  const f32x4* src = reinterpret_cast<const f32x4*>(partials + m * N + n0);
+  {
     const f32x4 p0 = src[0], p1 = src[1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[j] += p0[j];
-      v[4 + j] += p1[j];
+      v[j] = p0[j];
+      v[4 + j] = p1[j];
+    }
+  }
+  for (int k0 = 1; k0 < ks_count; k0 += 8) {
+    f32x4 p[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = min(k0 + i, ks_count - 1);
+      p[i][0] = src[k * slice / 4];
+      p[i][1] = src[k * slice / 4 + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (k0 + i < ks_count) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] += p[i][0][j];
+          v[4 + j] += p[i][1][j];
+        }
+      }
     }
   }
   const u32x4 sc = *reinterpret_cast<const u32x4*>(scale + n0);
@@ -220,12 +355,18 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __res
   if (blk_raw < nblocks) *reinterpret_cast<u32x4*>(y + m * N + n0) = o;
 }
 
-hipError_t launch_decode_gemm(const uint16_t* xr, const uint32_t* codes, const uint16_t* cb, float* partials,
-                              int32_t K, int32_t N, int32_t M, const DecodePlan& plan, hipStream_t stream) {
+hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const uint32_t* codes, const uint16_t* cb,
+                              float* partials, int32_t K, int32_t N, int32_t M, const DecodePlan& plan,
+                              hipStream_t stream) {
   const int grid = plan.ks_count * plan.ns_count;
-#define EXL3_DEC_CASE(nt)                                                                                  \
-  case nt:                                                                                                 \
-    decode_gemm_kernel<nt><<<grid, DEC_THREADS, 0, stream>>>(xr, codes, cb, partials, K, N, M, plan);      \
+#define EXL3_DEC_CASE(nt)                                                                                      \
+  case nt:                                                                                                     \
+    if (plan.x_in_lds)                                                                                         \
+      decode_gemm_kernel<nt, true><<<grid, DEC_THREADS, 0, stream>>>(xin, sign_k, codes, cb, partials, K, N,  \
+                                                                     M, plan);                                 \
+    else                                                                                                       \
+      decode_gemm_kernel<nt, false><<<grid, DEC_THREADS, 0, stream>>>(xin, sign_k, codes, cb, partials, K, N, \
+                                                                      M, plan);                                \
     break;
   switch (plan.nt_wave) {
     EXL3_DEC_CASE(1)
@@ -235,9 +376,8 @@ hipError_t launch_decode_gemm(const uint16_t* xr, const uint32_t* codes, const u
     EXL3_DEC_CASE(5)
     EXL3_DEC_CASE(6)
     EXL3_DEC_CASE(8)
-    EXL3_DEC_CASE(10)
-    EXL3_DEC_CASE(12)
     EXL3_DEC_CASE(9)
+    EXL3_DEC_CASE(10)
     default:
       return hipErrorInvalidValue;
   }

@@ -7,6 +7,10 @@
 // reduction slot for.
 #define DEC_NT_MAX 24
 
+// LDS the decode kernel keeps beside the 128 KiB codebook for the rotated
+// activation slice (rows < M, the workgroup's k range, fp16).
+#define DEC_XS_BYTES 32768
+
 namespace exl3 {
 
 struct DecodePlan {
@@ -17,10 +21,14 @@ struct DecodePlan {
   int32_t wn;             // waves along N inside a workgroup
   int32_t wk;             // waves along K inside a workgroup (wn * wk = 16)
   int32_t nt_wave;        // compiled n-tiles per wave (>= the largest wave share)
+  int32_t x_in_lds;       // 1: each workgroup rotates its own x slice into LDS
+                          // (M <= 16, slice <= DEC_XS_BYTES); 0: x is rotated
+                          // by a separate pass into scratch
 };
 
 // Per-wave n-tile counts the decode kernel is compiled for (16 waves of at
-// most 128 VGPRs: accumulators and two code-word sets grow with the count).
-static const int32_t kDecodeNtInstances[] = {1, 2, 3, 4, 5, 6, 8, 9, 10, 12};
+// most 128 VGPRs: accumulators and two code-word sets grow with the count;
+// 12 no longer fits without spilling).
+static const int32_t kDecodeNtInstances[] = {1, 2, 3, 4, 5, 6, 8, 9, 10};
 
 }  // namespace exl3
