@@ -86,7 +86,7 @@ def main():
         xl = _lib.to_device_u16(W.activations(lc["seed"], LOGITS_M, K))
         lg = torch.empty((LOGITS_M, n_pad), dtype=torch.int16, device=dev)
         am = torch.empty(LOGITS_M, dtype=torch.int64, device=dev)
-        lg_scratch = torch.empty(X.logits_scratch_bytes(LOGITS_M, n_valid, w_rows), dtype=torch.uint8, device=dev)
+        lg_scratch = torch.empty(X.logits_scratch_bytes(LOGITS_M, K, n_valid, w_rows), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log("inputs resident in %.1f s" % (time.time() - t_setup))
 

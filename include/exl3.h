@@ -160,7 +160,7 @@ int had_r_128(const uint16_t *in, uint16_t *out, int64_t rows, int64_t cols, con
  * read; the GEMM runs over whole 128-row tiles up to n_pad); fp32 accumulation.
  * The GEMM and the mask are one call: there is no way to obtain padded logits
  * without the mask. K must be a multiple of 128. scratch: at least
- * logits_scratch_bytes(M, n_valid, w_rows) bytes. M = 0 is a no-op. */
+ * logits_scratch_bytes(M, K, n_valid, w_rows) bytes. M = 0 is a no-op. */
 int logits_pad_mask_argmax(const uint16_t *x, int64_t M, int32_t K, const uint16_t *w, int64_t w_rows,
                            int64_t n_valid, uint16_t *logits, int64_t ld_logits, int64_t *argmax,
                            void *scratch, size_t scratch_bytes, void *stream);
@@ -169,8 +169,10 @@ int logits_pad_mask_argmax(const uint16_t *x, int64_t M, int32_t K, const uint16
  * [P1046 Summary]. Pure host function. */
 int64_t logits_padded_width(int64_t n_valid, int64_t w_rows);
 
-/* Scratch needed by logits_pad_mask_argmax. Pure host function. */
-size_t logits_scratch_bytes(int64_t M, int64_t n_valid, int64_t w_rows);
+/* Scratch needed by logits_pad_mask_argmax: per-wave (max, index) pairs and a
+ * copy of x in MFMA fragment order. 0 for invalid arguments. Pure host
+ * function. */
+size_t logits_scratch_bytes(int64_t M, int32_t K, int64_t n_valid, int64_t w_rows);
 
 /* Test hook: states[k * N + n] = the 16-bit trellis state behind W[k][n]. */
 int exl3_decode_states(const exl3_layer *layer, uint16_t *states, void *stream);

@@ -53,8 +53,9 @@ def test_scratch_sizes():
     assert 16 * 5120 * 2 + 17408 * 5120 * 2 <= pre <= 16 * 5120 * 2 + 17408 * 5120 * 2 + 256 * 256 * 256 * 4
     assert L.exl3_linear_scratch_bytes(100, 128, 1, 128) == 0
     assert L.exl3_linear_scratch_bytes(128, 128, 0, 128) == 0
-    assert L.logits_scratch_bytes(16, 248077, 248320) > 0
-    assert L.logits_scratch_bytes(16, 0, 10) == 0
+    assert L.logits_scratch_bytes(16, 5120, 248077, 248320) >= 16 * 5120 * 2  # includes the fragment-ordered x
+    assert L.logits_scratch_bytes(16, 5120, 0, 10) == 0
+    assert L.logits_scratch_bytes(16, -128, 248077, 248320) == 0
 
 
 def _layer(K=256, N=256, bits=4, codes=0x1000, cb=0x2000, scale=0x3000):

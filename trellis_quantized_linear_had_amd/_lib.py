@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
         L.logits_pad_mask_argmax.restype = ctypes.c_int
         L.logits_padded_width.argtypes = [i64, i64]
         L.logits_padded_width.restype = i64
-        L.logits_scratch_bytes.argtypes = [i64, i64, i64]
+        L.logits_scratch_bytes.argtypes = [i64, i32, i64, i64]
         L.logits_scratch_bytes.restype = sz
         L.exl3_decode_states.argtypes = [ctypes.POINTER(Exl3Layer), vp, vp]
         L.exl3_decode_states.restype = ctypes.c_int
@@ -187,8 +187,8 @@ def logits_padded_width(n_valid: int, w_rows: int) -> int:
     return int(lib().logits_padded_width(n_valid, w_rows))
 
 
-def logits_scratch_bytes(M: int, n_valid: int, w_rows: int) -> int:
-    return int(lib().logits_scratch_bytes(M, n_valid, w_rows))
+def logits_scratch_bytes(M: int, K: int, n_valid: int, w_rows: int) -> int:
+    return int(lib().logits_scratch_bytes(M, K, n_valid, w_rows))
 
 
 def logits_pad_mask_argmax(x: torch.Tensor, w: torch.Tensor, n_valid: int, scratch=None, logits=None,
@@ -202,7 +202,7 @@ def logits_pad_mask_argmax(x: torch.Tensor, w: torch.Tensor, n_valid: int, scrat
     if argmax is None:
         argmax = torch.empty(M, dtype=torch.int64, device=x.device)
     if scratch is None:
-        scratch = torch.empty(max(logits_scratch_bytes(M, n_valid, w_rows), 1), dtype=torch.uint8, device=x.device)
+        scratch = torch.empty(max(logits_scratch_bytes(M, K, n_valid, w_rows), 1), dtype=torch.uint8, device=x.device)
     check(lib().logits_pad_mask_argmax(_ptr(x), M, K, _ptr(w), w_rows, n_valid, _ptr(logits), ld_logits,
                                        _ptr(argmax), _ptr(scratch), scratch.numel(), _stream(stream)))
     return logits, argmax

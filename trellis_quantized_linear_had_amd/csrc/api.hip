@@ -34,8 +34,10 @@ hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, in
                            int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream);
 size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K);
 hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int64_t n_valid, int64_t n_pad,
-                         uint16_t* logits, int64_t ld, int64_t* argmax, float* pv, int32_t* pi, hipStream_t stream);
+                         uint16_t* logits, int64_t ld, int64_t* argmax, float* pv, int32_t* pi, uint16_t* xp,
+                         hipStream_t stream);
 int64_t logits_items(int64_t n_pad);
+size_t logits_xperm_bytes(int64_t M, int32_t K);
 }  // namespace exl3
 
 using namespace exl3;
@@ -356,11 +358,11 @@ int64_t logits_padded_width(int64_t n_valid, int64_t w_rows) {
   return std::min(aligned, w_rows);
 }
 
-size_t logits_scratch_bytes(int64_t M, int64_t n_valid, int64_t w_rows) {
+size_t logits_scratch_bytes(int64_t M, int32_t K, int64_t n_valid, int64_t w_rows) {
   const int64_t n_pad = logits_padded_width(n_valid, w_rows);
-  if (n_pad < 0 || M < 0) return 0;
+  if (n_pad < 0 || M < 0 || K < 0) return 0;
   const int64_t items = logits_items(n_pad);
-  return align256((size_t)items * M * 4) * 2;
+  return align256((size_t)items * M * 4) * 2 + align256(logits_xperm_bytes(M, K));
 }
 
 int logits_pad_mask_argmax(const uint16_t* x, int64_t M, int32_t K, const uint16_t* w, int64_t w_rows,
@@ -381,7 +383,7 @@ int logits_pad_mask_argmax(const uint16_t* x, int64_t M, int32_t K, const uint16
   if (!aligned16(x) || !aligned16(w) || ((uintptr_t)logits & 1) || ((uintptr_t)argmax & 7) ||
       ((uintptr_t)scratch & 255u))
     return fail(EXL3_EINVAL, "misaligned pointer");
-  const size_t need = logits_scratch_bytes(M, n_valid, w_rows);
+  const size_t need = logits_scratch_bytes(M, K, n_valid, w_rows);
   if (scratch_bytes < need)
     return fail(EXL3_ESCRATCH, "scratch has %zu bytes; this call needs %zu", scratch_bytes, need);
   int st = check_device();
@@ -389,7 +391,8 @@ int logits_pad_mask_argmax(const uint16_t* x, int64_t M, int32_t K, const uint16
   const int64_t items = logits_items(n_pad);
   float* pv = (float*)scratch;
   int32_t* pi = (int32_t*)((char*)scratch + align256((size_t)items * M * 4));
-  EXL3_TRY(launch_logits(x, (int32_t)M, K, w, n_valid, n_pad, logits, ld_logits, argmax, pv, pi,
+  uint16_t* xp = (uint16_t*)((char*)scratch + align256((size_t)items * M * 4) * 2);
+  EXL3_TRY(launch_logits(x, (int32_t)M, K, w, n_valid, n_pad, logits, ld_logits, argmax, pv, pi, xp,
                          (hipStream_t)stream_),
            "logits");
   return EXL3_OK;

@@ -6,17 +6,25 @@
 // decodable vocabulary).
 //
 // HBM-bound: each weight row is streamed once (2 bytes per element). A wave
-// owns 64 consecutive weight rows (four 16-row MFMA tiles) over all of K and
-// feeds them to v_mfma_f32_16x16x32_f16 as the A operand, with up to 16 rows of
-// x as the B operand. Inside a 128-wide k chunk, MFMA step s takes the k slice
+// owns 128 consecutive weight rows (eight 16-row MFMA tiles) over all of K and
+// feeds them to v_mfma_f32_16x16x32_f16 as the A operand, with 16 rows of x as
+// the B operand. Inside a 64-wide k chunk, MFMA step s takes the k slice
 // 32 s + 8 g .. + 8 in lane group g on both operands (a permutation of k, which
 // leaves the dot products unchanged), so each 16-byte load instruction reads
-// 64 contiguous bytes of each of 16 rows.
+// 64 contiguous bytes of each of 16 weight rows. A pre-pass stores x in that
+// fragment order (rows past M zero), so each B-fragment load reads 1 KiB of
+// contiguous memory instead of 16 rows 2K bytes apart, which measured ~40 us
+// slower per call at M = 16 (the row-strided lines crowd a few L2 channels).
+// The loads of the next chunk are issued before the MFMAs of the current one.
 #include "common.h"
 
 namespace exl3 {
 
 #define LG_WAVES 4
+#define LG_ROWS 128             // weight rows per wave
+#define LG_TILES (LG_ROWS / 16)
+#define LG_KC 64                // k per chunk
+#define LG_STEPS (LG_KC / 32)
 
 __device__ __forceinline__ void argmax_combine(float& bv, int& bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) {
@@ -25,7 +33,45 @@ __device__ __forceinline__ void argmax_combine(float& bv, int& bi, float v, int 
   }
 }
 
-__global__ __launch_bounds__(64 * LG_WAVES) void logits_kernel(const uint16_t* __restrict__ x, int32_t M, int32_t K,
+// x (M x K) -> xp[mg][j][g][q][0..8) = x[16 mg + q][32 j + 8 g + 0..8], zero
+// for rows past M: the B fragment of lane (g, q) at k-step j, for row group
+// mg, is 16 contiguous bytes and a wave's 64 fragments are 1 KiB.
+__global__ __launch_bounds__(256) void logits_xperm_kernel(const uint16_t* __restrict__ x, int32_t M, int32_t K,
+                                                           uint16_t* __restrict__ xp, int64_t nchunks) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16-byte chunk of xp
+  if (c >= nchunks) return;
+  const int q = (int)(c & 15), g = (int)((c >> 4) & 3);
+  const int64_t jm = c >> 6;  // mg * (K / 32) + j
+  const int64_t mg = jm / (K / 32), j = jm - mg * (K / 32);
+  const int64_t row = mg * 16 + q;
+  u32x4 v = {0, 0, 0, 0};
+  if (row < M) v = *reinterpret_cast<const u32x4*>(x + row * K + 32 * j + 8 * g);
+  *reinterpret_cast<u32x4*>(xp + c * 8) = v;
+}
+
+// Loads one LG_KC-wide chunk: LG_TILES x LG_STEPS weight fragments and the
+// LG_STEPS x fragments.
+__device__ __forceinline__ void logits_load_chunk(const uint16_t* const (&wrow)[LG_TILES], const uint16_t* xfrag,
+                                                  int kc, u32x4 (&av)[LG_TILES][LG_STEPS], u32x4 (&bv)[LG_STEPS]) {
+#pragma unroll
+  for (int t = 0; t < LG_TILES; ++t)
+#pragma unroll
+    for (int s = 0; s < LG_STEPS; ++s) av[t][s] = *reinterpret_cast<const u32x4*>(wrow[t] + kc + 32 * s);
+#pragma unroll
+  for (int s = 0; s < LG_STEPS; ++s) bv[s] = *reinterpret_cast<const u32x4*>(xfrag + (int64_t)(kc / 32 + s) * 64 * 8);
+}
+
+__device__ __forceinline__ void logits_mfma_chunk(const u32x4 (&av)[LG_TILES][LG_STEPS], const u32x4 (&bv)[LG_STEPS],
+                                                  f32x4 (&acc)[LG_TILES]) {
+#pragma unroll
+  for (int s = 0; s < LG_STEPS; ++s)
+#pragma unroll
+    for (int t = 0; t < LG_TILES; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av[t][s]),
+                                                      __builtin_bit_cast(f16x8, bv[s]), acc[t], 0, 0, 0);
+}
+
+__global__ __launch_bounds__(64 * LG_WAVES) void logits_kernel(const uint16_t* __restrict__ xp, int32_t M, int32_t K,
                                                                const uint16_t* __restrict__ w, int64_t n_valid,
                                                                int64_t n_pad, uint16_t* __restrict__ logits,
                                                                int64_t ld, bool vec_store, float* __restrict__ pv,
@@ -34,48 +80,43 @@ __global__ __launch_bounds__(64 * LG_WAVES) void logits_kernel(const uint16_t* _
   if (item >= n_items) return;  // whole wave; no workgroup barriers below
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, pl = lane & 15;
-  const int64_t p0 = item * 64;
+  const int64_t p0 = item * LG_ROWS;
   const int q = m0 + pl;
 
-  f32x4 acc[4];
+  f32x4 acc[LG_TILES];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < LG_TILES; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* wrow[4];
-  bool wok[4];
+  // Rows past the padded width read row 0 instead (valid memory, no branch
+  // in the loop); their sums are never stored or ranked.
+  const uint16_t* wrow[LG_TILES];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < LG_TILES; ++t) {
     const int64_t row = p0 + 16 * t + pl;
-    wok[t] = row < n_pad;
-    wrow[t] = w + (wok[t] ? row : 0) * (int64_t)K + 8 * g;
+    wrow[t] = w + (row < n_pad ? row : 0) * (int64_t)K + 8 * g;
   }
-  const bool qok = q < M;
-  const uint16_t* xrow = x + (int64_t)(qok ? q : 0) * K + 8 * g;
+  const uint16_t* xfrag = xp + ((int64_t)(m0 / 16) * (K / 32) * 64 + lane) * 8;
 
-  for (int kc = 0; kc < K; kc += 128) {
-    u32x4 av[4][4], bv[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        av[t][s] = wok[t] ? *reinterpret_cast<const u32x4*>(wrow[t] + kc + 32 * s) : (u32x4){0, 0, 0, 0};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      bv[s] = qok ? *reinterpret_cast<const u32x4*>(xrow + kc + 32 * s) : (u32x4){0, 0, 0, 0};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av[t][s]),
-                                                        __builtin_bit_cast(f16x8, bv[s]), acc[t], 0, 0, 0);
+  // Two chunk buffers: chunk c + 1 is in flight while the MFMAs of chunk c
+  // run (K is a multiple of 128, so chunks come in pairs).
+  u32x4 av0[LG_TILES][LG_STEPS], bv0[LG_STEPS], av1[LG_TILES][LG_STEPS], bv1[LG_STEPS];
+  logits_load_chunk(wrow, xfrag, 0, av0, bv0);
+  for (int kc = 0; kc < K; kc += 2 * LG_KC) {
+    logits_load_chunk(wrow, xfrag, kc + LG_KC, av1, bv1);
+    __builtin_amdgcn_sched_barrier(0);
+    logits_mfma_chunk(av0, bv0, acc);
+    if (kc + 2 * LG_KC < K) logits_load_chunk(wrow, xfrag, kc + 2 * LG_KC, av0, bv0);  // uniform
+    __builtin_amdgcn_sched_barrier(0);
+    logits_mfma_chunk(av1, bv1, acc);
   }
 
   // Epilogue: lane holds D[p = p0 + 16t + 4g + r][q]; round to fp16, mask the
   // pad columns, store, and keep the first maximum.
+  const bool qok = q < M;
   float best = -__builtin_inff();
   int besti = 0x7FFFFFFF;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < LG_TILES; ++t) {
     const int64_t pb = p0 + 16 * t + 4 * g;
     uint16_t h[4];
 #pragma unroll
@@ -104,9 +145,9 @@ __global__ __launch_bounds__(64 * LG_WAVES) void logits_kernel(const uint16_t* _
     const int i2 = __shfl_xor(besti, o);
     argmax_combine(best, besti, v2, i2);
   }
-  if (g == 0 && qok) {
-    pv[item * M + q] = best;
-    pi[item * M + q] = besti;
+  if (g == 0 && qok) {  // pairs stored [q][item]: the final pass reads each row contiguously
+    pv[(int64_t)q * n_items + item] = best;
+    pi[(int64_t)q * n_items + item] = besti;
   }
 }
 
@@ -119,7 +160,9 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const float* __restri
   const int q = blockIdx.x;
   float best = -__builtin_inff();
   int besti = 0x7FFFFFFF;
-  for (int64_t it = threadIdx.x; it < n_items; it += 256) argmax_combine(best, besti, pv[it * M + q], pi[it * M + q]);
+  const float* rv = pv + (int64_t)q * n_items;
+  const int32_t* ri = pi + (int64_t)q * n_items;
+  for (int64_t it = threadIdx.x; it < n_items; it += 256) argmax_combine(best, besti, rv[it], ri[it]);
   sv[threadIdx.x] = best;
   si[threadIdx.x] = besti;
   __syncthreads();
@@ -136,15 +179,23 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const float* __restri
   if (threadIdx.x == 0) out[q] = si[0];
 }
 
-int64_t logits_items(int64_t n_pad) { return (n_pad + 63) / 64; }
+int64_t logits_items(int64_t n_pad) { return (n_pad + LG_ROWS - 1) / LG_ROWS; }
+
+// fragment-ordered copy of x: 16-row groups, K fp16 each
+size_t logits_xperm_bytes(int64_t M, int32_t K) { return (size_t)((M + 15) / 16) * 16 * K * 2; }
 
 hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int64_t n_valid, int64_t n_pad,
-                         uint16_t* logits, int64_t ld, int64_t* argmax, float* pv, int32_t* pi, hipStream_t stream) {
+                         uint16_t* logits, int64_t ld, int64_t* argmax, float* pv, int32_t* pi, uint16_t* xp,
+                         hipStream_t stream) {
   const int64_t n_items = logits_items(n_pad);
   const bool vec = (ld % 4) == 0 && ((uintptr_t)logits % 8) == 0;
+  const int64_t xchunks = (int64_t)logits_xperm_bytes(M, K) / 16;
+  logits_xperm_kernel<<<(unsigned)((xchunks + 255) / 256), 256, 0, stream>>>(x, M, K, xp, xchunks);
+  hipError_t e0 = hipGetLastError();
+  if (e0 != hipSuccess) return e0;
   const unsigned grid = (unsigned)((n_items + LG_WAVES - 1) / LG_WAVES);
   for (int32_t m0 = 0; m0 < M; m0 += 16) {
-    logits_kernel<<<grid, 64 * LG_WAVES, 0, stream>>>(x, M, K, w, n_valid, n_pad, logits, ld, vec, pv, pi, n_items,
+    logits_kernel<<<grid, 64 * LG_WAVES, 0, stream>>>(xp, M, K, w, n_valid, n_pad, logits, ld, vec, pv, pi, n_items,
                                                       m0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
