@@ -43,11 +43,20 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 skips it)")
     ap.add_argument("--no-logits", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("KIND", "FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="print the traffic summary (markdown with a JSON block) of two rocprofv3 --pmc "
+                         "counter_collection.csv files taken over --pmc-workload KIND")
+    ap.add_argument("--pmc-workload", choices=("logits", "gemm", "decode"), default=None,
+                    help="run only a counter-collection workload: two 1 GiB device copies (calibration) then "
+                         "three calls of the named path; prints nothing else")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        print(pmc_summary(*args.pmc_summary))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -57,6 +66,10 @@ def main():
 
     import trellis_quantized_linear_had_amd as X
     from trellis_quantized_linear_had_amd import _lib
+
+    if args.pmc_workload:
+        pmc_workload(args.pmc_workload)
+        return
 
     lib = _lib.lib()
     dev = torch.device("cuda:0")
@@ -154,27 +167,67 @@ def main():
     value = len(DEC_M) * CODE_BYTES / (dec_seg_ms * 1e-3) / 1e9
     pre_tflops = PREFILL_FLOP / (pre_ms * 1e-3) / 1e12
     logits_bytes = n_pad * K * 2
-    rooflines = {
-        "decode_m16": {"bound": "hbm", "achieved": CODE_BYTES / (dec_ms[16] * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
-                       "unit": "GB/s", "us": dec_ms[16] * 1e3,
-                       "per_launch": "44564480 B packed codes (K5120 x N17408 x 0.5 B)"},
-        "prefill_m2048": {"bound": "mfma", "achieved": pre_tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "us": pre_ms * 1e3, "per_launch": "2*2048*5120*17408 FLOP incl. rotations + reconstruct"},
-    }
-    if log_ms is not None:
-        rooflines["logits_m16"] = {"bound": "hbm", "achieved": logits_bytes / (log_ms * 1e-3) / 1e9,
-                                   "peak": HBM_PEAK_GBPS, "unit": "GB/s", "us": log_ms * 1e3,
-                                   "per_launch": "%d B fp16 weight rows read (248192 x 5120 x 2)" % logits_bytes}
-    for r in rooflines.values():
+
+    # Per-kernel times: the library's event hook brackets the main kernel of
+    # each call on this stream (decode GEMM, full-tile prefill GEMM, logits
+    # GEMM); a separate loop after the timed steps, so the hook's event
+    # records never sit inside the timed region.
+    reps = 12
+    kern_us = {}
+    _lib.kernel_timer(True)
+    try:
+        for M in DEC_M:
+            for r in range(reps):
+                call_linear(dec_layers[r % 12], xs[M], M, ys[M], dec_scratch)
+            ms, n = _lib.kernel_timer_read(_lib.TIMER_DECODE)
+            kern_us["decode_gemm_kernel M=%d" % M] = ms / n * 1e3
+        for r in range(reps // 2):
+            call_linear(pre_layers[r % 6], xp, PREFILL_M, yp, pre_scratch)
+        ms, n = _lib.kernel_timer_read(_lib.TIMER_GEMM)
+        kern_us["gemm_had_kernel<0> M=2048"] = ms / n * 1e3
+        if not args.no_logits:
+            for r in range(reps // 2):
+                call_logits()
+            ms, n = _lib.kernel_timer_read(_lib.TIMER_LOGITS)
+            kern_us["logits_kernel M=16"] = ms / n * 1e3
+    finally:
+        _lib.kernel_timer(False)
+    torch.cuda.synchronize()
+
+    # Algorithmic work per launch: packed codes read by the decode GEMM; 2MNK
+    # FLOP over the full-tile launch's 512 of 544 256x256 tiles; fp16 weight
+    # rows read by the logits GEMM.
+    tiles = (N // 256) * (PREFILL_M // 256)       # 544 output tiles of 256 x 256
+    full_tiles = tiles // 256 * 256                 # 512 run at full K; the rest are split along K
+    gemm_full_flop = 2 * 256 * 256 * K * full_tiles
+    kernels = {}
+    for M in DEC_M:
+        us = kern_us["decode_gemm_kernel M=%d" % M]
+        kernels["decode_gemm_kernel M=%d" % M] = {
+            "bound": "hbm", "achieved": CODE_BYTES / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "us": us, "per_launch": "%d B packed codes (K5120 x N17408 x 0.5 B)" % CODE_BYTES}
+    us = kern_us["gemm_had_kernel<0> M=2048"]
+    kernels["gemm_had_kernel<0> M=2048"] = {
+        "bound": "mfma", "achieved": gemm_full_flop / (us * 1e-6) / 1e12, "peak": MFMA_F16_PEAK_TFLOPS,
+        "unit": "TFLOP/s", "us": us, "per_launch": "%d FLOP (2*256*256*5120 x %d full tiles)" % (gemm_full_flop, full_tiles)}
+    if not args.no_logits:
+        us = kern_us["logits_kernel M=16"]
+        kernels["logits_kernel M=16"] = {
+            "bound": "hbm", "achieved": logits_bytes / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "us": us, "per_launch": "%d B fp16 weight rows read (248192 x 5120 x 2)" % logits_bytes}
+    for r in kernels.values():
         r["frac"] = r["achieved"] / r["peak"]
-    # the dominant part of the step by GPU time
-    times = {"decode_m16": dec_ms[16], "prefill_m2048": pre_ms}
-    if log_ms is not None:
-        times["logits_m16"] = log_ms
-    dom = max(times, key=times.get)
-    roof = dict(rooflines[dom])
-    roof["kernel"] = dom
-    roof["traffic"] = None
+    # the dominant kernel: most GPU time per step (the decode GEMM runs once
+    # per row count, the others once)
+    step_us = {k: v["us"] for k, v in kernels.items() if not k.startswith("decode")}
+    step_us["decode_gemm_kernel"] = sum(kernels["decode_gemm_kernel M=%d" % M]["us"] for M in DEC_M)
+    dom = max(step_us, key=step_us.get)
+    dom_key = "decode_gemm_kernel M=16" if dom == "decode_gemm_kernel" else dom
+    roof = {k: kernels[dom_key][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof["traffic"] = stored_traffic(dom_key)
+    roof["kernel"] = dom_key
+    roof["us"] = kernels[dom_key]["us"]
+    roof["per_launch"] = kernels[dom_key]["per_launch"]
 
     result = {
         "metric": "decode GB/s + us/call at M=1..16; prefill TFLOP/s at M=2048, K5120xN17408",
@@ -200,13 +253,129 @@ def main():
         "prefill_tflops": round(pre_tflops, 1),
         "logits_us_per_call": None if log_ms is None else round(log_ms * 1e3, 2),
         "roofline": roof,
-        "rooflines": rooflines,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
         "cpu_baseline": None,
     }
 
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, log)
     print(json.dumps(result), flush=True)
+
+
+COPY_BYTES = 1 << 30
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "trellis_quantized_linear_had_amd", "csrc")
+# kernel name in the counter files, the key used in the bench line, and the
+# sources whose change makes a stored traffic figure stale
+PMC_KERNELS = {
+    "logits": ("exl3::logits_kernel", "logits_kernel M=16", ("logits.hip", "common.h")),
+    "gemm": ("exl3::gemm_had_kernel<0>", "gemm_had_kernel<0> M=2048", ("gemm_f16.hip", "common.h")),
+    "decode": ("exl3::decode_gemm_kernel<6, true>", "decode_gemm_kernel M=16",
+               ("decode_gemm.hip", "decode_plan.h", "trellis.h", "common.h")),
+}
+
+
+def sources_sha256(names) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def pmc_summary(kind: str, fetch_csv: str, write_csv: str) -> str:
+    """Per-dispatch HBM traffic of one kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for the
+    workload's 1 GiB device copy (COPY_BYTES read and written)."""
+    import csv
+
+    kname, key, srcs = PMC_KERNELS[kind]
+
+    def per_kernel(path):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            out.setdefault(r["Kernel_Name"].split("(")[0].replace("void ", ""), []).append(float(r["Counter_Value"]))
+        return out
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    copy = "__amd_rocclr_copyBuffer"
+    f_scale = COPY_BYTES / (sum(fetch[copy]) / len(fetch[copy]) * 1024)
+    w_scale = COPY_BYTES / (sum(write[copy]) / len(write[copy]) * 1024)
+    f_kib = sum(fetch[kname]) / len(fetch[kname])
+    w_kib = sum(write[kname]) / len(write[kname])
+    fetch_b, write_b = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
+    rec = {"kernel": key, "source_sha256": sources_sha256(srcs), "fetch_kib_raw": round(f_kib, 1),
+           "write_kib_raw": round(w_kib, 1), "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+           "fetch_bytes": round(fetch_b), "write_bytes": round(write_b), "traffic_bytes": round(fetch_b + write_b),
+           "dispatches": [len(fetch[kname]), len(write[kname])]}
+    lines = ["| counter | copy of 1 GiB (KiB) | scale | `%s` per dispatch (KiB) | scaled bytes |" % kname,
+             "|---|---|---|---|---|",
+             "| FETCH_SIZE | %.1f | %.5f | %.1f | %d |" % (sum(fetch[copy]) / len(fetch[copy]), f_scale, f_kib, fetch_b),
+             "| WRITE_SIZE | %.1f | %.5f | %.1f | %d |" % (sum(write[copy]) / len(write[copy]), w_scale, w_kib, write_b)]
+    return "\n".join(lines) + "\n\n```json\n" + json.dumps(rec) + "\n```\n"
+
+
+def stored_traffic(key: str):
+    """HBM bytes per launch of a kernel from its committed counter summary
+    (profiles/*traffic*.md), or None if there is none or the kernel's sources
+    changed since the counters were taken."""
+    import glob
+    import re
+
+    kind = next((k for k, v in PMC_KERNELS.items() if v[1] == key), None)
+    if kind is None:
+        return None
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        for block in re.findall(r"```json\n(.*?)\n```", open(path).read(), re.S):
+            rec = json.loads(block)
+            if rec.get("kernel") == key and rec.get("source_sha256") == sources_sha256(PMC_KERNELS[kind][2]):
+                return rec["traffic_bytes"]
+    return None
+
+
+def pmc_workload(kind: str):
+    """Counter-collection workload: a plain 1 GiB device-to-device copy twice
+    (reads and writes COPY_BYTES each: the calibration of FETCH_SIZE /
+    WRITE_SIZE), then three calls of one path at the bench's shapes."""
+    import torch
+
+    import trellis_quantized_linear_had_amd as X
+    from trellis_quantized_linear_had_amd import _lib
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    lib = _lib.lib()
+    sh = torch.cuda.current_stream().cuda_stream
+    cb = W.codebook()
+    if kind == "logits":
+        lc = W.LOGITS
+        n_valid, w_rows = lc["n_valid"], lc["w_rows"]
+        n_pad = X.logits_padded_width(n_valid, w_rows)
+        wl = _lib.to_device_u16(W.logits_weights(lc["seed"], w_rows, K, threads=16))
+        xl = _lib.to_device_u16(W.activations(lc["seed"], LOGITS_M, K))
+        lg = torch.empty((LOGITS_M, n_pad), dtype=torch.int16, device=dev)
+        am = torch.empty(LOGITS_M, dtype=torch.int64, device=dev)
+        scr = torch.empty(X.logits_scratch_bytes(LOGITS_M, K, n_valid, w_rows), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            _lib.check(lib.logits_pad_mask_argmax(xl.data_ptr(), LOGITS_M, K, wl.data_ptr(), w_rows, n_valid,
+                                                  lg.data_ptr(), n_pad, am.data_ptr(), scr.data_ptr(), scr.numel(), sh))
+    else:
+        M = PREFILL_M if kind == "gemm" else max(DEC_M)
+        layer = X.Layer.from_numpy(W.layer(W.SEED_PREFILL if kind == "gemm" else W.SEED_DECODE, K, N, 0), cb)
+        x = _lib.to_device_u16(W.activations(W.SEED_PREFILL if kind == "gemm" else W.SEED_DECODE, M, K, 0))
+        y = torch.empty((M, N), dtype=torch.int16, device=dev)
+        scr = torch.empty(X.linear_scratch_bytes(K, N, M), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            _lib.check(lib.exl3_linear(layer.c, x.data_ptr(), M, y.data_ptr(), scr.data_ptr(), scr.numel(), 128, sh))
+    torch.cuda.synchronize()
+    print("[bench] pmc workload %s done" % kind, file=sys.stderr, flush=True)
 
 
 def cpu_baseline(target_s: float, log):

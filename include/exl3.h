@@ -177,6 +177,19 @@ size_t logits_scratch_bytes(int64_t M, int32_t K, int64_t n_valid, int64_t w_row
 /* Test hook: states[k * N + n] = the 16-bit trellis state behind W[k][n]. */
 int exl3_decode_states(const exl3_layer *layer, uint16_t *states, void *stream);
 
+/* Measurement hook (for benchmarks; not used by the hot path). While enabled
+ * (on != 0), every later call records a pair of HIP events on its stream
+ * around one kernel: kind 0 the decode GEMM of exl3_linear, kind 1 the
+ * full-tile launch of the prefill GEMM (one per column slice), kind 2 the
+ * logits GEMM (one per 16-row group). Enabling costs an event creation per
+ * timed launch; leave it off under graph capture. */
+int exl3_kernel_timer_enable(int on);
+
+/* Waits for the recorded event pairs of one kind, returns their summed
+ * milliseconds and their count, and forgets them. EXL3_EINVAL for an unknown
+ * kind or NULL outputs; EXL3_EHIP if an event fails. */
+int exl3_kernel_timer_read(int kind, double *total_ms, int64_t *count);
+
 /* Human-readable text for a status; for EXL3_EHIP and validation failures it
  * names the condition of the most recent failing call on this thread. */
 const char *exl3_strerror(int status);

@@ -121,3 +121,15 @@ def test_logits_validation():
     assert call(x=0) == X.EXL3_EINVAL
     assert call(nbytes=0) == X.EXL3_ESCRATCH
     assert call(M=0) == X.EXL3_OK
+
+
+def test_kernel_timer_validation_without_gpu():
+    L = X.lib()
+    ms, n = ctypes.c_double(-1.0), ctypes.c_int64(-1)
+    assert L.exl3_kernel_timer_read(3, ctypes.byref(ms), ctypes.byref(n)) == X.EXL3_EINVAL
+    assert L.exl3_kernel_timer_read(-1, ctypes.byref(ms), ctypes.byref(n)) == X.EXL3_EINVAL
+    assert L.exl3_kernel_timer_read(0, None, ctypes.byref(n)) == X.EXL3_EINVAL
+    # nothing recorded: no HIP call, zero launches
+    assert L.exl3_kernel_timer_read(2, ctypes.byref(ms), ctypes.byref(n)) == X.EXL3_OK
+    assert (ms.value, n.value) == (0.0, 0)
+    assert L.exl3_kernel_timer_enable(0) == X.EXL3_OK

@@ -13,9 +13,12 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "exl3.h"
 #include "decode_plan.h"
+#include "timer.h"
 
 namespace exl3 {
 hipError_t launch_had128(const uint16_t* in, uint16_t* out, int64_t rows, int64_t cols, const uint16_t* sign_pre,
@@ -38,6 +41,46 @@ hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t
                          hipStream_t stream);
 int64_t logits_items(int64_t n_pad);
 size_t logits_xperm_bytes(int64_t M, int32_t K);
+}  // namespace exl3
+
+// Measurement hook state. Events are created only while the hook is on.
+namespace exl3 {
+namespace {
+struct TimedLaunch {
+  int kind;
+  hipEvent_t start, stop;
+};
+std::mutex g_timer_mu;
+std::vector<TimedLaunch> g_timed;
+std::atomic<bool> g_timer_on{false};
+thread_local hipEvent_t t_open[kTimerKinds] = {nullptr, nullptr, nullptr};
+}  // namespace
+
+void timer_begin(int kind, hipStream_t stream) {
+  if (t_open[kind]) {  // an earlier launch of this kind failed before its end
+    hipEventDestroy(t_open[kind]);
+    t_open[kind] = nullptr;
+  }
+  if (!g_timer_on.load(std::memory_order_relaxed)) return;
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return;
+  hipEventRecord(e, stream);
+  t_open[kind] = e;
+}
+
+void timer_end(int kind, hipStream_t stream) {
+  hipEvent_t a = t_open[kind];
+  if (!a) return;
+  t_open[kind] = nullptr;
+  hipEvent_t b = nullptr;
+  if (hipEventCreate(&b) != hipSuccess) {
+    hipEventDestroy(a);
+    return;
+  }
+  hipEventRecord(b, stream);
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  g_timed.push_back(TimedLaunch{kind, a, b});
+}
 }  // namespace exl3
 
 using namespace exl3;
@@ -284,12 +327,16 @@ int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
     uint16_t* xr = (uint16_t*)(sb + l.xr_off);
     float* part = (float*)(sb + l.part_off);
     if (l.plan.x_in_lds) {
+      timer_begin(kTimerDecode, stream);
       EXL3_TRY(launch_decode_gemm(x, L->sign_k, L->codes, L->codebook, part, K, N, (int32_t)M, l.plan, stream),
                "decode gemm");
+      timer_end(kTimerDecode, stream);
     } else {
       EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
+      timer_begin(kTimerDecode, stream);
       EXL3_TRY(launch_decode_gemm(xr, nullptr, L->codes, L->codebook, part, K, N, (int32_t)M, l.plan, stream),
                "decode gemm");
+      timer_end(kTimerDecode, stream);
     }
     EXL3_TRY(launch_decode_finalize(part, l.plan.ks_count, L->scale, L->sign_n, y, (int32_t)M, N, stream),
              "decode finalize");
@@ -399,3 +446,37 @@ int logits_pad_mask_argmax(const uint16_t* x, int64_t M, int32_t K, const uint16
 }
 
 }  // extern "C"
+
+int exl3_kernel_timer_enable(int on) {
+  g_timer_on.store(on != 0);
+  return EXL3_OK;
+}
+
+int exl3_kernel_timer_read(int kind, double* total_ms, int64_t* count) {
+  g_msg[0] = 0;
+  if (kind < 0 || kind >= kTimerKinds) return fail(EXL3_EINVAL, "timer kind %d is not 0, 1 or 2", kind);
+  if (!total_ms || !count) return fail(EXL3_EINVAL, "total_ms or count is NULL");
+  std::vector<TimedLaunch> mine;
+  {
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    std::vector<TimedLaunch> rest;
+    for (const TimedLaunch& t : g_timed) (t.kind == kind ? mine : rest).push_back(t);
+    g_timed.swap(rest);
+  }
+  double sum = 0.0;
+  int st = EXL3_OK;
+  for (const TimedLaunch& t : mine) {
+    float ms = 0.f;
+    if (st == EXL3_OK) {
+      hipError_t e = hipEventSynchronize(t.stop);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+      if (e != hipSuccess) st = fail(EXL3_EHIP, "timer event: %s", hipGetErrorString(e));
+    }
+    sum += ms;
+    hipEventDestroy(t.start);
+    hipEventDestroy(t.stop);
+  }
+  *total_ms = sum;
+  *count = (int64_t)mine.size();
+  return st;
+}

@@ -35,6 +35,7 @@
 // share one 256-row strip of W^T run together on one XCD and read it through
 // that XCD's L2.
 #include "common.h"
+#include "timer.h"
 
 namespace exl3 {
 
@@ -371,9 +372,12 @@ hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, in
                            int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream) {
   const GemmPlan g = gemm_plan(P, Q, K);
   f32x4* part = reinterpret_cast<f32x4*>(partial);
-  if (g.full > 0)
+  if (g.full > 0) {
+    timer_begin(kTimerGemm, stream);
     gemm_had_kernel<0><<<8 * ((g.full + 7) / 8), G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, 0, g.full,
                                                                          1, part);
+    timer_end(kTimerGemm, stream);
+  }
   if (g.rem > 0) {
     gemm_had_kernel<1><<<g.rem * g.splits, G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, g.full, g.rem,
                                                                    g.splits, part);

@@ -17,6 +17,7 @@
 // slower per call at M = 16 (the row-strided lines crowd a few L2 channels).
 // The loads of the next chunk are issued before the MFMAs of the current one.
 #include "common.h"
+#include "timer.h"
 
 namespace exl3 {
 
@@ -195,8 +196,10 @@ hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t
   if (e0 != hipSuccess) return e0;
   const unsigned grid = (unsigned)((n_items + LG_WAVES - 1) / LG_WAVES);
   for (int32_t m0 = 0; m0 < M; m0 += 16) {
+    timer_begin(kTimerLogits, stream);
     logits_kernel<<<grid, 64 * LG_WAVES, 0, stream>>>(xp, M, K, w, n_valid, n_pad, logits, ld, vec, pv, pi, n_items,
                                                       m0);
+    timer_end(kTimerLogits, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
