@@ -24,10 +24,11 @@
 // SIMD.
 //
 // Tail balance: tiles are dealt to the 256 CUs in rounds. The largest
-// multiple of 256 tiles runs whole; the remaining tiles are cut along K into
-// S = floor(256 / rem) pieces so the last round is full, each piece writes its
-// fp32 accumulator tile (in register order) to scratch, and a fixup kernel
-// sums the S pieces in a fixed order and runs the same rotation epilogue.
+// multiple of 256 tiles runs whole; the k-steps of the remaining tiles are
+// spread evenly over (up to) 256 workgroups, stream-K style, each writing an
+// fp32 accumulator tile (in register order) per tile it touches, and a fixup
+// kernel sums each tile's pieces in k order and runs the same rotation
+// epilogue.
 //
 // Workgroup order is XCD-aware: workgroups are dispatched round-robin over
 // the 8 XCDs, so workgroup w is given tile (w % 8) * ceil(T / 8) + w / 8. Each
@@ -78,67 +79,74 @@ __device__ __forceinline__ void load_rows_lds(const uint16_t* __restrict__ g, in
                                      16, 0, 0);
 }
 
-// Output rotation + signs + fp16 store of one wave's 128 x 64 block.
-// acc[i][j][r] holds D[p][q] with (inside the wave's 128-row rotation block)
-// p = 32 i + 8 (r >> 2) + 4 lhalf + (r & 3), q = 32 j + lrow. Index bits of p:
-// 0,1 <- r&3; 2 <- lhalf; 3,4 <- r>>2; 5,6 <- i.
-__device__ __forceinline__ void rotate_store(f32x16 (&acc)[4][G_QT], int lane, int pw, int qw, int P, int Q,
-                                             uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
-                                             const uint16_t* __restrict__ sign_n) {
+// Output rotation + signs + fp16 store of one 128 (p) x 32 (q) block of a
+// wave. a[i][r] holds D[p][q] with (inside the 128-row rotation block)
+// p = 32 i + 8 (r >> 2) + 4 lhalf + (r & 3), q = q0 + lrow. Index bits of p:
+// 0,1 <- r&3; 2 <- lhalf; 3,4 <- r>>2; 5,6 <- i. Six stages in registers, one
+// across lanes 32 apart.
+__device__ __forceinline__ void rotate_store_block(f32x16 (&a)[4], int lane, int pw, int q0, int P, int Q,
+                                                   uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
+                                                   const uint16_t* __restrict__ sign_n) {
   const int lrow = lane & 31, lhalf = lane >> 5;
 #pragma unroll
-  for (int j = 0; j < G_QT; ++j) {
-#pragma unroll
-    for (int h = 1; h <= 8; h <<= 1) {  // register bits r&1, r&2, r&4, r&8
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if ((r & h) == 0) {
-            const float a = acc[i][j][r], b = acc[i][j][r + h];
-            acc[i][j][r] = a + b;
-            acc[i][j][r + h] = a - b;
-          }
-    }
-#pragma unroll
-    for (int h = 1; h <= 2; h <<= 1) {  // register bits of i
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if ((i & h) == 0)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float a = acc[i][j][r], b = acc[i + h][j][r];
-            acc[i][j][r] = a + b;
-            acc[i + h][j][r] = a - b;
-          }
-    }
-    const float s = lhalf ? -1.f : 1.f;  // lane bit: partner 32 lanes away
+  for (int h = 1; h <= 8; h <<= 1) {  // register bits r&1, r&2, r&4, r&8
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float partner = __shfl_xor(acc[i][j][r], 32);
-        acc[i][j][r] = __builtin_fmaf(s, acc[i][j][r], partner);
-      }
+      for (int r = 0; r < 16; ++r)
+        if ((r & h) == 0) {
+          const float u = a[i][r], v = a[i][r + h];
+          a[i][r] = u + v;
+          a[i][r + h] = u - v;
+        }
   }
+#pragma unroll
+  for (int h = 1; h <= 2; h <<= 1) {  // register bits of i
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if ((i & h) == 0)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float u = a[i][r], v = a[i + h][r];
+          a[i][r] = u + v;
+          a[i + h][r] = u - v;
+        }
+  }
+  const float s = lhalf ? -1.f : 1.f;  // lane bit: partner 32 lanes away
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float partner = __shfl_xor(a[i][r], 32);
+      a[i][r] = __builtin_fmaf(s, a[i][r], partner);
+    }
   if (pw >= P) return;
+  const int q = q0 + lrow;
+  if (q >= Q) return;
+  uint16_t* yrow = y + (int64_t)q * ldy + n0 + pw;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int p = 32 * i + 8 * g + 4 * lhalf;
+      u32x2 o;
+      o[0] = pack_f16x2(a[i][4 * g] * EXL3_INV_SQRT128, a[i][4 * g + 1] * EXL3_INV_SQRT128);
+      o[1] = pack_f16x2(a[i][4 * g + 2] * EXL3_INV_SQRT128, a[i][4 * g + 3] * EXL3_INV_SQRT128);
+      if (sign_n) o ^= (*reinterpret_cast<const u32x2*>(sign_n + n0 + pw + p) & 0x80008000u);
+      *reinterpret_cast<u32x2*>(yrow + p) = o;
+    }
+}
+
+// Epilogue of one wave's 128 x 64 block: two 32-wide q blocks.
+__device__ __forceinline__ void rotate_store(f32x16 (&acc)[4][G_QT], int lane, int pw, int qw, int P, int Q,
+                                             uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
+                                             const uint16_t* __restrict__ sign_n) {
 #pragma unroll
   for (int j = 0; j < G_QT; ++j) {
-    const int q = qw + 32 * j + lrow;
-    if (q < Q) {
-      uint16_t* yrow = y + (int64_t)q * ldy + n0 + pw;
+    f32x16 blk[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int p = 32 * i + 8 * g + 4 * lhalf;
-          u32x2 o;
-          o[0] = pack_f16x2(acc[i][j][4 * g] * EXL3_INV_SQRT128, acc[i][j][4 * g + 1] * EXL3_INV_SQRT128);
-          o[1] = pack_f16x2(acc[i][j][4 * g + 2] * EXL3_INV_SQRT128, acc[i][j][4 * g + 3] * EXL3_INV_SQRT128);
-          if (sign_n) o ^= (*reinterpret_cast<const u32x2*>(sign_n + n0 + pw + p) & 0x80008000u);
-          *reinterpret_cast<u32x2*>(yrow + p) = o;
-        }
-    }
+    for (int i = 0; i < 4; ++i) blk[i] = acc[i][j];
+    rotate_store_block(blk, lane, pw, qw + 32 * j, P, Q, y, ldy, n0, sign_n);
   }
 }
 
@@ -157,58 +165,30 @@ __device__ __forceinline__ void store_partial(const f32x16 (&acc)[4][G_QT], f32x
 }
 
 // MODE 0: workgroup w computes tile tile_base + t (t in XCD order, t < count)
-// over all of K and runs the rotation epilogue. MODE 1: workgroup w computes
-// k-piece w % splits of tile tile_base + w / splits and writes the partial.
+// over all of K and runs the rotation epilogue. MODE 1 (stream-K tail): the
+// count tiles' k-steps, tile-major, are dealt in runs of `units` to the
+// workgroups; piece v (the workgroup's place in XCD order) covers
+// [v units, (v + 1) units), at most two tiles (units <= K / G_BK), and
+// writes one partial per tile it touches into slot 2 v + (tile - first tile
+// of v).
 template <int MODE>
 __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __restrict__ A,
                                                              const uint16_t* __restrict__ B,
                                                              uint16_t* __restrict__ y, int32_t P, int32_t Q,
                                                              int32_t K, int64_t ldy, int32_t n0,
                                                              const uint16_t* __restrict__ sign_n, int32_t tile_base,
-                                                             int32_t count, int32_t splits,
+                                                             int32_t count, int32_t units,
                                                              f32x4* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * G_STAGE];
 
   const int tiles_q = (Q + G_BQ - 1) / G_BQ;
-  int t, kb0, kb1;
   const int nk_all = K / G_BK;
-  if (MODE == 0) {
-    const int per_xcd = (count + 7) / 8;
-    t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-    if (t >= count) return;  // whole workgroup (uniform)
-    kb0 = 0;
-    kb1 = nk_all;
-  } else {
-    t = blockIdx.x / splits;
-    const int sp = blockIdx.x % splits, per = (nk_all + splits - 1) / splits;
-    kb0 = min(sp * per, nk_all);
-    kb1 = min(kb0 + per, nk_all);
-  }
-  const int tile = tile_base + t;
-  const int p_base = (tile / tiles_q) * G_BP, q_base = (tile % tiles_q) * G_BQ;
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wp = wave & 1, wq = wave >> 1;
+  const int lrow = lane & 31, lhalf = lane >> 5;
 
   f32x16 acc[4][G_QT];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < G_QT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  uint32_t offa[4], offb[4];
-  lane_offsets(K, p_base, P, 32 * wave, lane, offa);
-  lane_offsets(K, q_base, Q, 32 * wave, lane, offb);
-  auto issue_loads = [&](int stage, int k0) {
-    uint16_t* st = smem + stage * G_STAGE;
-    load_rows_lds(A, k0, offa, st, 32 * wave);
-    load_rows_lds(B, k0, offb, st + G_BP * G_BK, 32 * wave);
-  };
-
-  const int lrow = lane & 31, lhalf = lane >> 5;
   // fragments of one k16 sub-step: 4 A tiles and 2 B tiles, two register sets
   f16x8 af[2][4], bf[2][G_QT];
   auto read_frags = [&](int stage, int s, int buf) {
@@ -233,11 +213,7 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
   // sub-step are all issued in its first half (read, MFMA three times, then
   // three reads), so they land under the remaining five MFMAs instead of
   // after them.
-#ifndef EXL3_GEMM_SCHED
-#define EXL3_GEMM_SCHED 2
-#endif
   auto interleave = [&]() {
-#if EXL3_GEMM_SCHED == 2
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
@@ -245,25 +221,34 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
-#elif EXL3_GEMM_SCHED == 1
-#pragma unroll
-    for (int k = 0; k < 6; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-#endif
   };
 
-  // Schedule per k step kb (stage buffer b = (kb - kb0) & 1):
+  // acc = sum over k-steps [kb0, kb1) of one tile. Schedule per k step kb
+  // (stage buffer b = (kb - kb0) & 1):
   //   sub-steps 0..2: read the next sub-step's fragments, then MFMAs;
   //   sub-step 3: its fragments are in registers; wait for this wave's loads of
   //   stage kb+1, barrier (every wave is done reading buffer b and stage kb+1
   //   has landed), issue the loads of stage kb+2 into buffer b, read sub-step 0
   //   of stage kb+1, and only then run sub-step 3's MFMAs, which cover the
   //   barrier and the fragment-read latency.
-  const int nk = kb1 - kb0;
-  if (nk > 0) {
+  // Ends with a barrier, so the stage buffers may be refilled at once.
+  auto run_tile = [&](int p_base, int q_base, int kb0, int kb1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < G_QT; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    uint32_t offa[4], offb[4];
+    lane_offsets(K, p_base, P, 32 * wave, lane, offa);
+    lane_offsets(K, q_base, Q, 32 * wave, lane, offb);
+    auto issue_loads = [&](int stage, int k0) {
+      uint16_t* st = smem + stage * G_STAGE;
+      load_rows_lds(A, k0, offa, st, 32 * wave);
+      load_rows_lds(B, k0, offb, st + G_BP * G_BK, 32 * wave);
+    };
+    const int nk = kb1 - kb0;
+    if (nk <= 0) return;
     issue_loads(0, kb0 * G_BK);
     if (nk > 1) issue_loads(1, (kb0 + 1) * G_BK);
     if (nk > 1)
@@ -293,55 +278,107 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
       mfmas(1);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
 
-  if (MODE == 0)
+  if (MODE == 0) {
+    const int per_xcd = (count + 7) / 8;
+    const int t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (t >= count) return;  // whole workgroup (uniform)
+    const int tile = tile_base + t;
+    const int p_base = (tile / tiles_q) * G_BP, q_base = (tile % tiles_q) * G_BQ;
+    run_tile(p_base, q_base, 0, nk_all);
     rotate_store(acc, lane, p_base + 128 * wp, q_base + 32 * G_QT * wq, P, Q, y, ldy, n0, sign_n);
-  else
-    store_partial(acc, partial + (int64_t)blockIdx.x * (G_BP * G_BQ / 4));
+  } else {
+    // piece v = the workgroup's place in XCD order, as for whole tiles: each
+    // XCD walks a contiguous run of units
+    const int total = count * nk_all;
+    const int pieces = (total + units - 1) / units;
+    const int v = (int)(blockIdx.x % 8) * ((pieces + 7) / 8) + (int)(blockIdx.x / 8);
+    if (v >= pieces) return;  // whole workgroup (uniform)
+    int unit = v * units;
+    const int end = min(unit + units, total);
+    for (int seg = 0; seg < 2 && unit < end; ++seg) {
+      const int t = unit / nk_all, kb0 = unit - t * nk_all, kb1 = min(nk_all, kb0 + (end - unit));
+      const int tile = tile_base + t;
+      run_tile((tile / tiles_q) * G_BP, (tile % tiles_q) * G_BQ, kb0, kb1);
+      store_partial(acc, partial + (int64_t)(2 * v + seg) * (G_BP * G_BQ / 4));
+      unit += kb1 - kb0;
+    }
+  }
 }
 
-// Sums the k-pieces of one wave's 128 x 64 block in piece order and runs the
-// rotation epilogue. One single-wave workgroup per (tail tile, wave) spreads
-// the partial reads over the CUs.
-__global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict__ partial, int32_t splits,
-                                                        int32_t tile_base, int32_t P, int32_t Q,
+// Sums the k-pieces of one 128 (p) x 32 (q) block of a tail tile in piece
+// order and runs the rotation epilogue. One single-wave workgroup per (tail
+// tile, wave, 32-wide q block) spreads the partial reads over the CUs; the
+// loads of two pieces are in flight together.
+__global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict__ partial, int32_t units,
+                                                        int32_t tile_base, int32_t P, int32_t Q, int32_t K,
                                                         uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
                                                         const uint16_t* __restrict__ sign_n) {
-  const int item = blockIdx.x / 8, wave = blockIdx.x % 8;
+  const int per_tile = (G_THREADS / 64) * G_QT;
+  const int item = blockIdx.x / per_tile, wave = (blockIdx.x % per_tile) / G_QT, j = blockIdx.x % G_QT;
   const int tiles_q = (Q + G_BQ - 1) / G_BQ;
   const int tile = tile_base + item;
   const int p_base = (tile / tiles_q) * G_BP, q_base = (tile % tiles_q) * G_BQ;
   const int lane = threadIdx.x;
   const int tid = 64 * wave + lane;  // the thread of the k-piece workgroup this lane stands for
   const int wp = wave & 1, wq = wave >> 1;
-  f32x16 acc[4][G_QT];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < G_QT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  for (int sp = 0; sp < splits; ++sp) {
-    const f32x4* src = partial + ((int64_t)item * splits + sp) * (G_BP * G_BQ / 4);
+  // pieces of this tile: the workgroups whose unit runs overlap
+  // [item nk, (item + 1) nk), in k order; the slot of workgroup w is
+  // 2 w + (item - first tile of w)
+  const int nk = K / G_BK;
+  const int w_lo = item * nk / units, w_hi = ((item + 1) * nk - 1) / units;
+  auto piece = [&](int w) {
+    const int slot = 2 * w + (item - (w * units) / nk);
+    return partial + (int64_t)slot * (G_BP * G_BQ / 4) + tid;
+  };
+  f32x16 a[4];
+  {
+    const f32x4* src = piece(w_lo);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < G_QT; ++j)
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 v = src[((i * G_QT + j) * 4 + c) * G_THREADS];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const f32x4 v = src[((i * G_QT + j) * 4 + c) * G_THREADS + tid];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * c + e] += v[e];
-        }
+        for (int e = 0; e < 4; ++e) a[i][4 * c + e] = v[e];
+      }
   }
-  rotate_store(acc, lane, p_base + 128 * wp, q_base + 32 * G_QT * wq, P, Q, y, ldy, n0, sign_n);
+  for (int w = w_lo + 1; w <= w_hi; w += 2) {
+    const f32x4* s0 = piece(w);
+    const f32x4* s1 = piece(min(w + 1, w_hi));
+    f32x4 v0[16], v1[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v0[4 * i + c] = s0[((i * G_QT + j) * 4 + c) * G_THREADS];
+        v1[4 * i + c] = s1[((i * G_QT + j) * 4 + c) * G_THREADS];
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[i][4 * c + e] += v0[4 * i + c][e];
+    if (w + 1 <= w_hi) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[i][4 * c + e] += v1[4 * i + c][e];
+    }
+  }
+  rotate_store_block(a, lane, p_base + 128 * wp, q_base + 32 * G_QT * wq + 32 * j, P, Q, y, ldy, n0, sign_n);
 }
 
-// Round plan: `full` tiles run whole; the `rem` tiles after them are cut into
-// `splits` k-pieces (one round of pieces).
+// Round plan: `full` tiles (whole rounds of 256) run whole; the `rem` tiles
+// after them are spread stream-K style, `units` k-steps per workgroup over
+// `pieces` workgroups, when that beats one more whole round with idle CUs
+// (rem <= 224); otherwise they also run whole.
 struct GemmPlan {
-  int tiles, full, rem, splits;
+  int tiles, full, rem, units, pieces;
 };
 
 static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
@@ -349,14 +386,14 @@ static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
   g.tiles = ((P + G_BP - 1) / G_BP) * ((Q + G_BQ - 1) / G_BQ);
   g.full = g.tiles / G_CUS * G_CUS;
   g.rem = g.tiles - g.full;
-  g.splits = 1;
-  if (g.rem > 0) {
-    g.splits = G_CUS / g.rem;
-    const int nk = K / G_BK;
-    if (g.splits > nk) g.splits = nk;
-    if (g.splits < 2) g.splits = 1;
-  }
-  if (g.splits == 1) {  // no split: every tile runs whole
+  g.units = 0;
+  g.pieces = 0;
+  const int nk = K / G_BK;
+  if (g.rem > 0 && g.rem <= 224 && nk >= 2) {
+    const int64_t total = (int64_t)g.rem * nk;
+    g.units = (int)((total + G_CUS - 1) / G_CUS);  // <= nk because rem < G_CUS
+    g.pieces = (int)((total + g.units - 1) / g.units);
+  } else {
     g.full = g.tiles;
     g.rem = 0;
   }
@@ -365,7 +402,7 @@ static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
 
 size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K) {
   const GemmPlan g = gemm_plan(P, Q, K);
-  return (size_t)g.rem * g.splits * G_BP * G_BQ * sizeof(float);
+  return (size_t)g.pieces * 2 * G_BP * G_BQ * sizeof(float);
 }
 
 hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
@@ -375,13 +412,14 @@ hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, in
   if (g.full > 0) {
     timer_begin(kTimerGemm, stream);
     gemm_had_kernel<0><<<8 * ((g.full + 7) / 8), G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, 0, g.full,
-                                                                         1, part);
+                                                                         0, part);
     timer_end(kTimerGemm, stream);
   }
   if (g.rem > 0) {
-    gemm_had_kernel<1><<<g.rem * g.splits, G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, g.full, g.rem,
-                                                                   g.splits, part);
-    gemm_fixup_kernel<<<g.rem * 8, 64, 0, stream>>>(part, g.splits, g.full, P, Q, y, ldy, n0, sign_n);
+    gemm_had_kernel<1><<<8 * ((g.pieces + 7) / 8), G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, g.full,
+                                                                           g.rem, g.units, part);
+    gemm_fixup_kernel<<<g.rem * (G_THREADS / 64) * G_QT, 64, 0, stream>>>(part, g.units, g.full, P, Q, K, y, ldy, n0,
+                                                                          sign_n);
   }
   return hipGetLastError();
 }
