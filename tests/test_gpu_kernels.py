@@ -174,6 +174,22 @@ def test_linear_two_slices(T, X, cb):
     H.assert_rows_close(got[rows], ref)
 
 
+@pytest.mark.parametrize("K,N,M", [
+    (2560, 3328, 200),    # 13 tiles < 256 CUs: every tile in stream-K pieces of 3 k-steps over 40 (pieces straddle tiles)
+    (1024, 4352, 4096),   # 272 tiles: one whole round + 16 tiles split along K
+])
+def test_linear_prefill_gemm_tail(T, X, cb, K, N, M):
+    H.announce("linear prefill GEMM tail K%d N%d M%d" % (K, N, M))
+    L = WL.layer(28, K, N)
+    x = WL.activations(28, M, K)
+    rows = np.unique(np.array([0, 1, 31, 32, 127, 128, 255, 256, 257, M // 2, M - 2, M - 1], np.int64) % M)
+    ref = O.exl3_linear(x, L, cb, rows)
+    got = run_linear(X, L, cb, x, 1)
+    H.assert_rows_close(got[rows], ref)
+    again = run_linear(X, L, cb, x, 1)
+    assert np.array_equal(got, again)  # the piece order is fixed: bit-identical reruns
+
+
 def test_linear_without_signs(T, X, cb):
     H.announce("linear without sign vectors")
     K, N, M = 256, 384, 20

@@ -50,6 +50,13 @@ __device__ __forceinline__ float dpp_mov(float v) {
 #define EXL3_DPP_REV4 0x1B  // quad_perm [3,2,1,0]: lane ^ 3
 #define EXL3_DPP_HALF_MIRROR 0x141  // lane ^ 7 within 8 lanes
 #define EXL3_DPP_MIRROR 0x140       // lane ^ 15 within 16 lanes
+#define EXL3_DPP_PAIR_LO 0x50       // quad_perm [0,0,1,1]
+#define EXL3_DPP_PAIR_HI 0xFA       // quad_perm [2,2,3,3]
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
 
 // Value of lane ^ 4 and lane ^ 8 (within 16 lanes) by two DPP moves each,
 // on the VALU rather than the LDS crossbar: (l ^ 7) ^ 3 = l ^ 4 and

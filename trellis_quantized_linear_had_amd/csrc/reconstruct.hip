@@ -28,11 +28,14 @@ __device__ __forceinline__ void tile_column_offsets(const uint32_t* __restrict__
 }
 
 // Writes W^T: wt[j * ldw + k] = W[k][16 nt0 + j], j < 16 n_nt.
-// A unit is 4 k-tiles x 1 n-tile: lane (dk = lane >> 4, c = lane & 15) decodes
-// column c of k-tile 4 kg + dk. A wave walks its units (stride = all waves) in
-// groups of RC_GROUP; the code words of the next group load into a second
-// register set while the current group decodes, which keeps ~2 KB of codes
-// per wave in flight.
+// A unit is 4 k-tiles x 1 n-tile: lane (c = lane >> 2, dk = lane & 3) decodes
+// column c of k-tile 4 kg + dk, i.e. the 32 bytes at k offset 32 dk of the
+// unit's 128-byte piece of W^T row c. The quad of lanes holding one row swaps
+// halves with two DPP transposes, so each 16-byte store instruction writes 64
+// contiguous bytes of 16 rows (not 16-byte pieces 32 bytes apart). A wave
+// walks its units (stride = all waves) in groups of RC_GROUP; the code words
+// of the next group load into a second register set while the current group
+// decodes, which keeps ~2 KB of codes per wave in flight.
 #define RC_GROUP 4
 
 struct RcRegs {
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(1024) void reconstruct_nk_kernel(const uint32_t* __
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
-  const int c = lane & 15, dk = lane >> 4;
+  const int c = lane >> 2, dk = lane & 3;
   const int tiles_n = N / 16;
   // Unit indices are wave-uniform 32-bit values (K / 64 * n_nt < 2^31 for any
   // K, N the layer accepts), so their arithmetic stays on the scalar unit.
@@ -78,41 +81,69 @@ __global__ __launch_bounds__(1024) void reconstruct_nk_kernel(const uint32_t* __
       R.sc[i] = buffer_load_u32(srs, vsc, (uint32_t)(32 * (nt0 + ntl)));
     }
   };
+  // All RC_GROUP x 16 gathers of a group are issued before any is used, so a
+  // wave keeps 64 codebook reads in flight. Units past the wave's last reuse
+  // its last unit's words and store its (identical) bytes again: every group
+  // issues the same 8 stores, which keeps the wait for the next group's code
+  // words from also waiting on these stores (the vector-memory counter
+  // covers both).
   auto decode_group = [&](int ug, const RcRegs& R) {
+    uint32_t g[RC_GROUP][16];
 #pragma unroll
     for (int i = 0; i < RC_GROUP; ++i) {
-      const int uu = ug + i * nwaves;
-      if (uu > last) break;  // wave-uniform
-      const int kg = uu / n_nt, ntl = uu % n_nt;
-      const int kt = 4 * kg + dk;
       uint32_t a[8], b[8];
       window_offsets8(R.w0[i], R.w1[i], a);
       window_offsets8(R.w1[i], R.w2[i], b);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        g[i][r] = lds_cb(cb_lds, a[r]);
+        g[i][8 + r] = lds_cb(cb_lds, b[r]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every gather ahead of the first use
+#pragma unroll
+    for (int i = 0; i < RC_GROUP; ++i) {
+      const int uu = min(ug + i * nwaves, last);
+      const int kg = uu / n_nt, ntl = uu % n_nt;
       const f16 s = __builtin_bit_cast(f16, (uint16_t)(R.sc[i] >> sc_shift));
       const f16x2 s2 = {s, s};
-      u32x4 o[2];
+      u32x4 o[2];  // 16-byte pieces 2 dk and 2 dk + 1 of the row's 128 bytes
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t o0 = j < 4 ? a[2 * j] : b[2 * j - 8], o1 = j < 4 ? a[2 * j + 1] : b[2 * j - 7];
-        f16x2 v = {__builtin_bit_cast(f16, lds_cb(cb_lds, o0)), __builtin_bit_cast(f16, lds_cb(cb_lds, o1))};
+        f16x2 v = {__builtin_bit_cast(f16, (uint16_t)g[i][2 * j]), __builtin_bit_cast(f16, (uint16_t)g[i][2 * j + 1])};
         v = v * s2;  // one fp16 rounding of the exact product
         o[j >> 2][j & 3] = __builtin_bit_cast(uint32_t, v);
       }
-      u32x4* dst = reinterpret_cast<u32x4*>(wt + (int64_t)(16 * ntl + c) * ldw + 16 * kt);
-      dst[0] = o[0];
-      dst[1] = o[1];
+      // lane dk of the quad stores piece dk, then piece 4 + dk: piece p lives
+      // in lane p >> 1 as o[p & 1]
+      u32x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t l0 = dpp_mov_u32<EXL3_DPP_PAIR_LO>(o[0][e]), l1 = dpp_mov_u32<EXL3_DPP_PAIR_LO>(o[1][e]);
+        const uint32_t h0 = dpp_mov_u32<EXL3_DPP_PAIR_HI>(o[0][e]), h1 = dpp_mov_u32<EXL3_DPP_PAIR_HI>(o[1][e]);
+        lo[e] = (dk & 1) ? l1 : l0;
+        hi[e] = (dk & 1) ? h1 : h0;
+      }
+      uint16_t* row = wt + (int64_t)(16 * ntl + c) * ldw + 64 * kg;
+      *reinterpret_cast<u32x4*>(row + 8 * dk) = lo;
+      *reinterpret_cast<u32x4*>(row + 32 + 8 * dk) = hi;
     }
   };
 
+  // Two register sets; every wait for a set's code words has the other set's
+  // 8 stores and 16 loads behind it, on the first pass as in the loop.
   const int gstride = RC_GROUP * nwaves;
   RcRegs ra, rb;
   load_group(u, ra);
-  for (; u <= last; u += 2 * gstride) {
-    load_group(u + gstride, rb);
-    decode_group(u, ra);
-    if (u + gstride > last) break;
-    load_group(u + 2 * gstride, ra);
-    decode_group(u + gstride, rb);
+  load_group(u + gstride, rb);
+  decode_group(u, ra);
+  load_group(u + 2 * gstride, ra);
+  for (int ub = u + gstride; ub <= last; ub += 2 * gstride) {
+    decode_group(ub, rb);
+    if (ub + gstride > last) break;
+    load_group(ub + 2 * gstride, rb);
+    decode_group(ub + gstride, ra);
+    load_group(ub + 3 * gstride, ra);
   }
 }
 
