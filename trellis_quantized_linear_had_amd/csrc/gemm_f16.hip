@@ -164,20 +164,25 @@ __device__ __forceinline__ void store_partial(const f32x16 (&acc)[4][G_QT], f32x
       }
 }
 
+// Slot of the partial of piece v for tail tile t: the (piece, tile) pairs in
+// order. A tile boundary t nk inside a piece (not at its start) adds one pair,
+// and the boundaries at piece starts are the t with units | t nk, i.e. the
+// multiples of sdiv = units / gcd(nk, units): slot = v + t - t / sdiv.
+__device__ __forceinline__ int partial_slot(int v, int t, int sdiv) { return v + t - t / sdiv; }
+
 // MODE 0: workgroup w computes tile tile_base + t (t in XCD order, t < count)
 // over all of K and runs the rotation epilogue. MODE 1 (stream-K tail): the
 // count tiles' k-steps, tile-major, are dealt in runs of `units` to the
 // workgroups; piece v (the workgroup's place in XCD order) covers
 // [v units, (v + 1) units), at most two tiles (units <= K / G_BK), and
-// writes one partial per tile it touches into slot 2 v + (tile - first tile
-// of v).
+// writes one partial per tile it touches (slot partial_slot(v, tile)).
 template <int MODE>
 __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __restrict__ A,
                                                              const uint16_t* __restrict__ B,
                                                              uint16_t* __restrict__ y, int32_t P, int32_t Q,
                                                              int32_t K, int64_t ldy, int32_t n0,
                                                              const uint16_t* __restrict__ sign_n, int32_t tile_base,
-                                                             int32_t count, int32_t units,
+                                                             int32_t count, int32_t units, int32_t sdiv,
                                                              f32x4* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * G_STAGE];
 
@@ -301,7 +306,7 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
       const int t = unit / nk_all, kb0 = unit - t * nk_all, kb1 = min(nk_all, kb0 + (end - unit));
       const int tile = tile_base + t;
       run_tile((tile / tiles_q) * G_BP, (tile % tiles_q) * G_BQ, kb0, kb1);
-      store_partial(acc, partial + (int64_t)(2 * v + seg) * (G_BP * G_BQ / 4));
+      store_partial(acc, partial + (int64_t)partial_slot(v, t, sdiv) * (G_BP * G_BQ / 4));
       unit += kb1 - kb0;
     }
   }
@@ -312,7 +317,8 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
 // tile, wave, 32-wide q block) spreads the partial reads over the CUs; the
 // loads of two pieces are in flight together.
 __global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict__ partial, int32_t units,
-                                                        int32_t tile_base, int32_t P, int32_t Q, int32_t K,
+                                                        int32_t sdiv, int32_t tile_base, int32_t P, int32_t Q,
+                                                        int32_t K,
                                                         uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
                                                         const uint16_t* __restrict__ sign_n) {
   const int per_tile = (G_THREADS / 64) * G_QT;
@@ -323,15 +329,11 @@ __global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict_
   const int lane = threadIdx.x;
   const int tid = 64 * wave + lane;  // the thread of the k-piece workgroup this lane stands for
   const int wp = wave & 1, wq = wave >> 1;
-  // pieces of this tile: the workgroups whose unit runs overlap
-  // [item nk, (item + 1) nk), in k order; the slot of workgroup w is
-  // 2 w + (item - first tile of w)
+  // pieces of this tile: the ones whose unit runs overlap
+  // [item nk, (item + 1) nk), in k order
   const int nk = K / G_BK;
   const int w_lo = item * nk / units, w_hi = ((item + 1) * nk - 1) / units;
-  auto piece = [&](int w) {
-    const int slot = 2 * w + (item - (w * units) / nk);
-    return partial + (int64_t)slot * (G_BP * G_BQ / 4) + tid;
-  };
+  auto piece = [&](int w) { return partial + (int64_t)partial_slot(w, item, sdiv) * (G_BP * G_BQ / 4) + tid; };
   f32x16 a[4];
   {
     const f32x4* src = piece(w_lo);
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict_
 // `pieces` workgroups, when that beats one more whole round with idle CUs
 // (rem <= 224); otherwise they also run whole.
 struct GemmPlan {
-  int tiles, full, rem, units, pieces;
+  int tiles, full, rem, units, pieces, sdiv, slots;
 };
 
 static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
@@ -388,11 +390,22 @@ static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
   g.rem = g.tiles - g.full;
   g.units = 0;
   g.pieces = 0;
+  g.sdiv = 1;
+  g.slots = 0;
   const int nk = K / G_BK;
   if (g.rem > 0 && g.rem <= 224 && nk >= 2) {
     const int64_t total = (int64_t)g.rem * nk;
     g.units = (int)((total + G_CUS - 1) / G_CUS);  // <= nk because rem < G_CUS
     g.pieces = (int)((total + g.units - 1) / g.units);
+    int a = nk, b = g.units;  // gcd
+    while (b) {
+      const int r = a % b;
+      a = b;
+      b = r;
+    }
+    g.sdiv = g.units / a;
+    const int t_last = g.rem - 1;
+    g.slots = g.pieces + t_last - t_last / g.sdiv;  // one past the last slot
   } else {
     g.full = g.tiles;
     g.rem = 0;
@@ -402,7 +415,7 @@ static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
 
 size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K) {
   const GemmPlan g = gemm_plan(P, Q, K);
-  return (size_t)g.pieces * 2 * G_BP * G_BQ * sizeof(float);
+  return (size_t)g.slots * G_BP * G_BQ * sizeof(float);
 }
 
 hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
@@ -412,14 +425,14 @@ hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, in
   if (g.full > 0) {
     timer_begin(kTimerGemm, stream);
     gemm_had_kernel<0><<<8 * ((g.full + 7) / 8), G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, 0, g.full,
-                                                                         0, part);
+                                                                         0, 1, part);
     timer_end(kTimerGemm, stream);
   }
   if (g.rem > 0) {
     gemm_had_kernel<1><<<8 * ((g.pieces + 7) / 8), G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, g.full,
-                                                                           g.rem, g.units, part);
-    gemm_fixup_kernel<<<g.rem * (G_THREADS / 64) * G_QT, 64, 0, stream>>>(part, g.units, g.full, P, Q, K, y, ldy, n0,
-                                                                          sign_n);
+                                                                           g.rem, g.units, g.sdiv, part);
+    gemm_fixup_kernel<<<g.rem * (G_THREADS / 64) * G_QT, 64, 0, stream>>>(part, g.units, g.sdiv, g.full, P, Q, K, y,
+                                                                          ldy, n0, sign_n);
   }
   return hipGetLastError();
 }
