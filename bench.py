@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=3, metavar=("KIND", "FETCH_CSV", "WRITE_CSV"), default=None,
                     help="print the traffic summary (markdown with a JSON block) of two rocprofv3 --pmc "
                          "counter_collection.csv files taken over --pmc-workload KIND")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: time the fused and prefill paths over M on both MLP "
+                         "geometries (crossover) and the wide projection, and print a markdown summary")
     ap.add_argument("--pmc-workload", choices=("logits", "gemm", "decode"), default=None,
                     help="run only a counter-collection workload: two 1 GiB device copies (calibration) then "
                          "three calls of the named path; prints nothing else")
@@ -69,6 +72,9 @@ def main():
 
     if args.pmc_workload:
         pmc_workload(args.pmc_workload)
+        return
+    if args.sweep:
+        print(sweep())
         return
 
     lib = _lib.lib()
@@ -376,6 +382,76 @@ def pmc_workload(kind: str):
             _lib.check(lib.exl3_linear(layer.c, x.data_ptr(), M, y.data_ptr(), scr.data_ptr(), scr.numel(), 128, sh))
     torch.cuda.synchronize()
     print("[bench] pmc workload %s done" % kind, file=sys.stderr, flush=True)
+
+
+def sweep() -> str:
+    """Fused (decode-GEMM) and prefill (reconstruct + GEMM) paths over M on
+    both MLP geometries, forced through prefill_min_m (0: fused at every M;
+    1: prefill at every M), 6 rotating weight sets (267 MB of codes, above the
+    256 MB MALL); then the wide projection K5120 x N32768 at M = 2048 (one
+    32768-column slice) with its scratch bytes. Back-to-back calls between one
+    event pair per cell."""
+    import torch
+
+    import trellis_quantized_linear_had_amd as X
+    from trellis_quantized_linear_had_amd import _lib
+
+    lib = _lib.lib()
+    dev = torch.device("cuda:0")
+    sh = torch.cuda.current_stream().cuda_stream
+    cb = W.codebook()
+
+    def time_calls(layers, x, M, y, scr, pm, reps):
+        def one(i):
+            _lib.check(lib.exl3_linear(layers[i % len(layers)].c, x.data_ptr(), M, y.data_ptr(), scr.data_ptr(),
+                                       scr.numel(), pm, sh))
+        for i in range(2):
+            one(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            one(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    out = ["| geometry | M | fused µs | prefill µs | faster | prefill TFLOP/s |", "|---|---|---|---|---|---|"]
+    cross = {}
+    for gi, (Kg, Ng) in enumerate(((5120, 17408), (17408, 5120))):
+        layers = [X.Layer.from_numpy(W.layer(W.SEED_PREFILL, Kg, Ng, 2 * s + gi), cb) for s in range(6)]
+        for M in (16, 32, 64, 96, 128, 192, 256, 512, 1024, 2048, 4096):
+            x = _lib.to_device_u16(W.activations(W.SEED_PREFILL, M, Kg, gi))
+            y = torch.empty((M, Ng), dtype=torch.int16, device=dev)
+            scr = torch.empty(max(X.linear_scratch_bytes(Kg, Ng, M, 0), X.linear_scratch_bytes(Kg, Ng, M, 1)),
+                              dtype=torch.uint8, device=dev)
+            fused = time_calls(layers, x, M, y, scr, 0, 6) if M <= 1024 else None
+            pre = time_calls(layers, x, M, y, scr, 1, 6)
+            if fused is not None and pre < fused and (Kg, Ng) not in cross:
+                cross[(Kg, Ng)] = M
+            out.append("| K%d×N%d | %d | %s | %.1f | %s | %.1f |" % (
+                Kg, Ng, M, "%.1f" % fused if fused is not None else "—", pre,
+                "—" if fused is None else ("prefill" if pre < fused else "fused"), 2 * M * Kg * Ng / pre / 1e6))
+            print("[bench] sweep K%d N%d M%d done" % (Kg, Ng, M), file=sys.stderr, flush=True)
+            del x, y, scr
+        del layers
+        torch.cuda.empty_cache()
+    lines = ["\n".join(out), ""]
+    for (Kg, Ng), M in cross.items():
+        lines.append("Crossover K%d×N%d: prefill is faster from M = %d on (among the M measured)." % (Kg, Ng, M))
+    Kw, Nw, Mw = 5120, 32768, 2048
+    layers = [X.Layer.from_numpy(W.layer(W.SEED_WIDE, Kw, Nw, s), cb) for s in range(3)]
+    x = _lib.to_device_u16(W.activations(W.SEED_WIDE, Mw, Kw))
+    y = torch.empty((Mw, Nw), dtype=torch.int16, device=dev)
+    need = X.linear_scratch_bytes(Kw, Nw, Mw)
+    scr = torch.empty(need, dtype=torch.uint8, device=dev)
+    us = time_calls(layers, x, Mw, y, scr, 128, 6)
+    lines.append("")
+    lines.append("Wide projection K%d×N%d, M = %d (one 32768-column slice): %.1f µs per call, %.1f TFLOP/s; "
+                 "scratch %d B (x̃ %d B + fp16 W slice %d B + GEMM-tail partials %d B)" % (
+                     Kw, Nw, Mw, us, 2 * Mw * Kw * Nw / us / 1e6, need, Mw * Kw * 2, Kw * Nw * 2,
+                     need - Mw * Kw * 2 - Kw * Nw * 2))
+    return "\n".join(lines)
 
 
 def cpu_baseline(target_s: float, log):
