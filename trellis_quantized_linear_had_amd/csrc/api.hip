@@ -153,16 +153,25 @@ bool use_prefill(int64_t M, int32_t prefill_min_m) { return prefill_min_m > 0 &&
 // the slowest wave sets the time of its workgroup; every round of workgroups
 // pays the 128 KiB codebook copy into LDS (~3000 clocks); partials are
 // written and read once.
-// Chooses (ks, ns, wn, wk, NT) for the decode kernel: every workgroup gets
-// the same work, the grid fills at most whole rounds of 256 CUs, and the
-// modelled cost (per round: the workgroup's tile-steps, the padded per-wave
-// share and a codebook load; plus the fp32 partial traffic) is least. With x_in_lds the workgroup's k
-// range is a whole number of 128-element blocks and its rotated slice of the
-// M rows fits DEC_XS_BYTES.
-static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, DecodePlan& best) {
+// Chooses (ks, ns, wn, wk, NT, G) for the decode kernel: every workgroup
+// gets the same work, the grid fills at most whole rounds of 256 CUs, and the
+// modelled cost (per round: the workgroup's tile-steps and the padded
+// per-wave share, once per pass of G row groups, plus a round cost of about
+// 4 us for the codebook load, prologue and reduction; plus
+// the fp32 partial traffic) is least. The LDS gathers are the bound, so a pass
+// of G groups costs about one gather pass (the extra MFMAs and A fragments add
+// a few per cent per group). With x_in_lds (one group) the workgroup's k range
+// is a whole number of 128-element blocks and its rotated slice of the M rows
+// fits DEC_XS_BYTES.
+static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, int G, DecodePlan& best,
+                               double& best_cost) {
   const int ksteps = K / 32, ntiles = N / 16;
-  const int64_t mgroups = (M + 15) / 16;
-  double best_cost = 1e300;
+  const int64_t passes = (M + 16 * G - 1) / (16 * G);
+  const double gfac = 1.0 + 0.05 * (G - 1);
+  const int32_t* inst = G == 1 ? kDecodeNtInstances : G == 2 ? kDecodeNtInstancesG2 : kDecodeNtInstancesG4;
+  const int ninst = G == 1 ? (int)(sizeof(kDecodeNtInstances) / sizeof(int32_t))
+                           : G == 2 ? (int)(sizeof(kDecodeNtInstancesG2) / sizeof(int32_t))
+                                    : (int)(sizeof(kDecodeNtInstancesG4) / sizeof(int32_t));
   bool found = false;
   const int wns[5] = {1, 2, 4, 8, 16};
   for (int wi = 0; wi < 5; ++wi) {
@@ -180,9 +189,9 @@ static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, D
         const int ntpw_real = (ntiles + ns - 1) / ns;
         const int per_wave_n = (ntpw_real + wn - 1) / wn;
         int nt_inst = 0;
-        for (int32_t v : kDecodeNtInstances)
-          if (v >= per_wave_n) {
-            nt_inst = v;
+        for (int i = 0; i < ninst; ++i)
+          if (inst[i] >= per_wave_n) {
+            nt_inst = inst[i];
             break;
           }
         if (nt_inst == 0) continue;
@@ -191,12 +200,13 @@ static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, D
         // the CU's LDS gathers cover the workgroup's real tile-steps; the
         // padded per-wave share bounds the slowest wave
         const double decode =
-            (double)rounds * (30.0 * mgroups * ((double)ntpw_real * kpw + 16.0 * kpw_wave * nt_inst) + 3000.0);
+            (double)rounds *
+            (30.0 * passes * gfac * ((double)ntpw_real * kpw + 16.0 * kpw_wave * nt_inst) + 10000.0);
         const double partial = (double)ks * M * N * 8.0 / 2083.0;
         const double cost = decode + partial;
         if (cost < best_cost - 1e-9) {
           best_cost = cost;
-          best = DecodePlan{ks, ns, kpw, ntpw_real, wn, wk, nt_inst, x_in_lds ? 1 : 0};
+          best = DecodePlan{ks, ns, kpw, ntpw_real, wn, wk, nt_inst, x_in_lds ? 1 : 0, G};
           found = true;
         }
       }
@@ -206,9 +216,12 @@ static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, D
 }
 
 DecodePlan plan_decode(int32_t K, int32_t N, int64_t M) {
-  DecodePlan p{1, 1, K / 32, 1, 1, 16, 1, 0};
-  if (M <= 16 && plan_decode_search(K, N, M, true, p)) return p;
-  plan_decode_search(K, N, M, false, p);
+  DecodePlan p{1, 1, K / 32, 1, 1, 16, 1, 0, 1};
+  double cost = 1e300;
+  if (M <= 16 && plan_decode_search(K, N, M, true, 1, p, cost)) return p;
+  cost = 1e300;
+  for (int G : {1, 2, 4})
+    if (G == 1 || 16 * (G / 2) < M) plan_decode_search(K, N, M, false, G, p, cost);
   return p;
 }
 

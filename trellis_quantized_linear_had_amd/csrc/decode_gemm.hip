@@ -41,24 +41,28 @@ __device__ __forceinline__ void decode_load_codes(__amdgpu_buffer_rsrc_t codes, 
   }
 }
 
-// The A fragment of one k-step (8 consecutive k of one row of Xr) and the
-// step's code words. The A fragment goes first: loads of one kind retire in
-// order, so the MFMAs of the previous step (which need only that step's A
-// fragment) never wait for this step's code words. XL: the fragment comes
-// from the workgroup's rotated slice in LDS (16-byte chunk j of row m stored
-// at chunk j ^ (m & 15), so the 16 rows one read instruction touches fall on
-// distinct banks); otherwise from Xr in global memory.
-template <int NT, bool XL>
+// The A fragments of one k-step (8 consecutive k of one row of Xr, for each
+// of the G row groups of the pass) and the step's code words. The A fragments
+// go first: loads of one kind retire in order, so the MFMAs of the previous
+// step (which need only that step's A fragments) never wait for this step's
+// code words. XL (one group): the fragment comes from the workgroup's rotated
+// slice in LDS (16-byte chunk j of row m stored at chunk j ^ (m & 15), so the
+// 16 rows one read instruction touches fall on distinct banks); otherwise
+// from Xr in global memory.
+template <int NT, bool XL, int G>
 __device__ __forceinline__ void decode_load_step(__amdgpu_buffer_rsrc_t codes, int ntiles_total, int step,
-                                                 const int (&tbase)[NT], int loff, int loff1, const uint16_t* xsrc,
-                                                 int xstep0, bool mok, uint32_t (&lo)[NT], uint32_t (&hi)[NT],
-                                                 f16x8& a) {
-  if (XL) {
-    const int j = 4 * (step - xstep0) + (threadIdx.x & 63) / 16;  // chunk in the row
-    a = mok ? *reinterpret_cast<const f16x8*>(xsrc + 8 * (j ^ (threadIdx.x & 15)))
-            : (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
-  } else {
-    a = mok ? *reinterpret_cast<const f16x8*>(xsrc + 32 * step) : (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+                                                 const int (&tbase)[NT], int loff, int loff1,
+                                                 const uint16_t* const (&xsrc)[G], int xstep0, const bool (&mok)[G],
+                                                 uint32_t (&lo)[NT], uint32_t (&hi)[NT], f16x8 (&a)[G]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (XL) {
+      const int j = 4 * (step - xstep0) + (threadIdx.x & 63) / 16;  // chunk in the row
+      a[g] = mok[g] ? *reinterpret_cast<const f16x8*>(xsrc[g] + 8 * (j ^ (threadIdx.x & 15)))
+                    : (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    } else {
+      a[g] = mok[g] ? *reinterpret_cast<const f16x8*>(xsrc[g] + 32 * step) : (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    }
   }
   decode_load_codes<NT>(codes, ntiles_total, step, tbase, loff, loff1, lo, hi);
 }
@@ -79,25 +83,29 @@ __device__ __forceinline__ f16x8 pack_tile(const uint32_t (&g)[8]) {
   return __builtin_bit_cast(f16x8, p);
 }
 
-// The gathers of tile t + 1 are issued before the MFMA of tile t consumes
+// The gathers of tile t + 1 are issued before the MFMAs of tile t consume
 // tile t, so two tiles' gathers (up to the 15 outstanding LDS reads a wave can
-// track) are in flight per wave.
-template <int NT>
+// track) are in flight per wave. Each decoded tile feeds the MFMAs of all G
+// row groups: the gathers, the bound, are shared by up to 64 rows.
+template <int NT, int G>
 __device__ __forceinline__ void decode_mfma_step(const uint16_t* cb_lds, const uint32_t (&lo)[NT],
-                                                 const uint32_t (&hi)[NT], const f16x8& a, f32x4 (&acc)[NT]) {
+                                                 const uint32_t (&hi)[NT], const f16x8 (&a)[G],
+                                                 f32x4 (&acc)[G][NT]) {
   uint32_t cur[8], nxt[8];
   gather_tile(cb_lds, lo[0], hi[0], cur);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (t + 1 < NT) gather_tile(cb_lds, lo[t + 1], hi[t + 1], nxt);
-    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pack_tile(cur), acc[t], 0, 0, 0);
+    const f16x8 b = pack_tile(cur);
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[g], b, acc[g][t], 0, 0, 0);
     if (t + 1 < NT)
 #pragma unroll
       for (int j = 0; j < 8; ++j) cur[j] = nxt[j];
   }
 }
 
-template <int NT, bool XL>
+template <int NT, bool XL, int G>
 __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t* __restrict__ xin,
                                                                   const uint16_t* __restrict__ sign_k,
                                                                   const uint32_t* __restrict__ codes,
@@ -206,44 +214,17 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
   // release fence would wait for them.)
   __syncthreads();
 
-  for (int m0 = 0; m0 < M; m0 += 16) {
-    f32x4 acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    const int mrow = m0 + c;
-    const bool mok = mrow < M;
-    // XL: the row of the LDS slice; otherwise the row of Xr in global memory
-    // at this lane's 8-element k offset.
-    const uint16_t* xsrc = XL ? xs + (mok ? mrow : 0) * (sw * 32)
-                              : xin + (int64_t)(mok ? mrow : 0) * K + 8 * (lane >> 4);
-    if (busy) {
-      uint32_t lo0[NT], hi0[NT], lo1[NT], hi1[NT];
-      f16x8 a0, a1;
-      const int last = ws_end - 1;
-      decode_load_step<NT, XL>(crs, ntiles_total, ws_begin, tbase, loff, loff1, xsrc, s_begin, mok, lo0, hi0, a0);
-      for (int step = ws_begin; step < ws_end; step += 2) {
-        decode_load_step<NT, XL>(crs, ntiles_total, min(step + 1, last), tbase, loff, loff1, xsrc, s_begin, mok,
-                                 lo1, hi1, a1);
-        decode_mfma_step<NT>(cb_lds, lo0, hi0, a0, acc);
-        if (step + 1 < ws_end) {
-          decode_load_step<NT, XL>(crs, ntiles_total, min(step + 2, last), tbase, loff, loff1, xsrc, s_begin, mok,
-                                   lo0, hi0, a0);
-          decode_mfma_step<NT>(cb_lds, lo1, hi1, a1, acc);
-        }
-      }
-    }
-
-    // Fixed-order reduction over the wk waves that share these n-tiles:
-    // sum = ((w_0 + w_1) + w_2) + ... over the waves' k order, for every
-    // output. D layout of the MFMA: lane holds rows 4*(lane>>4) + r, column
-    // lane & 15.
-    const int eoff = 4 * (lane >> 4) * 16 + c;
-    const int wt_off = wt_begin - t_begin;
-    if (m0 + 16 >= M) {
-      // Last row group: no gather follows, so the whole LDS block holds one
-      // slot per (wave, tile) and all waves store at once, in passes of
-      // `chunk` tiles.
+  // Fixed-order reduction over the wk waves that share these n-tiles, for
+  // the 16 rows m0g .. m0g + 15: sum = ((w_0 + w_1) + w_2) + ... over the
+  // waves' k order, for every output. D layout of the MFMA: lane holds rows
+  // 4*(lane>>4) + r, column lane & 15. `dead`: no gather follows, so the whole
+  // LDS block holds one slot per (wave, tile) and all waves store at once, in
+  // passes of `chunk` tiles; otherwise (the codebook is still needed) the
+  // waves accumulate through the small reduction buffer one at a time.
+  const int eoff = 4 * (lane >> 4) * 16 + c;
+  const int wt_off = wt_begin - t_begin;
+  auto reduce_store = [&](const f32x4 (&accg)[NT], int m0g, bool dead) {
+    if (dead) {
       float* slots = lds;
       const int chunk = 40960 / 256 / plan.wk;
       __syncthreads();
@@ -253,21 +234,19 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
           const int tt = wt_off + t - t0;
           if (t < nt_w && tt >= 0 && tt < chunk)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) slots[(wk_idx * chunk + tt) * 256 + eoff + r * 16] = acc[t][r];
+            for (int r = 0; r < 4; ++r) slots[(wk_idx * chunk + tt) * 256 + eoff + r * 16] = accg[t][r];
         }
         __syncthreads();
         const int nout = min(chunk, tw - t0) * 256;
         for (int idx = threadIdx.x; idx < nout; idx += DEC_THREADS) {
           float sum = slots[idx];
           for (int j = 1; j < plan.wk; ++j) sum += slots[j * chunk * 256 + idx];
-          const int t = t0 + (idx >> 8), e = idx & 255, m = m0 + (e >> 4), n = (t_begin + t) * 16 + (e & 15);
+          const int t = t0 + (idx >> 8), e = idx & 255, m = m0g + (e >> 4), n = (t_begin + t) * 16 + (e & 15);
           if (m < M) partials[((int64_t)ks * M + m) * N + n] = sum;
         }
         __syncthreads();
       }
     } else {
-      // More row groups follow and need the codebook: accumulate through the
-      // small reduction buffer one wave at a time, in the same order.
       const int rbase = wt_off * 256 + eoff;
       for (int j = 0; j < plan.wk; ++j) {
         if (wk_idx == j) {
@@ -277,7 +256,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 float* p = &red[rbase + t * 256 + r * 16];
-                *p = (j == 0) ? acc[t][r] : *p + acc[t][r];
+                *p = (j == 0) ? accg[t][r] : *p + accg[t][r];
               }
             }
           }
@@ -286,11 +265,53 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
       }
       // partials[ks][m][n]
       for (int idx = threadIdx.x; idx < tw * 256; idx += DEC_THREADS) {
-        const int t = idx >> 8, e = idx & 255, m = m0 + (e >> 4), n = (t_begin + t) * 16 + (e & 15);
+        const int t = idx >> 8, e = idx & 255, m = m0g + (e >> 4), n = (t_begin + t) * 16 + (e & 15);
         if (m < M) partials[((int64_t)ks * M + m) * N + n] = red[idx];
       }
       __syncthreads();
     }
+  };
+
+  // Passes of G row groups (16 rows each) over the wave's tiles and k range.
+  for (int m0 = 0; m0 < M; m0 += 16 * G) {
+    f32x4 acc[G][NT];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[g][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    // XL: the row of the LDS slice; otherwise the row of Xr in global memory
+    // at this lane's 8-element k offset.
+    bool mok[G];
+    const uint16_t* xsrc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int mrow = m0 + 16 * g + c;
+      mok[g] = mrow < M;
+      xsrc[g] = XL ? xs + (mok[g] ? mrow : 0) * (sw * 32) : xin + (int64_t)(mok[g] ? mrow : 0) * K + 8 * (lane >> 4);
+    }
+    if (busy) {
+      uint32_t lo0[NT], hi0[NT], lo1[NT], hi1[NT];
+      f16x8 a0[G], a1[G];
+      const int last = ws_end - 1;
+      decode_load_step<NT, XL, G>(crs, ntiles_total, ws_begin, tbase, loff, loff1, xsrc, s_begin, mok, lo0, hi0,
+                                  a0);
+      for (int step = ws_begin; step < ws_end; step += 2) {
+        decode_load_step<NT, XL, G>(crs, ntiles_total, min(step + 1, last), tbase, loff, loff1, xsrc, s_begin, mok,
+                                    lo1, hi1, a1);
+        decode_mfma_step<NT, G>(cb_lds, lo0, hi0, a0, acc);
+        if (step + 1 < ws_end) {
+          decode_load_step<NT, XL, G>(crs, ntiles_total, min(step + 2, last), tbase, loff, loff1, xsrc, s_begin,
+                                      mok, lo0, hi0, a0);
+          decode_mfma_step<NT, G>(cb_lds, lo1, hi1, a1, acc);
+        }
+      }
+    }
+
+    const bool dead = m0 + 16 * G >= M;  // last pass: the codebook is no longer read
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (m0 + 16 * g < M) reduce_store(acc[g], m0 + 16 * g, dead);  // uniform
   }
 }
 
@@ -359,29 +380,57 @@ hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const
                               float* partials, int32_t K, int32_t N, int32_t M, const DecodePlan& plan,
                               hipStream_t stream) {
   const int grid = plan.ks_count * plan.ns_count;
-#define EXL3_DEC_CASE(nt)                                                                                      \
-  case nt:                                                                                                     \
-    if (plan.x_in_lds)                                                                                         \
-      decode_gemm_kernel<nt, true><<<grid, DEC_THREADS, 0, stream>>>(xin, sign_k, codes, cb, partials, K, N,  \
-                                                                     M, plan);                                 \
-    else                                                                                                       \
-      decode_gemm_kernel<nt, false><<<grid, DEC_THREADS, 0, stream>>>(xin, sign_k, codes, cb, partials, K, N, \
-                                                                      M, plan);                                \
+#define EXL3_DEC_LAUNCH(nt, xl, g)                                                                              \
+  decode_gemm_kernel<nt, xl, g><<<grid, DEC_THREADS, 0, stream>>>(xin, sign_k, codes, cb, partials, K, N, M, plan)
+#define EXL3_DEC_CASE1(nt)                  \
+  case nt:                                  \
+    if (plan.x_in_lds)                      \
+      EXL3_DEC_LAUNCH(nt, true, 1);         \
+    else                                    \
+      EXL3_DEC_LAUNCH(nt, false, 1);        \
     break;
-  switch (plan.nt_wave) {
-    EXL3_DEC_CASE(1)
-    EXL3_DEC_CASE(2)
-    EXL3_DEC_CASE(3)
-    EXL3_DEC_CASE(4)
-    EXL3_DEC_CASE(5)
-    EXL3_DEC_CASE(6)
-    EXL3_DEC_CASE(8)
-    EXL3_DEC_CASE(9)
-    EXL3_DEC_CASE(10)
-    default:
-      return hipErrorInvalidValue;
+#define EXL3_DEC_CASEG(nt, g) \
+  case nt:                    \
+    EXL3_DEC_LAUNCH(nt, false, g); \
+    break;
+  if (plan.groups == 1) {
+    switch (plan.nt_wave) {
+      EXL3_DEC_CASE1(1)
+      EXL3_DEC_CASE1(2)
+      EXL3_DEC_CASE1(3)
+      EXL3_DEC_CASE1(4)
+      EXL3_DEC_CASE1(5)
+      EXL3_DEC_CASE1(6)
+      EXL3_DEC_CASE1(8)
+      EXL3_DEC_CASE1(9)
+      EXL3_DEC_CASE1(10)
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else if (plan.groups == 2 && !plan.x_in_lds) {
+    switch (plan.nt_wave) {
+      EXL3_DEC_CASEG(1, 2)
+      EXL3_DEC_CASEG(2, 2)
+      EXL3_DEC_CASEG(3, 2)
+      EXL3_DEC_CASEG(4, 2)
+      EXL3_DEC_CASEG(5, 2)
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else if (plan.groups == 4 && !plan.x_in_lds) {
+    switch (plan.nt_wave) {
+      EXL3_DEC_CASEG(1, 4)
+      EXL3_DEC_CASEG(2, 4)
+      EXL3_DEC_CASEG(3, 4)
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
   }
-#undef EXL3_DEC_CASE
+#undef EXL3_DEC_CASEG
+#undef EXL3_DEC_CASE1
+#undef EXL3_DEC_LAUNCH
   return hipGetLastError();
 }
 

@@ -24,11 +24,15 @@ struct DecodePlan {
   int32_t x_in_lds;       // 1: each workgroup rotates its own x slice into LDS
                           // (M <= 16, slice <= DEC_XS_BYTES); 0: x is rotated
                           // by a separate pass into scratch
+  int32_t groups;         // 16-row groups per pass sharing each decoded tile (1, 2, 4)
 };
 
 // Per-wave n-tile counts the decode kernel is compiled for (16 waves of at
 // most 128 VGPRs: accumulators and two code-word sets grow with the count;
 // 12 no longer fits without spilling).
 static const int32_t kDecodeNtInstances[] = {1, 2, 3, 4, 5, 6, 8, 9, 10};
+// ... and with 2 or 4 row groups per pass (accumulators grow with the groups)
+static const int32_t kDecodeNtInstancesG2[] = {1, 2, 3, 4, 5};
+static const int32_t kDecodeNtInstancesG4[] = {1, 2, 3};
 
 }  // namespace exl3
