@@ -39,12 +39,19 @@ def build(force: bool = False) -> str:
 
 _lib = None
 
+# A test may point the loader at another build of the same source (the
+# mutation tests run the pins against deliberately broken copies, in their
+# own process); nothing else sets this.
+_OVERRIDE_ENV = "EXL3_ORACLE_LIB_OVERRIDE"
+
 
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get(_OVERRIDE_ENV)
+        if not path:
+            path = build()
+        L = ctypes.CDLL(path)
         L.oracle_f16_to_f64.argtypes = [_u16p, _f64p, _i64]
         L.oracle_f64_to_f16.argtypes = [_f64p, _u16p, _i64]
         L.oracle_trellis_states.argtypes = [_u32p, _i64, _i64, _u16p]
