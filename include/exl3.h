@@ -72,7 +72,7 @@ extern "C" {
 enum {
   EXL3_OK = 0,
   EXL3_EINVAL = 1,   /* NULL pointer where one is required, negative size */
-  EXL3_ESHAPE = 2,   /* K or N not a multiple of 128, bits != 4, misaligned slice */
+  EXL3_ESHAPE = 2,   /* K or N not a multiple of 128, bits != 4, misaligned slice, size beyond a limit */
   EXL3_ESCRATCH = 3, /* scratch smaller than the matching *_scratch_bytes() */
   EXL3_EWIDTH = 4,   /* n_valid < 1, n_valid > w_rows, ld_logits < padded width */
   EXL3_EHIP = 5,     /* a HIP runtime call or kernel launch failed */
@@ -110,11 +110,16 @@ typedef struct exl3_layer {
  * prefill path runs (input rotation into scratch; then, per slice of at most
  * EXL3_MAX_CHUNK_COLS columns, reconstruct the slice to fp16 into scratch and
  * run the MFMA GEMM whose epilogue applies the output rotation and sign_n);
- * otherwise the fused decode path runs (input rotation into scratch; a
- * decode-GEMM that decodes every trellis tile once per call and multiplies it
- * with all M rows; a finalize kernel that sums the split-K partials in a fixed
- * order and applies the output rotation). prefill_min_m = 0 means the fused
- * path for every M. M = 0 is a no-op returning EXL3_OK.
+ * otherwise the fused decode path runs (a decode-GEMM that decodes every
+ * trellis tile once per pass of up to 64 rows and multiplies it with those
+ * rows -- for M <= 16 it also applies the input rotation itself, otherwise a
+ * rotation pass writes it to scratch first -- then an output-stage kernel that
+ * sums the split-K partials in a fixed order and applies the output rotation
+ * and sign_n). prefill_min_m = 0 means the fused path for every M. M = 0 is a
+ * no-op returning EXL3_OK.
+ * Limits (EXL3_ESHAPE otherwise): K, N positive multiples of 128, K < 65536,
+ * K * N / 2 (the packed codes) below 4 GiB, and on the prefill path
+ * M * K * 2 below 4 GiB.
  * scratch: device memory of at least
  *   exl3_linear_scratch_bytes(K, N, M, prefill_min_m) bytes, owned by the
  * caller and reusable across layers of the same geometry; its contents are

@@ -77,6 +77,8 @@ def _linear(layer, x=0x4000, M=1, y=0x5000, scratch=0x6000, nbytes=1 << 30, pm=1
     (_layer(codes=0), X.EXL3_EINVAL),
     (_layer(cb=0), X.EXL3_EINVAL),
     (_layer(codes=0x1004), X.EXL3_EINVAL),
+    (_layer(K=65536, N=128), X.EXL3_ESHAPE),          # K past the 32-bit slice addressing
+    (_layer(K=65408, N=131584), X.EXL3_ESHAPE),       # packed codes past 4 GiB
 ])
 def test_linear_rejects_bad_layers(layer, status):
     assert _linear(layer) == status
@@ -94,6 +96,10 @@ def test_linear_rejects_bad_calls():
     assert _linear(good, nbytes=need - 1) == X.EXL3_ESCRATCH
     assert b"needs" in X.lib().exl3_strerror(X.EXL3_ESCRATCH)
     assert _linear(good, pm=-1) == X.EXL3_EINVAL
+    # the prefill path addresses the rotated input with 32-bit offsets: M * K * 2 < 4 GiB
+    big = _layer(K=65408, N=128)
+    assert _linear(big, M=32833, pm=128) == X.EXL3_ESHAPE    # 32833 * 65408 * 2 > 2^32
+    assert b"4 GiB" in X.lib().exl3_strerror(X.EXL3_ESHAPE)
 
 
 def test_reconstruct_and_had_validation():

@@ -190,6 +190,46 @@ def test_linear_prefill_gemm_tail(T, X, cb, K, N, M):
     assert np.array_equal(got, again)  # the piece order is fixed: bit-identical reruns
 
 
+def test_empty_calls_are_noops(T, X, cb):
+    """M = 0 (and a zero-row rotation) returns OK and leaves the outputs as
+    they were."""
+    import torch
+
+    from trellis_quantized_linear_had_amd import _lib
+
+    H.announce("empty calls")
+    K, N = 256, 384
+    lay = X.Layer.from_numpy(WL.layer(32, K, N), cb)
+    x = dev16(WL.activations(32, 4, K))
+    y = torch.full((4, N), 0x1234, dtype=torch.int16, device="cuda")
+    scratch = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+    L = _lib.lib()
+    for pm in (0, 1, 128):
+        assert L.exl3_linear(lay.c, x.data_ptr(), 0, y.data_ptr(), scratch.data_ptr(), scratch.numel(), pm, sh) == 0
+    assert L.had_r_128(x.data_ptr(), y.data_ptr(), 0, K, None, None, sh) == 0
+    w = dev16(np.zeros((300, K), np.uint16))
+    am = torch.full((4,), -5, dtype=torch.int64, device="cuda")
+    assert L.logits_pad_mask_argmax(x.data_ptr(), 0, K, w.data_ptr(), 300, 257, y.data_ptr(), N, am.data_ptr(),
+                                    scratch.data_ptr(), scratch.numel(), sh) == 0
+    torch.cuda.synchronize()
+    assert bool((y == 0x1234).all()) and bool((am == -5).all())
+
+
+def test_linear_zero_codes_rank_one(T, X, cb):
+    """All-zero codes: every weight is fp16(cb[0] * scale[n]) (the oracle's
+    rank-1 closed form is pinned on the CPU); both paths against the oracle."""
+    H.announce("linear all-zero codes K512 N640")
+    K, N = 512, 640
+    L = WL.layer(33, K, N)
+    L["codes"] = np.zeros_like(L["codes"])
+    for M in (3, 130):
+        x = WL.activations(33, M, K)
+        ref = O.exl3_linear(x, L, cb)
+        H.assert_rows_close(run_linear(X, L, cb, x, 0), ref, what="fused M=%d" % M)
+        H.assert_rows_close(run_linear(X, L, cb, x, 1), ref, what="prefill M=%d" % M)
+
+
 def test_linear_without_signs(T, X, cb):
     H.announce("linear without sign vectors")
     K, N, M = 256, 384, 20

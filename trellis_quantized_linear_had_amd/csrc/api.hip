@@ -138,6 +138,11 @@ int validate_layer(const exl3_layer* L) {
   if (L->bits != 4) return fail(EXL3_ESHAPE, "bits = %d; only 4 bits per weight is supported", L->bits);
   if (L->K <= 0 || L->N <= 0 || L->K % 128 || L->N % 128)
     return fail(EXL3_ESHAPE, "K = %d and N = %d must be positive multiples of 128", L->K, L->N);
+  // The kernels address the packed codes (K N / 2 bytes) and one fp16 weight
+  // slice (K x up to 32768 columns) with 32-bit byte offsets.
+  if ((int64_t)L->K * L->N / 2 > (int64_t)UINT32_MAX)
+    return fail(EXL3_ESHAPE, "K = %d, N = %d: the packed codes exceed 4 GiB", L->K, L->N);
+  if (L->K >= 65536) return fail(EXL3_ESHAPE, "K = %d must be below 65536", L->K);
   if (!aligned16(L->codes) || !aligned16(L->codebook) || !aligned16(L->scale) || !aligned16(L->sign_k) ||
       !aligned16(L->sign_n))
     return fail(EXL3_EINVAL, "layer tensors must be 16-byte aligned");
@@ -146,13 +151,6 @@ int validate_layer(const exl3_layer* L) {
 
 bool use_prefill(int64_t M, int32_t prefill_min_m) { return prefill_min_m > 0 && M >= prefill_min_m; }
 
-// Work decomposition of the fused decode path: choose workgroup and wave
-// grids (16 waves per workgroup) that give every workgroup the same number of
-// tiles and keep the split-K partial traffic small. Cost model in GPU clocks:
-// a 16-column x 32-row tile costs ~60 clocks of the LDS gather pipe per CU;
-// the slowest wave sets the time of its workgroup; every round of workgroups
-// pays the 128 KiB codebook copy into LDS (~3000 clocks); partials are
-// written and read once.
 // Chooses (ks, ns, wn, wk, NT, G) for the decode kernel: every workgroup
 // gets the same work, the grid fills at most whole rounds of 256 CUs, and the
 // modelled cost (per round: the workgroup's tile-steps and the padded
@@ -316,6 +314,10 @@ int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
   if (!aligned16(x) || !aligned16(y) || ((uintptr_t)scratch & 255u))
     return fail(EXL3_EINVAL, "x and y must be 16-byte aligned and scratch 256-byte aligned");
   const int32_t K = L->K, N = L->N;
+  // the prefill GEMM addresses the rotated input (M x K fp16) with 32-bit
+  // byte offsets
+  if (use_prefill(M, prefill_min_m) && M * K * 2 > (int64_t)UINT32_MAX)
+    return fail(EXL3_ESHAPE, "M = %lld, K = %d: the prefill path needs M * K * 2 below 4 GiB", (long long)M, K);
   const size_t need = exl3_linear_scratch_bytes(K, N, M, prefill_min_m);
   if (scratch_bytes < need)
     return fail(EXL3_ESCRATCH, "scratch has %zu bytes; this call needs %zu", scratch_bytes, need);
@@ -388,6 +390,11 @@ int exl3_decode_states(const exl3_layer* L, uint16_t* states, void* stream_) {
   if (!L || !L->codes) return fail(EXL3_EINVAL, "layer or codes is NULL");
   if (L->K <= 0 || L->N <= 0 || L->K % 128 || L->N % 128)
     return fail(EXL3_ESHAPE, "K = %d and N = %d must be positive multiples of 128", L->K, L->N);
+  // The kernels address the packed codes (K N / 2 bytes) and one fp16 weight
+  // slice (K x up to 32768 columns) with 32-bit byte offsets.
+  if ((int64_t)L->K * L->N / 2 > (int64_t)UINT32_MAX)
+    return fail(EXL3_ESHAPE, "K = %d, N = %d: the packed codes exceed 4 GiB", L->K, L->N);
+  if (L->K >= 65536) return fail(EXL3_ESHAPE, "K = %d must be below 65536", L->K);
   if (!states || !aligned16(states) || !aligned16(L->codes)) return fail(EXL3_EINVAL, "states NULL or misaligned");
   int st = check_device();
   if (st) return st;
