@@ -31,8 +31,17 @@ PREFILL_M = 2048
 LOGITS_M = 16
 CODE_BYTES = K * N // 2                 # packed 4-bit codes of one layer: 44,564,480 B
 PREFILL_FLOP = 2 * PREFILL_M * K * N    # 365,072,220,160
+# reconstruct of the K5120 x N17408 slice: codes read, fp16 W^T written, column
+# scales read: 44,564,480 + 178,257,920 + 34,816 B
+RECON_BYTES = K * N // 2 + K * N * 2 + N * 2
 HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+# Secondary roof of the decode kernels: one random 16-bit codebook read from
+# LDS per weight; a probe measured 8.5 such reads per CU per clock, so 256 CUs
+# at the 2.4 GHz peak clock decode 5.22e12 weights/s = 2611 GB/s of packed
+# 4-bit codes.
+LDS_GATHERS_PER_CU_CLK = 8.5
+LDS_GATHER_ROOF_GBPS = LDS_GATHERS_PER_CU_CLK * 256 * 2.4e9 * 0.5 / 1e9
 
 
 def parse():
@@ -49,7 +58,7 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: time the fused and prefill paths over M on both MLP "
                          "geometries (crossover) and the wide projection, and print a markdown summary")
-    ap.add_argument("--pmc-workload", choices=("logits", "gemm", "decode"), default=None,
+    ap.add_argument("--pmc-workload", choices=("logits", "gemm", "decode", "reconstruct"), default=None,
                     help="run only a counter-collection workload: two 1 GiB device copies (calibration) then "
                          "three calls of the named path; prints nothing else")
     return ap.parse_args()
@@ -191,6 +200,8 @@ def main():
             call_linear(pre_layers[r % 6], xp, PREFILL_M, yp, pre_scratch)
         ms, n = _lib.kernel_timer_read(_lib.TIMER_GEMM)
         kern_us["gemm_had_kernel<0> M=2048"] = ms / n * 1e3
+        ms, n = _lib.kernel_timer_read(_lib.TIMER_RECONSTRUCT)
+        kern_us["reconstruct_nk_kernel K5120xN17408"] = ms / n * 1e3
         if not args.no_logits:
             for r in range(reps // 2):
                 call_logits()
@@ -209,20 +220,27 @@ def main():
     kernels = {}
     for M in DEC_M:
         us = kern_us["decode_gemm_kernel M=%d" % M]
+        gbps = CODE_BYTES / (us * 1e-6) / 1e9
         kernels["decode_gemm_kernel M=%d" % M] = {
-            "bound": "hbm", "achieved": CODE_BYTES / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "us": us, "per_launch": "%d B packed codes (K5120 x N17408 x 0.5 B)" % CODE_BYTES}
+            "bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "us": us, "per_launch": "%d B packed codes (K5120 x N17408 x 0.5 B)" % CODE_BYTES,
+            "lds_gather_roof_GBps": LDS_GATHER_ROOF_GBPS, "lds_gather_frac": gbps / LDS_GATHER_ROOF_GBPS}
     us = kern_us["gemm_had_kernel<0> M=2048"]
     kernels["gemm_had_kernel<0> M=2048"] = {
         "bound": "mfma", "achieved": gemm_full_flop / (us * 1e-6) / 1e12, "peak": MFMA_F16_PEAK_TFLOPS,
         "unit": "TFLOP/s", "us": us, "per_launch": "%d FLOP (2*256*256*5120 x %d full tiles)" % (gemm_full_flop, full_tiles)}
+    us = kern_us["reconstruct_nk_kernel K5120xN17408"]
+    kernels["reconstruct_nk_kernel K5120xN17408"] = {
+        "bound": "hbm", "achieved": RECON_BYTES / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "us": us, "per_launch": "%d B: packed codes read + fp16 W^T written + column scales read" % RECON_BYTES}
     if not args.no_logits:
         us = kern_us["logits_kernel M=16"]
         kernels["logits_kernel M=16"] = {
             "bound": "hbm", "achieved": logits_bytes / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "us": us, "per_launch": "%d B fp16 weight rows read (248192 x 5120 x 2)" % logits_bytes}
-    for r in kernels.values():
+    for k, r in kernels.items():
         r["frac"] = r["achieved"] / r["peak"]
+        r["traffic"] = stored_traffic(k)
     # the dominant kernel: most GPU time per step (the decode GEMM runs once
     # per row count, the others once)
     step_us = {k: v["us"] for k, v in kernels.items() if not k.startswith("decode")}
@@ -279,6 +297,8 @@ PMC_KERNELS = {
     "gemm": ("exl3::gemm_had_kernel<0>", "gemm_had_kernel<0> M=2048", ("gemm_f16.hip", "common.h")),
     "decode": ("exl3::decode_gemm_kernel<6, true>", "decode_gemm_kernel M=16",
                ("decode_gemm.hip", "decode_plan.h", "trellis.h", "common.h")),
+    "reconstruct": ("exl3::reconstruct_nk_kernel", "reconstruct_nk_kernel K5120xN17408",
+                    ("reconstruct.hip", "trellis.h", "common.h")),
 }
 
 
@@ -301,12 +321,15 @@ def pmc_summary(kind: str, fetch_csv: str, write_csv: str) -> str:
 
     def per_kernel(path):
         out = {}
-        for r in csv.DictReader(open(path)):
+        for r in sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"])):
             out.setdefault(r["Kernel_Name"].split("(")[0].replace("void ", ""), []).append(float(r["Counter_Value"]))
         return out
 
     fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
     copy = "__amd_rocclr_copyBuffer"
+    # the calibration copies are the workload's first two copy dispatches
+    # (host-to-device uploads of the inputs add small ones later)
+    fetch[copy], write[copy] = fetch[copy][:2], write[copy][:2]
     f_scale = COPY_BYTES / (sum(fetch[copy]) / len(fetch[copy]) * 1024)
     w_scale = COPY_BYTES / (sum(write[copy]) / len(write[copy]) * 1024)
     f_kib = sum(fetch[kname]) / len(fetch[kname])
@@ -373,9 +396,10 @@ def pmc_workload(kind: str):
             _lib.check(lib.logits_pad_mask_argmax(xl.data_ptr(), LOGITS_M, K, wl.data_ptr(), w_rows, n_valid,
                                                   lg.data_ptr(), n_pad, am.data_ptr(), scr.data_ptr(), scr.numel(), sh))
     else:
-        M = PREFILL_M if kind == "gemm" else max(DEC_M)
-        layer = X.Layer.from_numpy(W.layer(W.SEED_PREFILL if kind == "gemm" else W.SEED_DECODE, K, N, 0), cb)
-        x = _lib.to_device_u16(W.activations(W.SEED_PREFILL if kind == "gemm" else W.SEED_DECODE, M, K, 0))
+        pre = kind in ("gemm", "reconstruct")  # both run inside the prefill call
+        M = PREFILL_M if pre else max(DEC_M)
+        layer = X.Layer.from_numpy(W.layer(W.SEED_PREFILL if pre else W.SEED_DECODE, K, N, 0), cb)
+        x = _lib.to_device_u16(W.activations(W.SEED_PREFILL if pre else W.SEED_DECODE, M, K, 0))
         y = torch.empty((M, N), dtype=torch.int16, device=dev)
         scr = torch.empty(X.linear_scratch_bytes(K, N, M), dtype=torch.uint8, device=dev)
         for _ in range(3):

@@ -186,7 +186,8 @@ int exl3_decode_states(const exl3_layer *layer, uint16_t *states, void *stream);
  * (on != 0), every later call records a pair of HIP events on its stream
  * around one kernel: kind 0 the decode GEMM of exl3_linear, kind 1 the
  * full-tile launch of the prefill GEMM (one per column slice), kind 2 the
- * logits GEMM (one per 16-row group). Enabling costs an event creation per
+ * logits GEMM (one per 16-row group), kind 3 the prefill path's reconstruct
+ * of one column slice (its one or more launches). Enabling costs an event creation per
  * timed launch; leave it off under graph capture. */
 int exl3_kernel_timer_enable(int on);
 

@@ -136,7 +136,7 @@ def test_logits_validation():
 def test_kernel_timer_validation_without_gpu():
     L = X.lib()
     ms, n = ctypes.c_double(-1.0), ctypes.c_int64(-1)
-    assert L.exl3_kernel_timer_read(3, ctypes.byref(ms), ctypes.byref(n)) == X.EXL3_EINVAL
+    assert L.exl3_kernel_timer_read(4, ctypes.byref(ms), ctypes.byref(n)) == X.EXL3_EINVAL
     assert L.exl3_kernel_timer_read(-1, ctypes.byref(ms), ctypes.byref(n)) == X.EXL3_EINVAL
     assert L.exl3_kernel_timer_read(0, None, ctypes.byref(n)) == X.EXL3_EINVAL
     # nothing recorded: no HIP call, zero launches

@@ -85,7 +85,7 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-TIMER_DECODE, TIMER_GEMM, TIMER_LOGITS = 0, 1, 2
+TIMER_DECODE, TIMER_GEMM, TIMER_LOGITS, TIMER_RECONSTRUCT = 0, 1, 2, 3
 
 
 def kernel_timer(on: bool) -> None:

@@ -53,18 +53,21 @@ struct TimedLaunch {
 std::mutex g_timer_mu;
 std::vector<TimedLaunch> g_timed;
 std::atomic<bool> g_timer_on{false};
-thread_local hipEvent_t t_open[kTimerKinds] = {nullptr, nullptr, nullptr};
+thread_local hipEvent_t t_open[kTimerKinds] = {};
 }  // namespace
 
 void timer_begin(int kind, hipStream_t stream) {
   if (t_open[kind]) {  // an earlier launch of this kind failed before its end
-    hipEventDestroy(t_open[kind]);
+    (void)hipEventDestroy(t_open[kind]);
     t_open[kind] = nullptr;
   }
   if (!g_timer_on.load(std::memory_order_relaxed)) return;
   hipEvent_t e = nullptr;
   if (hipEventCreate(&e) != hipSuccess) return;
-  hipEventRecord(e, stream);
+  if (hipEventRecord(e, stream) != hipSuccess) {
+    (void)hipEventDestroy(e);
+    return;
+  }
   t_open[kind] = e;
 }
 
@@ -73,11 +76,11 @@ void timer_end(int kind, hipStream_t stream) {
   if (!a) return;
   t_open[kind] = nullptr;
   hipEvent_t b = nullptr;
-  if (hipEventCreate(&b) != hipSuccess) {
-    hipEventDestroy(a);
+  if (hipEventCreate(&b) != hipSuccess || hipEventRecord(b, stream) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    if (b) (void)hipEventDestroy(b);
     return;
   }
-  hipEventRecord(b, stream);
   std::lock_guard<std::mutex> lk(g_timer_mu);
   g_timed.push_back(TimedLaunch{kind, a, b});
 }
@@ -333,7 +336,9 @@ int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
     EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
     for (int32_t n0 = 0; n0 < N; n0 += l.chunk) {
       const int32_t nc = std::min(l.chunk, N - n0);
+      timer_begin(kTimerReconstruct, stream);
       EXL3_TRY(launch_reconstruct_nk(L->codes, L->codebook, L->scale, K, N, n0, nc, wt, K, stream), "reconstruct");
+      timer_end(kTimerReconstruct, stream);
       EXL3_TRY(launch_gemm_had(wt, xr, y, nc, (int32_t)M, K, N, n0, L->sign_n, (float*)(sb + l.part_off), stream),
                "gemm");
     }
@@ -474,7 +479,7 @@ int exl3_kernel_timer_enable(int on) {
 
 int exl3_kernel_timer_read(int kind, double* total_ms, int64_t* count) {
   g_msg[0] = 0;
-  if (kind < 0 || kind >= kTimerKinds) return fail(EXL3_EINVAL, "timer kind %d is not 0, 1 or 2", kind);
+  if (kind < 0 || kind >= kTimerKinds) return fail(EXL3_EINVAL, "timer kind %d is not 0, 1, 2 or 3", kind);
   if (!total_ms || !count) return fail(EXL3_EINVAL, "total_ms or count is NULL");
   std::vector<TimedLaunch> mine;
   {
@@ -493,8 +498,8 @@ int exl3_kernel_timer_read(int kind, double* total_ms, int64_t* count) {
       if (e != hipSuccess) st = fail(EXL3_EHIP, "timer event: %s", hipGetErrorString(e));
     }
     sum += ms;
-    hipEventDestroy(t.start);
-    hipEventDestroy(t.stop);
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
   }
   *total_ms = sum;
   *count = (int64_t)mine.size();

@@ -7,7 +7,7 @@
 
 namespace exl3 {
 
-enum TimerKind { kTimerDecode = 0, kTimerGemm = 1, kTimerLogits = 2, kTimerKinds = 3 };
+enum TimerKind { kTimerDecode = 0, kTimerGemm = 1, kTimerLogits = 2, kTimerReconstruct = 3, kTimerKinds = 4 };
 
 // Record the opening / closing event of one timed launch on `stream` (no-op
 // while the hook is disabled). Each begin must be followed by its end on the
