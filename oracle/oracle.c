@@ -23,15 +23,17 @@
  * transpose of this one and random +-1 signs on both rotations.
  *
  * The pages name the trellis format without defining it (vLLM PR #316, summary
- * and "Problem"; vLLM PR #314, "Problem"), so this project fixes a stand-in:
- *   - 4 bits per weight, 16x16 tiles over (k, n); tile (kt, nt) is 32 little-
- *     endian uint32 words starting at word (kt * N/16 + nt) * 32;
- *   - bit p (0 <= p < 1024) of a tile is bit (p mod 32) of word (p / 32);
+ * and "Problem"; vLLM PR #314, "Problem"), so this project fixes a stand-in,
+ * with b = bits per weight (1..8; the pages' MLP layers use 4, their lm_head
+ * 6: vLLM PR #316, "Problem" and follow-up item 3):
+ *   - 16x16 tiles over (k, n); tile (kt, nt) is 8b little-endian uint32 words
+ *     (256 b bits) starting at word (kt * N/16 + nt) * 8b;
+ *   - bit p (0 <= p < 256 b) of a tile is bit (p mod 32) of word (p / 32);
  *   - trellis step i (0..255) of the tile is the weight at row k = 16kt + i%16,
  *     column n = 16nt + i/16 (k runs fastest);
- *   - state(i) is the 16-bit window that starts at bit 4i, least significant
- *     bit first, wrapping from bit 1023 to bit 0 (tail-biting): a shift
- *     register that takes in 4 new bits per step;
+ *   - state(i) is the 16-bit window that starts at bit b*i, least significant
+ *     bit first, wrapping from the tile's last bit to bit 0 (tail-biting): a
+ *     shift register that takes in b new bits per step;
  *   - the weight is the fp16 codebook entry cb[state] times the fp16 scale of
  *     its column, rounded once to fp16.
  *
@@ -100,38 +102,40 @@ void oracle_f64_to_f16(const double *in, uint16_t *out, int64_t n) {
 
 /* ------------------------------------------------------------- trellis ---- */
 
-/* Bit p of a tile (32 words, LSB-first). */
+/* Bit p of a tile (LSB-first words). */
 static int tile_bit(const uint32_t *tile, int p) { return (tile[p >> 5] >> (p & 31)) & 1; }
 
-/* state(i): the 16-bit window starting at bit 4i, LSB first, tail-biting. */
-static uint16_t tile_state(const uint32_t *tile, int i) {
+/* state(i): the 16-bit window starting at bit bits*i, LSB first, wrapping at
+ * the tile's 256*bits bits (tail-biting). */
+static uint16_t tile_state(const uint32_t *tile, int bits, int i) {
+  const int tile_len = 256 * bits;
   unsigned s = 0;
-  for (int t = 0; t < 16; ++t) s |= (unsigned)tile_bit(tile, (4 * i + t) & 1023) << t;
+  for (int t = 0; t < 16; ++t) s |= (unsigned)tile_bit(tile, (bits * i + t) % tile_len) << t;
   return (uint16_t)s;
 }
 
-static uint16_t weight_state(const uint32_t *codes, int64_t N, int64_t k, int64_t n) {
+static uint16_t weight_state(const uint32_t *codes, int64_t N, int bits, int64_t k, int64_t n) {
   int64_t kt = k / 16, nt = n / 16;
-  const uint32_t *tile = codes + (kt * (N / 16) + nt) * 32;
+  const uint32_t *tile = codes + (kt * (N / 16) + nt) * 8 * bits;
   int i = (int)((n % 16) * 16 + (k % 16));
-  return tile_state(tile, i);
+  return tile_state(tile, bits, i);
 }
 
 /* states: K x N row-major, the trellis state behind every weight. */
-void oracle_trellis_states(const uint32_t *codes, int64_t K, int64_t N, uint16_t *states) {
+void oracle_trellis_states(const uint32_t *codes, int64_t K, int64_t N, int64_t bits, uint16_t *states) {
 #pragma omp parallel for schedule(static)
   for (int64_t k = 0; k < K; ++k)
-    for (int64_t n = 0; n < N; ++n) states[k * N + n] = weight_state(codes, N, k, n);
+    for (int64_t n = 0; n < N; ++n) states[k * N + n] = weight_state(codes, N, (int)bits, k, n);
 }
 
 /* W[k, n0 + j] for j < n_count, written K x n_count row-major. */
 void oracle_reconstruct(const uint32_t *codes, const uint16_t *cb, const uint16_t *scale, int64_t K,
-                        int64_t N, int64_t n0, int64_t n_count, uint16_t *w) {
+                        int64_t N, int64_t bits, int64_t n0, int64_t n_count, uint16_t *w) {
 #pragma omp parallel for schedule(static)
   for (int64_t k = 0; k < K; ++k)
     for (int64_t j = 0; j < n_count; ++j) {
       int64_t n = n0 + j;
-      double v = h2d(cb[weight_state(codes, N, k, n)]) * h2d(scale[n]); /* exact product */
+      double v = h2d(cb[weight_state(codes, N, (int)bits, k, n)]) * h2d(scale[n]); /* exact product */
       w[k * n_count + j] = d2h(v);
     }
 }
@@ -199,11 +203,11 @@ void oracle_had128(const uint16_t *in, int64_t rows, int64_t cols, const uint16_
 void oracle_exl3_linear(const uint16_t *x, int64_t M, const int64_t *rows, int64_t n_rows,
                         const uint32_t *codes, const uint16_t *cb, const uint16_t *scale,
                         const uint16_t *sign_k, const uint16_t *sign_n, int64_t K, int64_t N,
-                        uint16_t *y) {
+                        int64_t bits, uint16_t *y) {
   (void)M;
   double *tab = h2d_table();
   uint16_t *w = (uint16_t *)malloc((size_t)K * N * sizeof(uint16_t));
-  oracle_reconstruct(codes, cb, scale, K, N, 0, N, w);
+  oracle_reconstruct(codes, cb, scale, K, N, bits, 0, N, w);
   double *sk = (double *)malloc(K * sizeof(double));
   double *sn = (double *)malloc(N * sizeof(double));
   for (int64_t k = 0; k < K; ++k) sk[k] = tab[sign_k[k]];

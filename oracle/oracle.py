@@ -54,12 +54,12 @@ def lib():
         L = ctypes.CDLL(path)
         L.oracle_f16_to_f64.argtypes = [_u16p, _f64p, _i64]
         L.oracle_f64_to_f16.argtypes = [_f64p, _u16p, _i64]
-        L.oracle_trellis_states.argtypes = [_u32p, _i64, _i64, _u16p]
-        L.oracle_reconstruct.argtypes = [_u32p, _u16p, _u16p, _i64, _i64, _i64, _i64, _u16p]
+        L.oracle_trellis_states.argtypes = [_u32p, _i64, _i64, _i64, _u16p]
+        L.oracle_reconstruct.argtypes = [_u32p, _u16p, _u16p, _i64, _i64, _i64, _i64, _i64, _u16p]
         L.oracle_hadamard_matrix.argtypes = [_i8p]
         L.oracle_had128.argtypes = [_u16p, _i64, _i64, ctypes.c_void_p, ctypes.c_void_p, _u16p]
         L.oracle_exl3_linear.argtypes = [_u16p, _i64, _i64p, _i64, _u32p, _u16p, _u16p, _u16p,
-                                         _u16p, _i64, _i64, _u16p]
+                                         _u16p, _i64, _i64, _i64, _u16p]
         L.oracle_padded_width.argtypes = [_i64, _i64]
         L.oracle_padded_width.restype = _i64
         L.oracle_logits.argtypes = [_u16p, _i64, _i64p, _i64, _u16p, _i64, _i64, _i64, _u16p, _i64p]
@@ -85,18 +85,24 @@ def f64_to_f16(d) -> np.ndarray:
     return out
 
 
-def trellis_states(codes, K: int, N: int) -> np.ndarray:
+def _codes(codes, K: int, N: int, bits: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint32)
+    if not 1 <= bits <= 8 or codes.size != K * N * bits // 32:
+        raise ValueError("codes must hold K*N*bits/32 words, bits in 1..8")
+    return codes
+
+
+def trellis_states(codes, K: int, N: int, bits: int = 4) -> np.ndarray:
     out = np.empty((K, N), np.uint16)
-    lib().oracle_trellis_states(np.ascontiguousarray(codes, np.uint32), K, N, out)
+    lib().oracle_trellis_states(_codes(codes, K, N, bits), K, N, bits, out)
     return out
 
 
-def reconstruct(codes, cb, scale, K: int, N: int, n0: int = 0, n_count: int | None = None):
+def reconstruct(codes, cb, scale, K: int, N: int, n0: int = 0, n_count: int | None = None, bits: int = 4):
     if n_count is None:
         n_count = N - n0
     out = np.empty((K, n_count), np.uint16)
-    lib().oracle_reconstruct(np.ascontiguousarray(codes, np.uint32), _u16(cb), _u16(scale), K, N,
-                             n0, n_count, out)
+    lib().oracle_reconstruct(_codes(codes, K, N, bits), _u16(cb), _u16(scale), K, N, bits, n0, n_count, out)
     return out
 
 
@@ -129,9 +135,10 @@ def exl3_linear(x, layer: dict, cb, rows=None) -> np.ndarray:
         rows = np.arange(M, dtype=np.int64)
     rows = np.ascontiguousarray(rows, np.int64)
     y = np.empty((len(rows), N), np.uint16)
-    lib().oracle_exl3_linear(x, M, rows, len(rows), np.ascontiguousarray(layer["codes"], np.uint32),
+    bits = int(layer.get("bits", 4))
+    lib().oracle_exl3_linear(x, M, rows, len(rows), _codes(layer["codes"], K, N, bits),
                              _u16(cb), _u16(layer["scale"]), _u16(layer["sign_k"]),
-                             _u16(layer["sign_n"]), K, N, y)
+                             _u16(layer["sign_n"]), K, N, bits, y)
     return y
 
 

@@ -5,6 +5,7 @@ import scipy.linalg
 
 import workloads as WL
 from oracle import oracle as O
+from tests import brute_trellis as BT
 
 H = scipy.linalg.hadamard(128).astype(np.float64) / np.sqrt(128)
 
@@ -63,3 +64,22 @@ def test_zero_codes_rank_one_closed_form():
     yr = val(f16(xr.sum(axis=1, keepdims=True) * w_col[None, :]))
     y_ref = O.had128(f16(yr), None, L["sign_n"])
     assert np.array_equal(O.exl3_linear(x, L, cb), y_ref)
+
+
+def test_matches_library_sequence_other_widths():
+    # W from the brute-force shift register and numpy's exact float32 product
+    # (one fp16 rounding), then the same matmul sequence as above
+    K, N, M = 128, 256, 3
+    cb = WL.codebook()
+    x = WL.activations(WL.SEED_TINY, M, K)
+    HK, HN = blockdiag(K), blockdiag(N)
+    for bits in (3, 6):
+        L = WL.layer(WL.SEED_TINY, K, N, 0, bits)
+        st = BT.states_matrix(L["codes"], K, N, bits)
+        W = (cb[st].view(np.float16).astype(np.float32) *
+             L["scale"].view(np.float16).astype(np.float32)[None, :]).astype(np.float16).astype(np.float64)
+        sk, sn = val(L["sign_k"]), val(L["sign_n"])
+        xr = val(f16((val(x) * sk) @ HK.T))
+        yr = val(f16(xr @ W))
+        y_ref = f16((yr @ HN.T) * sn)
+        assert np.array_equal(O.exl3_linear(x, L, cb), y_ref), bits

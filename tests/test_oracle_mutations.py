@@ -11,7 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = ["tests/test_oracle_fp16.py", "tests/test_oracle_hadamard.py", "tests/test_oracle_trellis.py",
-        "tests/test_oracle_linear.py", "tests/test_oracle_logits.py"]
+        "tests/test_oracle_trellis_bits.py", "tests/test_oracle_linear.py", "tests/test_oracle_logits.py"]
 
 # (name, exact text in oracle.c, replacement): each replaced text occurs once.
 MUTATIONS = [
@@ -20,13 +20,19 @@ MUTATIONS = [
     ("hadamard_negated", "& 1) ? -1 : 1; }", "& 1) ? 1 : -1; }"),
     ("hadamard_or_index", "__builtin_popcount((unsigned)(i & j))", "__builtin_popcount((unsigned)(i | j))"),
     ("hadamard_norm_dropped", "acc *= norm;", "acc *= 1.0;"),
-    ("window_off_by_one_bit", "(4 * i + t) & 1023", "(4 * i + t + 1) & 1023"),
-    ("window_msb_first", "tile_bit(tile, (4 * i + t) & 1023) << t;", "tile_bit(tile, (4 * i + t) & 1023) << (15 - t);"),
+    ("window_off_by_one_bit", "(bits * i + t) % tile_len", "(bits * i + t + 1) % tile_len"),
+    ("window_msb_first", "tile_bit(tile, (bits * i + t) % tile_len) << t;",
+     "tile_bit(tile, (bits * i + t) % tile_len) << (15 - t);"),
+    ("step_always_4_bits", "tile_bit(tile, (bits * i + t) % tile_len)", "tile_bit(tile, (4 * i + t) % tile_len)"),
+    ("tile_length_fixed", "const int tile_len = 256 * bits;", "const int tile_len = 1024;"),
     ("steps_n_fastest", "(n % 16) * 16 + (k % 16)", "(k % 16) * 16 + (n % 16)"),
-    ("neighbour_tile", "codes + (kt * (N / 16) + nt) * 32", "codes + ((kt * (N / 16) + nt) ^ 1) * 32"),
+    ("neighbour_tile", "codes + (kt * (N / 16) + nt) * 8 * bits", "codes + ((kt * (N / 16) + nt) ^ 1) * 8 * bits"),
+    ("tile_stride_fixed", "codes + (kt * (N / 16) + nt) * 8 * bits", "codes + (kt * (N / 16) + nt) * 32"),
+    ("linear_bits_ignored", "oracle_reconstruct(codes, cb, scale, K, N, bits, 0, N, w);",
+     "oracle_reconstruct(codes, cb, scale, K, N, 4, 0, N, w);"),
     ("scale_dropped", "* h2d(scale[n]); /* exact product */", "; /* exact product */"),
-    ("scale_slice_column", "h2d(cb[weight_state(codes, N, k, n)]) * h2d(scale[n])",
-     "h2d(cb[weight_state(codes, N, k, n)]) * h2d(scale[j])"),
+    ("scale_slice_column", "h2d(cb[weight_state(codes, N, (int)bits, k, n)]) * h2d(scale[n])",
+     "h2d(cb[weight_state(codes, N, (int)bits, k, n)]) * h2d(scale[j])"),
     ("input_signs_ignored", "had_row(xin, sk, NULL, K, xh);", "had_row(xin, NULL, NULL, K, xh);"),
     ("output_signs_ignored", "had_row(yh, NULL, sn, N, yo);", "had_row(yh, NULL, NULL, N, yo);"),
     ("gemm_transposed_operand", "acc[n] += a * tab[wk[n]];", "acc[n] += a * tab[w[(n * N + k) % (K * N)]];"),

@@ -58,20 +58,26 @@ def signs(config_seed: int, tensor_id: int, n: int, *extra: int) -> np.ndarray:
     return np.where(bits == 1, FP16_ONE, FP16_MINUS_ONE).astype(np.uint16)
 
 
-def layer(config_seed: int, K: int, N: int, set_id: int = 0) -> dict:
+def layer(config_seed: int, K: int, N: int, set_id: int = 0, bits: int = 4) -> dict:
     """One quantized layer: packed codes (uint32 words), column scales, sign vectors.
 
-    codes has K*N/8 uint32 words (4 bits per weight); scale, sign_k and sign_n are
-    fp16 bit patterns (uint16).
+    codes has K*N*bits/32 uint32 words (bits per weight, 1..8; the 4-bit codes
+    come from the stream of [config_seed, T_CODES, set_id], other widths from
+    [config_seed, T_CODES, set_id, bits]); scale, sign_k and sign_n are fp16 bit
+    patterns (uint16).
     """
     if K % 128 or N % 128:
         raise ValueError("K and N must be multiples of 128")
-    codes = rng(config_seed, T_CODES, set_id).integers(0, 2**32, size=K * N // 8, dtype=np.uint32)
+    if not 1 <= bits <= 8:
+        raise ValueError("bits must be in 1..8")
+    stream = rng(config_seed, T_CODES, set_id) if bits == 4 else rng(config_seed, T_CODES, set_id, bits)
+    codes = stream.integers(0, 2**32, size=K * N * bits // 32, dtype=np.uint32)
     scale = rng(config_seed, T_SCALE, set_id).uniform(0.005, 0.02, size=N)
     scale = scale.astype(np.float16).view(np.uint16)
     return {
         "K": K,
         "N": N,
+        "bits": bits,
         "codes": codes,
         "scale": scale,
         "sign_k": signs(config_seed, T_SIGN_K, K, set_id),
