@@ -38,18 +38,19 @@
  *     share a scratch buffer race.
  *
  * Stand-in weight format. The pages name the EXL3 trellis ("4-bit-class
- * trellis format", codebook selectors) without defining it, so this library
- * fixes its own documented stand-in:
+ * trellis format", codebook selectors; 4-bit MLP layers and a 6-bit lm_head,
+ * [P316] "Problem") without defining it, so this library fixes its own
+ * documented stand-in, with b = `bits` per weight, 1 <= b <= 8:
  *   - The layer maps X (M x K) to Y (M x N); the stored weight W is K x N.
- *   - W is cut into 16 x 16 tiles over (k, n). Tile (kt, nt) is 32 uint32
- *     words (128 bytes, 4 bits per weight) starting at word
- *     (kt * (N / 16) + nt) * 32 of `codes`.
- *   - Bit p (0 <= p < 1024) of a tile is bit (p % 32) of word (p / 32).
+ *   - W is cut into 16 x 16 tiles over (k, n). Tile (kt, nt) is 8 b uint32
+ *     words (32 b bytes: 128 at 4 bits) starting at word
+ *     (kt * (N / 16) + nt) * 8 b of `codes` (K N b / 32 words in all).
+ *   - Bit p (0 <= p < 256 b) of a tile is bit (p % 32) of word (p / 32).
  *   - Trellis step i (0..255) of a tile is the weight at k = 16 kt + i % 16,
  *     n = 16 nt + i / 16 (k runs fastest).
- *   - state(i) = sum_{t<16} bit((4 i + t) mod 1024) << t: a 16-bit shift
- *     register that takes in 4 new bits per step; the last three windows wrap
- *     round to the start of the tile (tail-biting).
+ *   - state(i) = sum_{t<16} bit((b i + t) mod 256 b) << t: a 16-bit shift
+ *     register that takes in b new bits per step; the windows that run past
+ *     the tile's last bit wrap round to its start (tail-biting).
  *   - W[k][n] = fp16_rne(codebook[state] * scale[n]) (the product of two fp16
  *     values is exact in fp32, so this is a single rounding).
  *   - The layer computes, per 128-element block and with H the natural-order
@@ -57,7 +58,9 @@
  *         Xr = had(X * sign_k),  Yr = Xr . W,  Y = had(Yr) * sign_n,
  *     i.e. the pages' y = had_r_128(W . had_r_128(x)) with their W equal to
  *     the transpose of this W, plus random +-1 signs on both rotations.
- *   - Only bits = 4 is supported.
+ *   - Every width 1..8 uses the same 65536-entry codebook. The fused path is
+ *     compiled for more tile shapes and for 2 or 4 row groups per pass at
+ *     4 bits; the other widths take one row group per pass.
  */
 #ifndef EXL3_H
 #define EXL3_H
@@ -72,7 +75,7 @@ extern "C" {
 enum {
   EXL3_OK = 0,
   EXL3_EINVAL = 1,   /* NULL pointer where one is required, negative size */
-  EXL3_ESHAPE = 2,   /* K or N not a multiple of 128, bits != 4, misaligned slice, size beyond a limit */
+  EXL3_ESHAPE = 2,   /* K or N not a multiple of 128, bits outside 1..8, misaligned slice, size beyond a limit */
   EXL3_ESCRATCH = 3, /* scratch smaller than the matching *_scratch_bytes() */
   EXL3_EWIDTH = 4,   /* n_valid < 1, n_valid > w_rows, ld_logits < padded width */
   EXL3_EHIP = 5,     /* a HIP runtime call or kernel launch failed */
@@ -87,7 +90,8 @@ enum {
  *              is used), applied before the input rotation; NULL = all +1.
  *   sign_n   : N fp16 values, +-1.0, applied after the output rotation;
  *              NULL = all +1.
- *   K, N     : multiples of 128; bits must be 4. */
+ *   K, N     : multiples of 128; bits in 1..8; the codes take K N bits / 8
+ *              bytes, at most 4 GiB; K below 65536. */
 typedef struct exl3_layer {
   const uint32_t *codes;
   const uint16_t *codebook;
@@ -128,8 +132,8 @@ int exl3_linear(const exl3_layer *layer, const uint16_t *x, int64_t M, uint16_t 
                 size_t scratch_bytes, int32_t prefill_min_m, void *stream);
 
 /* Scratch needed by exl3_linear for this geometry, row count and threshold
- * (the path is chosen the same way). Pure host function. Returns 0 for
- * invalid shapes. */
+ * (the path is chosen the same way), enough for a layer of any width 1..8.
+ * Pure host function. Returns 0 for invalid shapes. */
 size_t exl3_linear_scratch_bytes(int32_t K, int32_t N, int64_t M, int32_t prefill_min_m);
 
 /* Reconstruct columns [n0, n0 + n_count) of W to fp16 [P316 "Kernel

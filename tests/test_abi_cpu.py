@@ -73,7 +73,9 @@ def _linear(layer, x=0x4000, M=1, y=0x5000, scratch=0x6000, nbytes=1 << 30, pm=1
 @pytest.mark.parametrize("layer,status", [
     (_layer(K=100), X.EXL3_ESHAPE),
     (_layer(N=130), X.EXL3_ESHAPE),
-    (_layer(bits=3), X.EXL3_ESHAPE),
+    (_layer(bits=0), X.EXL3_ESHAPE),
+    (_layer(bits=9), X.EXL3_ESHAPE),
+    (_layer(K=65408, N=65792, bits=8), X.EXL3_ESHAPE),  # 8-bit codes past 4 GiB (4 bits would fit)
     (_layer(codes=0), X.EXL3_EINVAL),
     (_layer(cb=0), X.EXL3_EINVAL),
     (_layer(codes=0x1004), X.EXL3_EINVAL),
@@ -83,6 +85,16 @@ def _linear(layer, x=0x4000, M=1, y=0x5000, scratch=0x6000, nbytes=1 << 30, pm=1
 def test_linear_rejects_bad_layers(layer, status):
     assert _linear(layer) == status
     assert X.lib().exl3_strerror(status)
+
+
+def test_every_width_from_1_to_8_passes_validation():
+    # validation passes, so the call gets as far as the scratch check
+    for bits in range(1, 9):
+        assert _linear(_layer(bits=bits), nbytes=0) == X.EXL3_ESCRATCH, bits
+    assert _linear(_layer(K=65408, N=65792, bits=4), nbytes=0) == X.EXL3_ESCRATCH
+    states = X.lib().exl3_decode_states
+    assert states(ctypes.byref(_layer(bits=9)), 0x7000, None) == X.EXL3_ESHAPE
+    assert states(ctypes.byref(_layer(bits=0)), 0x7000, None) == X.EXL3_ESHAPE
 
 
 def test_linear_rejects_bad_calls():

@@ -154,7 +154,7 @@ class Layer:
     @classmethod
     def from_numpy(cls, spec: dict, codebook, device="cuda"):
         return cls(spec["codes"], codebook, spec["scale"], spec.get("sign_k"), spec.get("sign_n"),
-                   K=spec["K"], N=spec["N"], device=device)
+                   K=spec["K"], N=spec["N"], bits=spec.get("bits", 4), device=device)
 
     @property
     def c(self):

@@ -24,12 +24,13 @@ namespace exl3 {
 hipError_t launch_had128(const uint16_t* in, uint16_t* out, int64_t rows, int64_t cols, const uint16_t* sign_pre,
                          const uint16_t* sign_post, hipStream_t stream);
 hipError_t launch_reconstruct_nk(const uint32_t* codes, const uint16_t* cb, const uint16_t* scale, int32_t K,
-                                 int32_t N, int32_t n0, int32_t n_count, uint16_t* wt, int64_t ldw, hipStream_t stream);
-hipError_t launch_reconstruct_kn(const uint32_t* codes, const uint16_t* cb, const uint16_t* scale, int32_t K,
-                                 int32_t N, int32_t n0, int32_t n_count, uint16_t* w, int64_t ldw, bool states,
+                                 int32_t N, int32_t bits, int32_t n0, int32_t n_count, uint16_t* wt, int64_t ldw,
                                  hipStream_t stream);
+hipError_t launch_reconstruct_kn(const uint32_t* codes, const uint16_t* cb, const uint16_t* scale, int32_t K,
+                                 int32_t N, int32_t bits, int32_t n0, int32_t n_count, uint16_t* w, int64_t ldw,
+                                 bool states, hipStream_t stream);
 hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const uint32_t* codes, const uint16_t* cb,
-                              float* partials, int32_t K, int32_t N, int32_t M, const DecodePlan& plan,
+                              float* partials, int32_t K, int32_t N, int32_t M, int32_t bits, const DecodePlan& plan,
                               hipStream_t stream);
 hipError_t launch_decode_finalize(const float* partials, int32_t ks_count, const uint16_t* scale,
                                   const uint16_t* sign_n, uint16_t* y, int32_t M, int32_t N, hipStream_t stream);
@@ -135,17 +136,24 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Shape checks shared by every call that reads packed codes.
+int validate_codes_shape(const exl3_layer* L) {
+  if (L->bits < 1 || L->bits > 8) return fail(EXL3_ESHAPE, "bits = %d; 1 to 8 bits per weight are supported", L->bits);
+  if (L->K <= 0 || L->N <= 0 || L->K % 128 || L->N % 128)
+    return fail(EXL3_ESHAPE, "K = %d and N = %d must be positive multiples of 128", L->K, L->N);
+  // The kernels address the packed codes (K N bits / 8 bytes) and one fp16
+  // weight slice (K x up to 32768 columns) with 32-bit byte offsets.
+  if ((int64_t)L->K * L->N * L->bits / 8 > (int64_t)UINT32_MAX)
+    return fail(EXL3_ESHAPE, "K = %d, N = %d, bits = %d: the packed codes exceed 4 GiB", L->K, L->N, L->bits);
+  if (L->K >= 65536) return fail(EXL3_ESHAPE, "K = %d must be below 65536", L->K);
+  return EXL3_OK;
+}
+
 int validate_layer(const exl3_layer* L) {
   if (!L) return fail(EXL3_EINVAL, "layer is NULL");
   if (!L->codes || !L->codebook || !L->scale) return fail(EXL3_EINVAL, "layer codes, codebook or scale is NULL");
-  if (L->bits != 4) return fail(EXL3_ESHAPE, "bits = %d; only 4 bits per weight is supported", L->bits);
-  if (L->K <= 0 || L->N <= 0 || L->K % 128 || L->N % 128)
-    return fail(EXL3_ESHAPE, "K = %d and N = %d must be positive multiples of 128", L->K, L->N);
-  // The kernels address the packed codes (K N / 2 bytes) and one fp16 weight
-  // slice (K x up to 32768 columns) with 32-bit byte offsets.
-  if ((int64_t)L->K * L->N / 2 > (int64_t)UINT32_MAX)
-    return fail(EXL3_ESHAPE, "K = %d, N = %d: the packed codes exceed 4 GiB", L->K, L->N);
-  if (L->K >= 65536) return fail(EXL3_ESHAPE, "K = %d must be below 65536", L->K);
+  const int st = validate_codes_shape(L);
+  if (st) return st;
   if (!aligned16(L->codes) || !aligned16(L->codebook) || !aligned16(L->scale) || !aligned16(L->sign_k) ||
       !aligned16(L->sign_n))
     return fail(EXL3_EINVAL, "layer tensors must be 16-byte aligned");
@@ -164,15 +172,19 @@ bool use_prefill(int64_t M, int32_t prefill_min_m) { return prefill_min_m > 0 &&
 // a few per cent per group). With x_in_lds (one group) the workgroup's k range
 // is a whole number of 128-element blocks and its rotated slice of the M rows
 // fits DEC_XS_BYTES.
-static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, int G, DecodePlan& best,
-                               double& best_cost) {
+static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, int G, bool four_bits,
+                               DecodePlan& best, double& best_cost) {
   const int ksteps = K / 32, ntiles = N / 16;
   const int64_t passes = (M + 16 * G - 1) / (16 * G);
   const double gfac = 1.0 + 0.05 * (G - 1);
-  const int32_t* inst = G == 1 ? kDecodeNtInstances : G == 2 ? kDecodeNtInstancesG2 : kDecodeNtInstancesG4;
-  const int ninst = G == 1 ? (int)(sizeof(kDecodeNtInstances) / sizeof(int32_t))
-                           : G == 2 ? (int)(sizeof(kDecodeNtInstancesG2) / sizeof(int32_t))
-                                    : (int)(sizeof(kDecodeNtInstancesG4) / sizeof(int32_t));
+  const int32_t* inst = !four_bits ? kDecodeNtInstancesOther
+                        : G == 1    ? kDecodeNtInstances
+                        : G == 2    ? kDecodeNtInstancesG2
+                                    : kDecodeNtInstancesG4;
+  const int ninst = !four_bits ? (int)(sizeof(kDecodeNtInstancesOther) / sizeof(int32_t))
+                    : G == 1   ? (int)(sizeof(kDecodeNtInstances) / sizeof(int32_t))
+                    : G == 2   ? (int)(sizeof(kDecodeNtInstancesG2) / sizeof(int32_t))
+                               : (int)(sizeof(kDecodeNtInstancesG4) / sizeof(int32_t));
   bool found = false;
   const int wns[5] = {1, 2, 4, 8, 16};
   for (int wi = 0; wi < 5; ++wi) {
@@ -216,13 +228,15 @@ static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, i
   return found;
 }
 
-DecodePlan plan_decode(int32_t K, int32_t N, int64_t M) {
-  DecodePlan p{1, 1, K / 32, 1, 1, 16, 1, 0, 1};
+// The 4-bit kernel is compiled for more tile counts and for 2 or 4 row
+// groups per pass; the other widths share one smaller instance set.
+DecodePlan plan_decode(int32_t K, int32_t N, int64_t M, bool four_bits) {
+  DecodePlan p{1, 1, K / 32, 1, 1, 16, four_bits ? 1 : 2, 0, 1};
   double cost = 1e300;
-  if (M <= 16 && plan_decode_search(K, N, M, true, 1, p, cost)) return p;
+  if (M <= 16 && plan_decode_search(K, N, M, true, 1, four_bits, p, cost)) return p;
   cost = 1e300;
   for (int G : {1, 2, 4})
-    if (G == 1 || 16 * (G / 2) < M) plan_decode_search(K, N, M, false, G, p, cost);
+    if (G == 1 || (four_bits && 16 * (G / 2) < M)) plan_decode_search(K, N, M, false, G, four_bits, p, cost);
   return p;
 }
 
@@ -249,28 +263,29 @@ PrefillLayout prefill_layout(int32_t K, int32_t N, int64_t M) {
   return l;
 }
 
-// plan_decode is a pure function of (K, N, M); a small per-thread memo keeps
-// its search off the per-call host path.
-DecodePlan plan_decode_cached(int32_t K, int32_t N, int64_t M) {
+// plan_decode is a pure function of (K, N, M, 4 bits or not); a small
+// per-thread memo keeps its search off the per-call host path.
+DecodePlan plan_decode_cached(int32_t K, int32_t N, int64_t M, bool four_bits) {
   struct Entry {
     int32_t K, N;
     int64_t M;
+    bool four_bits;
     DecodePlan plan;
   };
   thread_local Entry memo[16];
   thread_local int used = 0, next = 0;
   for (int i = 0; i < used; ++i)
-    if (memo[i].K == K && memo[i].N == N && memo[i].M == M) return memo[i].plan;
-  const DecodePlan p = plan_decode(K, N, M);
-  memo[next] = Entry{K, N, M, p};
+    if (memo[i].K == K && memo[i].N == N && memo[i].M == M && memo[i].four_bits == four_bits) return memo[i].plan;
+  const DecodePlan p = plan_decode(K, N, M, four_bits);
+  memo[next] = Entry{K, N, M, four_bits, p};
   next = (next + 1) % 16;
   if (used < 16) ++used;
   return p;
 }
 
-DecodeLayout decode_layout(int32_t K, int32_t N, int64_t M) {
+DecodeLayout decode_layout(int32_t K, int32_t N, int64_t M, int32_t bits) {
   DecodeLayout l;
-  l.plan = plan_decode_cached(K, N, M);
+  l.plan = plan_decode_cached(K, N, M, bits == 4);
   l.xr_off = 0;
   l.part_off = align256((size_t)M * K * 2);
   l.total = l.part_off + align256((size_t)l.plan.ks_count * M * N * 4);
@@ -300,7 +315,10 @@ const char* exl3_strerror(int status) {
 size_t exl3_linear_scratch_bytes(int32_t K, int32_t N, int64_t M, int32_t prefill_min_m) {
   if (K <= 0 || N <= 0 || K % 128 || N % 128 || M < 0) return 0;
   if (M == 0) return 0;
-  return use_prefill(M, prefill_min_m) ? prefill_layout(K, N, M).total : decode_layout(K, N, M).total;
+  if (use_prefill(M, prefill_min_m)) return prefill_layout(K, N, M).total;
+  // the decode path's partial slices depend on the plan, which differs
+  // between 4 bits and the other widths: enough for either
+  return std::max(decode_layout(K, N, M, 4).total, decode_layout(K, N, M, 3).total);
 }
 
 int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* scratch, size_t scratch_bytes,
@@ -337,24 +355,27 @@ int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
     for (int32_t n0 = 0; n0 < N; n0 += l.chunk) {
       const int32_t nc = std::min(l.chunk, N - n0);
       timer_begin(kTimerReconstruct, stream);
-      EXL3_TRY(launch_reconstruct_nk(L->codes, L->codebook, L->scale, K, N, n0, nc, wt, K, stream), "reconstruct");
+      EXL3_TRY(launch_reconstruct_nk(L->codes, L->codebook, L->scale, K, N, L->bits, n0, nc, wt, K, stream),
+               "reconstruct");
       timer_end(kTimerReconstruct, stream);
       EXL3_TRY(launch_gemm_had(wt, xr, y, nc, (int32_t)M, K, N, n0, L->sign_n, (float*)(sb + l.part_off), stream),
                "gemm");
     }
   } else {
-    const DecodeLayout l = decode_layout(K, N, M);
+    const DecodeLayout l = decode_layout(K, N, M, L->bits);
     uint16_t* xr = (uint16_t*)(sb + l.xr_off);
     float* part = (float*)(sb + l.part_off);
     if (l.plan.x_in_lds) {
       timer_begin(kTimerDecode, stream);
-      EXL3_TRY(launch_decode_gemm(x, L->sign_k, L->codes, L->codebook, part, K, N, (int32_t)M, l.plan, stream),
+      EXL3_TRY(launch_decode_gemm(x, L->sign_k, L->codes, L->codebook, part, K, N, (int32_t)M, L->bits, l.plan,
+                                  stream),
                "decode gemm");
       timer_end(kTimerDecode, stream);
     } else {
       EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
       timer_begin(kTimerDecode, stream);
-      EXL3_TRY(launch_decode_gemm(xr, nullptr, L->codes, L->codebook, part, K, N, (int32_t)M, l.plan, stream),
+      EXL3_TRY(launch_decode_gemm(xr, nullptr, L->codes, L->codebook, part, K, N, (int32_t)M, L->bits, l.plan,
+                                  stream),
                "decode gemm");
       timer_end(kTimerDecode, stream);
     }
@@ -382,10 +403,12 @@ int exl3_reconstruct(const exl3_layer* L, int32_t n0, int32_t n_count, uint16_t*
   if (st) return st;
   hipStream_t stream = (hipStream_t)stream_;
   if (layout == EXL3_LAYOUT_NK)
-    EXL3_TRY(launch_reconstruct_nk(L->codes, L->codebook, L->scale, L->K, L->N, n0, n_count, w, ldw, stream),
+    EXL3_TRY(launch_reconstruct_nk(L->codes, L->codebook, L->scale, L->K, L->N, L->bits, n0, n_count, w, ldw,
+                                   stream),
              "reconstruct");
   else
-    EXL3_TRY(launch_reconstruct_kn(L->codes, L->codebook, L->scale, L->K, L->N, n0, n_count, w, ldw, false, stream),
+    EXL3_TRY(launch_reconstruct_kn(L->codes, L->codebook, L->scale, L->K, L->N, L->bits, n0, n_count, w, ldw, false,
+                                   stream),
              "reconstruct");
   return EXL3_OK;
 }
@@ -393,17 +416,12 @@ int exl3_reconstruct(const exl3_layer* L, int32_t n0, int32_t n_count, uint16_t*
 int exl3_decode_states(const exl3_layer* L, uint16_t* states, void* stream_) {
   g_msg[0] = 0;
   if (!L || !L->codes) return fail(EXL3_EINVAL, "layer or codes is NULL");
-  if (L->K <= 0 || L->N <= 0 || L->K % 128 || L->N % 128)
-    return fail(EXL3_ESHAPE, "K = %d and N = %d must be positive multiples of 128", L->K, L->N);
-  // The kernels address the packed codes (K N / 2 bytes) and one fp16 weight
-  // slice (K x up to 32768 columns) with 32-bit byte offsets.
-  if ((int64_t)L->K * L->N / 2 > (int64_t)UINT32_MAX)
-    return fail(EXL3_ESHAPE, "K = %d, N = %d: the packed codes exceed 4 GiB", L->K, L->N);
-  if (L->K >= 65536) return fail(EXL3_ESHAPE, "K = %d must be below 65536", L->K);
-  if (!states || !aligned16(states) || !aligned16(L->codes)) return fail(EXL3_EINVAL, "states NULL or misaligned");
-  int st = check_device();
+  int st = validate_codes_shape(L);
   if (st) return st;
-  EXL3_TRY(launch_reconstruct_kn(L->codes, nullptr, nullptr, L->K, L->N, 0, L->N, states, L->N, true,
+  if (!states || !aligned16(states) || !aligned16(L->codes)) return fail(EXL3_EINVAL, "states NULL or misaligned");
+  st = check_device();
+  if (st) return st;
+  EXL3_TRY(launch_reconstruct_kn(L->codes, nullptr, nullptr, L->K, L->N, L->bits, 0, L->N, states, L->N, true,
                                  (hipStream_t)stream_),
            "decode states");
   return EXL3_OK;

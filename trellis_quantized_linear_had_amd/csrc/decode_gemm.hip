@@ -25,20 +25,26 @@ namespace exl3 {
 #define DEC_THREADS 1024
 #define DEC_WAVES 16
 
-// Loads the code words of NT tiles of one k-step: two per lane (the lane's
-// windows start in word d and end in word d + 1, mod 32). The tile bases are
-// wave-uniform (scalar registers); each lane adds a 32-bit offset (its k-tile
-// row and word).
-template <int NT>
+// Code words per tile and lane: a lane's 8 windows (steps 16c + 8h .. + 7)
+// span BITS * 7 + 16 bits from bit BITS (16c + 8h) of the tile; at 4 bits
+// that is words d = 2c + h and d + 1 (mod 32).
+template <int BITS>
+struct DecWidth {
+  static constexpr int kWords = BITS == 4 ? 2 : TrellisWidth<BITS>::words(8, 8);
+};
+
+// Loads the code words of NT tiles of one k-step, NW per lane. The tile
+// bases are wave-uniform (scalar registers); each lane adds a 32-bit offset
+// (its k-tile row and word).
+template <int NT, int NW, int BITS>
 __device__ __forceinline__ void decode_load_codes(__amdgpu_buffer_rsrc_t codes, int ntiles_total, int step,
-                                                  const int (&tbase)[NT], int loff, int loff1, uint32_t (&lo)[NT],
-                                                  uint32_t (&hi)[NT]) {
-  const uint32_t row = (uint32_t)(2 * step) * ntiles_total * 128u;  // bytes
+                                                  const int (&tbase)[NT], const int (&loff)[NW],
+                                                  uint32_t (&w)[NT][NW]) {
+  const uint32_t row = (uint32_t)(2 * step) * ntiles_total * (uint32_t)TrellisWidth<BITS>::kTileBytes;  // bytes
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    lo[t] = buffer_load_u32(codes, loff, row + tbase[t]);
-    hi[t] = buffer_load_u32(codes, loff1, row + tbase[t]);
-  }
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < NW; ++j) w[t][j] = buffer_load_u32(codes, loff[j], row + tbase[t]);
 }
 
 // The A fragments of one k-step (8 consecutive k of one row of Xr, for each
@@ -49,11 +55,11 @@ __device__ __forceinline__ void decode_load_codes(__amdgpu_buffer_rsrc_t codes, 
 // slice in LDS (16-byte chunk j of row m stored at chunk j ^ (m & 15), so the
 // 16 rows one read instruction touches fall on distinct banks); otherwise
 // from Xr in global memory.
-template <int NT, bool XL, int G>
+template <int NT, bool XL, int G, int NW, int BITS>
 __device__ __forceinline__ void decode_load_step(__amdgpu_buffer_rsrc_t codes, int ntiles_total, int step,
-                                                 const int (&tbase)[NT], int loff, int loff1,
+                                                 const int (&tbase)[NT], const int (&loff)[NW],
                                                  const uint16_t* const (&xsrc)[G], int xstep0, const bool (&mok)[G],
-                                                 uint32_t (&lo)[NT], uint32_t (&hi)[NT], f16x8 (&a)[G]) {
+                                                 uint32_t (&w)[NT][NW], f16x8 (&a)[G]) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (XL) {
@@ -64,14 +70,19 @@ __device__ __forceinline__ void decode_load_step(__amdgpu_buffer_rsrc_t codes, i
       a[g] = mok[g] ? *reinterpret_cast<const f16x8*>(xsrc[g] + 32 * step) : (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  decode_load_codes<NT>(codes, ntiles_total, step, tbase, loff, loff1, lo, hi);
+  decode_load_codes<NT, NW, BITS>(codes, ntiles_total, step, tbase, loff, w);
 }
 
 // Issues the 8 codebook gathers of one tile; the halves stay unpacked until
 // the MFMA that consumes them, so the wait for them can sit right before it.
-__device__ __forceinline__ void gather_tile(const uint16_t* cb_lds, uint32_t lo, uint32_t hi, uint32_t (&g)[8]) {
+template <int NW, int BITS>
+__device__ __forceinline__ void gather_tile(const uint16_t* cb_lds, const uint32_t (&w)[NW], uint32_t woff,
+                                            uint32_t (&g)[8]) {
   uint32_t off[8];
-  window_offsets8(lo, hi, off);
+  if constexpr (BITS == 4)
+    window_offsets8(w[0], w[1], off);
+  else
+    window_offsets_any<BITS, 8, NW>(w, woff, off);
 #pragma unroll
   for (int j = 0; j < 8; ++j) g[j] = lds_cb(cb_lds, off[j]);
 }
@@ -87,15 +98,14 @@ __device__ __forceinline__ f16x8 pack_tile(const uint32_t (&g)[8]) {
 // tile t, so two tiles' gathers (up to the 15 outstanding LDS reads a wave can
 // track) are in flight per wave. Each decoded tile feeds the MFMAs of all G
 // row groups: the gathers, the bound, are shared by up to 64 rows.
-template <int NT, int G>
-__device__ __forceinline__ void decode_mfma_step(const uint16_t* cb_lds, const uint32_t (&lo)[NT],
-                                                 const uint32_t (&hi)[NT], const f16x8 (&a)[G],
-                                                 f32x4 (&acc)[G][NT]) {
+template <int NT, int G, int NW, int BITS>
+__device__ __forceinline__ void decode_mfma_step(const uint16_t* cb_lds, const uint32_t (&w)[NT][NW], uint32_t woff,
+                                                 const f16x8 (&a)[G], f32x4 (&acc)[G][NT]) {
   uint32_t cur[8], nxt[8];
-  gather_tile(cb_lds, lo[0], hi[0], cur);
+  gather_tile<NW, BITS>(cb_lds, w[0], woff, cur);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    if (t + 1 < NT) gather_tile(cb_lds, lo[t + 1], hi[t + 1], nxt);
+    if (t + 1 < NT) gather_tile<NW, BITS>(cb_lds, w[t + 1], woff, nxt);
     const f16x8 b = pack_tile(cur);
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[g], b, acc[g][t], 0, 0, 0);
@@ -105,7 +115,7 @@ __device__ __forceinline__ void decode_mfma_step(const uint16_t* cb_lds, const u
   }
 }
 
-template <int NT, bool XL, int G>
+template <int NT, bool XL, int G, int BITS>
 __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t* __restrict__ xin,
                                                                   const uint16_t* __restrict__ sign_k,
                                                                   const uint32_t* __restrict__ codes,
@@ -143,18 +153,20 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
   // Lane roles in the 16x16x32 MFMA: A row (= x row) and B column (= n) are
   // lane & 15; the 8-element k slice is lane >> 4: k-tile (lane >> 5) of the
   // step, half (lane >> 4) & 1 of that tile's 16 rows.
+  constexpr int NW = DecWidth<BITS>::kWords, TW = TrellisWidth<BITS>::kTileWords;
   const int c = lane & 15;
   const int ktile_in_step = lane >> 5;
-  const int d = 2 * c + ((lane >> 4) & 1);  // first code word of the lane's windows
-  const int d1 = (d + 1) & 31;
-  const int loff = (ktile_in_step * ntiles_total * 32 + d) * 4;  // bytes
-  const int loff1 = (ktile_in_step * ntiles_total * 32 + d1) * 4;
-  const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((int64_t)K * N / 2));
+  const int wstart = BITS * (16 * c + 8 * ((lane >> 4) & 1));  // first bit of the lane's windows
+  const uint32_t woff = (uint32_t)(wstart & 31);
+  int loff[NW];  // bytes
+#pragma unroll
+  for (int j = 0; j < NW; ++j) loff[j] = (ktile_in_step * ntiles_total * TW + (wstart / 32 + j) % TW) * 4;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((int64_t)K * N * BITS / 8));
   // Tiles past the wave's range re-read its last tile (no branches in the
   // hot loop); their sums are never stored.
   int tbase[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) tbase[t] = (wt_begin + min(t, max(nt_w, 1) - 1)) * 128;  // bytes
+  for (int t = 0; t < NT; ++t) tbase[t] = (wt_begin + min(t, max(nt_w, 1) - 1)) * TrellisWidth<BITS>::kTileBytes;
 
   // Prologue. The codebook copy is in flight while (XL) the workgroup
   // rotates its x slice: rows < M, k in [32 s_begin, 32 s_end), 16 lanes per
@@ -291,19 +303,18 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
       xsrc[g] = XL ? xs + (mok[g] ? mrow : 0) * (sw * 32) : xin + (int64_t)(mok[g] ? mrow : 0) * K + 8 * (lane >> 4);
     }
     if (busy) {
-      uint32_t lo0[NT], hi0[NT], lo1[NT], hi1[NT];
+      uint32_t w0[NT][NW], w1[NT][NW];
       f16x8 a0[G], a1[G];
       const int last = ws_end - 1;
-      decode_load_step<NT, XL, G>(crs, ntiles_total, ws_begin, tbase, loff, loff1, xsrc, s_begin, mok, lo0, hi0,
-                                  a0);
+      decode_load_step<NT, XL, G, NW, BITS>(crs, ntiles_total, ws_begin, tbase, loff, xsrc, s_begin, mok, w0, a0);
       for (int step = ws_begin; step < ws_end; step += 2) {
-        decode_load_step<NT, XL, G>(crs, ntiles_total, min(step + 1, last), tbase, loff, loff1, xsrc, s_begin, mok,
-                                    lo1, hi1, a1);
-        decode_mfma_step<NT, G>(cb_lds, lo0, hi0, a0, acc);
+        decode_load_step<NT, XL, G, NW, BITS>(crs, ntiles_total, min(step + 1, last), tbase, loff, xsrc, s_begin,
+                                              mok, w1, a1);
+        decode_mfma_step<NT, G, NW, BITS>(cb_lds, w0, woff, a0, acc);
         if (step + 1 < ws_end) {
-          decode_load_step<NT, XL, G>(crs, ntiles_total, min(step + 2, last), tbase, loff, loff1, xsrc, s_begin,
-                                      mok, lo0, hi0, a0);
-          decode_mfma_step<NT, G>(cb_lds, lo1, hi1, a1, acc);
+          decode_load_step<NT, XL, G, NW, BITS>(crs, ntiles_total, min(step + 2, last), tbase, loff, xsrc, s_begin,
+                                                mok, w0, a0);
+          decode_mfma_step<NT, G, NW, BITS>(cb_lds, w1, woff, a1, acc);
         }
       }
     }
@@ -377,33 +388,58 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __res
 }
 
 hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const uint32_t* codes, const uint16_t* cb,
-                              float* partials, int32_t K, int32_t N, int32_t M, const DecodePlan& plan,
+                              float* partials, int32_t K, int32_t N, int32_t M, int32_t bits, const DecodePlan& plan,
                               hipStream_t stream) {
   const int grid = plan.ks_count * plan.ns_count;
-#define EXL3_DEC_LAUNCH(nt, xl, g)                                                                              \
-  decode_gemm_kernel<nt, xl, g><<<grid, DEC_THREADS, 0, stream>>>(xin, sign_k, codes, cb, partials, K, N, M, plan)
-#define EXL3_DEC_CASE1(nt)                  \
-  case nt:                                  \
-    if (plan.x_in_lds)                      \
-      EXL3_DEC_LAUNCH(nt, true, 1);         \
-    else                                    \
-      EXL3_DEC_LAUNCH(nt, false, 1);        \
+#define EXL3_DEC_LAUNCH(nt, xl, g, b)                                                                          \
+  decode_gemm_kernel<nt, xl, g, b><<<grid, DEC_THREADS, 0, stream>>>(xin, sign_k, codes, cb, partials, K, N, M, \
+                                                                     plan)
+#define EXL3_DEC_CASE1(nt, b)          \
+  case nt:                             \
+    if (plan.x_in_lds)                 \
+      EXL3_DEC_LAUNCH(nt, true, 1, b); \
+    else                               \
+      EXL3_DEC_LAUNCH(nt, false, 1, b);\
     break;
-#define EXL3_DEC_CASEG(nt, g) \
-  case nt:                    \
-    EXL3_DEC_LAUNCH(nt, false, g); \
+#define EXL3_DEC_CASEG(nt, g)         \
+  case nt:                            \
+    EXL3_DEC_LAUNCH(nt, false, g, 4); \
     break;
-  if (plan.groups == 1) {
+#define EXL3_DEC_OTHER(b)                                               \
+  case b:                                                               \
+    if (plan.groups != 1) return hipErrorInvalidValue;                  \
+    switch (plan.nt_wave) {                                             \
+      EXL3_DEC_CASE1(2, b)                                              \
+      EXL3_DEC_CASE1(3, b)                                              \
+      EXL3_DEC_CASE1(5, b)                                              \
+      EXL3_DEC_CASE1(6, b)                                              \
+      default:                                                          \
+        return hipErrorInvalidValue;                                    \
+    }                                                                   \
+    break;
+  if (bits != 4) {
+    switch (bits) {
+      EXL3_DEC_OTHER(1)
+      EXL3_DEC_OTHER(2)
+      EXL3_DEC_OTHER(3)
+      EXL3_DEC_OTHER(5)
+      EXL3_DEC_OTHER(6)
+      EXL3_DEC_OTHER(7)
+      EXL3_DEC_OTHER(8)
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else if (plan.groups == 1) {
     switch (plan.nt_wave) {
-      EXL3_DEC_CASE1(1)
-      EXL3_DEC_CASE1(2)
-      EXL3_DEC_CASE1(3)
-      EXL3_DEC_CASE1(4)
-      EXL3_DEC_CASE1(5)
-      EXL3_DEC_CASE1(6)
-      EXL3_DEC_CASE1(8)
-      EXL3_DEC_CASE1(9)
-      EXL3_DEC_CASE1(10)
+      EXL3_DEC_CASE1(1, 4)
+      EXL3_DEC_CASE1(2, 4)
+      EXL3_DEC_CASE1(3, 4)
+      EXL3_DEC_CASE1(4, 4)
+      EXL3_DEC_CASE1(5, 4)
+      EXL3_DEC_CASE1(6, 4)
+      EXL3_DEC_CASE1(8, 4)
+      EXL3_DEC_CASE1(9, 4)
+      EXL3_DEC_CASE1(10, 4)
       default:
         return hipErrorInvalidValue;
     }
@@ -428,6 +464,7 @@ hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const
   } else {
     return hipErrorInvalidValue;
   }
+#undef EXL3_DEC_OTHER
 #undef EXL3_DEC_CASEG
 #undef EXL3_DEC_CASE1
 #undef EXL3_DEC_LAUNCH

@@ -34,5 +34,8 @@ static const int32_t kDecodeNtInstances[] = {1, 2, 3, 4, 5, 6, 8, 9, 10};
 // ... and with 2 or 4 row groups per pass (accumulators grow with the groups)
 static const int32_t kDecodeNtInstancesG2[] = {1, 2, 3, 4, 5};
 static const int32_t kDecodeNtInstancesG4[] = {1, 2, 3};
+// ... and at widths other than 4 bits (one row group per pass; up to three
+// code words per tile and lane)
+static const int32_t kDecodeNtInstancesOther[] = {2, 3, 5, 6};
 
 }  // namespace exl3

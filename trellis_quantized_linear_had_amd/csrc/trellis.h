@@ -1,4 +1,6 @@
-// Device-side decode of the stand-in trellis format (format defined in exl3.h).
+// Device-side decode of the stand-in trellis format (format defined in exl3.h):
+// b bits per weight, 16x16 tiles of 8b little-endian words, state(i) = the
+// 16-bit window at bit b*i of the tile, wrapping at its 256b bits.
 #pragma once
 
 #include "common.h"
@@ -53,6 +55,47 @@ __device__ __forceinline__ void window_states8(uint32_t lo, uint32_t hi, uint32_
   s[5] = a1 >> 16;
   s[6] = a2 >> 16;
   s[7] = a3 >> 16;
+}
+
+// Windows of NS consecutive steps at any width. A lane whose first window
+// starts at bit `start` of its tile holds the NW words from word start / 32
+// on (mod the tile's 8 BITS words): w[j] = tile[(start / 32 + j) % (8 BITS)],
+// and off = start % 32. One funnel shift per word drops the offset; after it
+// window r starts at bit r * BITS, a compile-time position, so each window is
+// at most one v_alignbit plus one SDWA shift.
+template <int BITS>
+struct TrellisWidth {
+  static_assert(BITS >= 1 && BITS <= 8, "1..8 bits per weight");
+  static constexpr int kTileWords = 8 * BITS;
+  static constexpr int kTileBytes = 32 * BITS;
+  // largest start % 32 of a window run that begins at a step that is a
+  // multiple of `step_align` (16: a tile column; 8: half a column)
+  static constexpr int off_max(int step_align) {
+    return (step_align * BITS) % 32 == 0 ? 0 : (step_align * BITS) % 16 == 0 ? 16 : (step_align * BITS) % 8 == 0 ? 24 : 31;
+  }
+  // words a lane loads for NS windows whose first step is a multiple of step_align
+  static constexpr int words(int ns, int step_align) { return (off_max(step_align) + BITS * (ns - 1) + 16 + 31) / 32; }
+};
+
+template <int BITS, int NS, int NW>
+__device__ __forceinline__ void window_offsets_any(const uint32_t (&w)[NW], uint32_t off, uint32_t (&out)[NS]) {
+  constexpr int NA = (BITS * (NS - 1) + 16 + 31) / 32;  // words after the shift
+  static_assert(NA <= NW, "too few words for the windows");
+  const uint32_t one = 1;
+  uint32_t a[NA + 1];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) a[j] = __builtin_amdgcn_alignbit(j + 1 < NW ? w[j + 1] : 0u, w[j], off);
+  a[NA] = 0;
+#pragma unroll
+  for (int r = 0; r < NS; ++r) {
+    const int pos = r * BITS, idx = pos >> 5, sh = pos & 31;
+    if (sh == 0)
+      out[r] = twice_lo16(a[idx], one);
+    else if (sh == 16)
+      out[r] = twice_hi16(a[idx], one);
+    else
+      out[r] = twice_lo16(__builtin_amdgcn_alignbit(a[idx + 1], a[idx], sh), one);
+  }
 }
 
 // Codebook gather from LDS: the 65536 fp16 entries sit at byte offset 2*state.
