@@ -58,6 +58,10 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: time the fused and prefill paths over M on both MLP "
                          "geometries (crossover) and the wide projection, and print a markdown summary")
+    ap.add_argument("--bits-sweep", action="store_true",
+                    help="instead of the bench line: time decode (M = 1, 16) and prefill (M = 2048) calls and the "
+                         "decode and reconstruct kernels at every width 1..8 bits per weight, K5120 x N17408, and "
+                         "print a markdown summary")
     ap.add_argument("--pmc-workload", choices=("logits", "gemm", "decode", "reconstruct"), default=None,
                     help="run only a counter-collection workload: two 1 GiB device copies (calibration) then "
                          "three calls of the named path; prints nothing else")
@@ -84,6 +88,9 @@ def main():
         return
     if args.sweep:
         print(sweep())
+        return
+    if args.bits_sweep:
+        print(bits_sweep())
         return
 
     lib = _lib.lib()
@@ -476,6 +483,76 @@ def sweep() -> str:
                      Kw, Nw, Mw, us, 2 * Mw * Kw * Nw / us / 1e6, need, Mw * Kw * 2, Kw * Nw * 2,
                      need - Mw * Kw * 2 - Kw * Nw * 2))
     return "\n".join(lines)
+
+
+def bits_sweep() -> str:
+    """Every width 1..8 at K5120 x N17408: decode calls at M = 1 and 16 and a
+    prefill call at M = 2048, each over enough rotating weight sets that their
+    codes (K N bits / 8 bytes each) exceed 512 MB, beyond the 256 MB MALL;
+    back-to-back calls between one event pair, then the decode and
+    reconstruct kernels alone through the library's event hook. Rates use
+    the algorithmic bytes of the width: packed codes for decode; codes +
+    fp16 W^T + scales for reconstruct."""
+    import torch
+
+    import trellis_quantized_linear_had_amd as X
+    from trellis_quantized_linear_had_amd import _lib
+
+    lib = _lib.lib()
+    dev = torch.device("cuda:0")
+    sh = torch.cuda.current_stream().cuda_stream
+    cb = W.codebook()
+
+    def time_calls(layers, x, M, y, scr, reps):
+        def one(i):
+            _lib.check(lib.exl3_linear(layers[i % len(layers)].c, x.data_ptr(), M, y.data_ptr(), scr.data_ptr(),
+                                       scr.numel(), 128, sh))
+        for i in range(2):
+            one(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            one(i)
+        e1.record()
+        torch.cuda.synchronize()
+        call_us = e0.elapsed_time(e1) / reps * 1e3
+        _lib.kernel_timer(True)
+        try:
+            for i in range(reps):
+                one(i)
+            kern = {k: _lib.kernel_timer_read(k) for k in (_lib.TIMER_DECODE, _lib.TIMER_RECONSTRUCT)}
+        finally:
+            _lib.kernel_timer(False)
+        kern_us = {k: (ms / n * 1e3 if n else None) for k, (ms, n) in kern.items()}
+        return call_us, kern_us
+
+    out = ["| bits | code bytes | decode M=1 µs | GB/s | decode kernel µs | GB/s | of 8 TB/s | of LDS-gather roof | "
+           "decode M=16 µs | prefill M=2048 µs | TFLOP/s | reconstruct kernel µs | TB/s |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for bits in range(1, 9):
+        code_bytes = K * N * bits // 8
+        nsets = min(48, -(-512 * 2**20 // code_bytes))
+        layers = [X.Layer.from_numpy(W.layer(W.SEED_DECODE, K, N, s, bits), cb) for s in range(nsets)]
+        row = {}
+        for M in (1, 16, PREFILL_M):
+            x = _lib.to_device_u16(W.activations(W.SEED_DECODE, M, K))
+            y = torch.empty((M, N), dtype=torch.int16, device=dev)
+            scr = torch.empty(X.linear_scratch_bytes(K, N, M), dtype=torch.uint8, device=dev)
+            row[M] = time_calls(layers, x, M, y, scr, 24 if M < 128 else 6)
+            del x, y, scr
+        roof = LDS_GATHER_ROOF_GBPS * bits / 4  # one gather per weight: bits / 8 bytes of codes
+        dk = row[1][1][_lib.TIMER_DECODE]
+        rk = row[PREFILL_M][1][_lib.TIMER_RECONSTRUCT]
+        rbytes = K * N * bits // 8 + K * N * 2 + N * 2
+        out.append("| %d | %d | %.1f | %.0f | %.1f | %.0f | %.1f %% | %.1f %% | %.1f | %.1f | %.1f | %.1f | %.2f |" % (
+            bits, code_bytes, row[1][0], code_bytes / row[1][0] / 1e3, dk, code_bytes / dk / 1e3,
+            100 * code_bytes / dk / 1e3 / HBM_PEAK_GBPS, 100 * code_bytes / dk / 1e3 / roof, row[16][0],
+            row[PREFILL_M][0], PREFILL_FLOP / row[PREFILL_M][0] / 1e6, rk, rbytes / rk / 1e6))
+        print("[bench] bits-sweep %d done (%d weight sets)" % (bits, nsets), file=sys.stderr, flush=True)
+        del layers
+        torch.cuda.empty_cache()
+    return "\n".join(out)
 
 
 def cpu_baseline(target_s: float, log):
