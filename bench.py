@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: time the fused and prefill paths over M on both MLP "
                          "geometries (crossover) and the wide projection, and print a markdown summary")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of the bench line: run the library's probes (LDS gathers, MFMA loop, HBM "
+                         "streams) and print the measured ceilings")
     ap.add_argument("--bits-sweep", action="store_true",
                     help="instead of the bench line: time decode (M = 1, 16) and prefill (M = 2048) calls and the "
                          "decode and reconstruct kernels at every width 1..8 bits per weight, K5120 x N17408, and "
@@ -91,6 +94,12 @@ def main():
         return
     if args.bits_sweep:
         print(bits_sweep())
+        return
+    if args.ceilings:
+        c = ceilings()
+        print("| ceiling | value |\n|---|---|")
+        for k, v in c.items():
+            print("| %s | %s |" % (k, "%.4g" % v if isinstance(v, float) else v))
         return
 
     lib = _lib.lib()
@@ -245,9 +254,22 @@ def main():
         kernels["logits_kernel M=16"] = {
             "bound": "hbm", "achieved": logits_bytes / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "us": us, "per_launch": "%d B fp16 weight rows read (248192 x 5120 x 2)" % logits_bytes}
+    ceil = ceilings(log)
     for k, r in kernels.items():
         r["frac"] = r["achieved"] / r["peak"]
         r["traffic"] = stored_traffic(k)
+        if k.startswith("decode"):
+            r["measured_ceiling"] = {"what": "LDS random-gather probe, GB/s of 4-bit codes",
+                                     "value": ceil["lds_gather_GBps_4bit_codes"]}
+        elif k.startswith("gemm"):
+            r["measured_ceiling"] = {"what": "independent fp16 MFMA loop, TFLOP/s", "value": ceil["mfma_f16_TFLOPs"]}
+        elif k.startswith("logits"):
+            r["measured_ceiling"] = {"what": "HBM read stream, GB/s", "value": ceil["hbm_read_GBps"]}
+        else:  # reconstruct: its reads at the read-stream rate plus its writes at the write-stream rate
+            t_ceil = (K * N // 2 + N * 2) / ceil["hbm_read_GBps"] + K * N * 2 / ceil["hbm_write_GBps"]
+            r["measured_ceiling"] = {"what": "HBM read + write streams, GB/s for this mix",
+                                     "value": RECON_BYTES / t_ceil}
+        r["frac_of_measured_ceiling"] = r["achieved"] / r["measured_ceiling"]["value"]
     # the dominant kernel: most GPU time per step (the decode GEMM runs once
     # per row count, the others once)
     step_us = {k: v["us"] for k, v in kernels.items() if not k.startswith("decode")}
@@ -286,6 +308,7 @@ def main():
         "roofline": roof,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
+        "ceilings": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in ceil.items()},
         "cpu_baseline": None,
     }
 
@@ -483,6 +506,87 @@ def sweep() -> str:
                      Kw, Nw, Mw, us, 2 * Mw * Kw * Nw / us / 1e6, need, Mw * Kw * 2, Kw * Nw * 2,
                      need - Mw * Kw * 2 - Kw * Nw * 2))
     return "\n".join(lines)
+
+
+def ceilings(log=None) -> dict:
+    """Measured ceilings on this GPU, from the library's probes: random 16-bit
+    LDS reads (the trellis codebook gathers), independent fp16 MFMAs (the
+    prefill GEMM's instruction, on operands that change every iteration) for
+    about 40 ms so the clock settles, and HBM streams: 1 GiB read flat, 2.5 GiB
+    read in the padded-logits row pattern (the read ceiling is the faster of
+    the two), 1 GiB written, and a 1 GiB device copy through torch.
+    Each is the best of three runs; the compute probes also report the shader
+    clock their loops ran at (s_memtime cycles over s_memrealtime time)."""
+    import torch
+
+    from trellis_quantized_linear_had_amd import _lib
+
+    lib = _lib.lib()
+    sh = torch.cuda.current_stream().cuda_stream
+    dev = torch.device("cuda:0")
+    sink = torch.empty(_lib.PROBE_SINK_BYTES, dtype=torch.uint8, device=dev)
+    clocks = torch.zeros(4 * _lib.PROBE_WORKGROUPS, dtype=torch.int64, device=dev)
+
+    def timed(fn, reps=3):
+        best, best_clk = None, None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            _lib.check(fn())
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            c = clocks.cpu().numpy().view(np.uint64).reshape(-1, 4).astype(np.float64)
+            cyc = c[:, 1] - c[:, 0]
+            ghz = float(np.mean(cyc / ((c[:, 3] - c[:, 2]) / 100e6)) / 1e9) if np.all(c[:, 3] > c[:, 2]) else None
+            if best is None or ms < best:
+                best, best_clk = ms, (float(np.mean(cyc)), ghz)
+        return best, best_clk
+
+    out = {}
+    it = 4000
+    ms, (cyc, ghz) = timed(lambda: lib.exl3_probe_lds_gather(it, sink.data_ptr(), clocks.data_ptr(), sh))
+    per_wg = 1024 * 16 * it
+    out["lds_gather_lookups_per_cu_clk"] = per_wg / cyc
+    out["lds_gather_clock_GHz"] = ghz
+    out["lds_gather_lookups_per_s"] = _lib.PROBE_WORKGROUPS * per_wg / (ms * 1e-3)
+    out["lds_gather_GBps_4bit_codes"] = out["lds_gather_lookups_per_s"] * 0.5 / 1e9
+    it = 100000
+    ms, (cyc, ghz) = timed(lambda: lib.exl3_probe_mfma(it, sink.data_ptr(), clocks.data_ptr(), sh))
+    out["mfma_f16_TFLOPs"] = _lib.PROBE_WORKGROUPS * 8 * 8 * it * 32768 / (ms * 1e-3) / 1e12
+    out["mfma_clock_GHz"] = ghz
+    nbytes = 1 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf2 = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _lib.check(lib.exl3_probe_stream(1, 0, buf.data_ptr(), nbytes, sink.data_ptr(), sh))
+    ms, _ = timed(lambda: lib.exl3_probe_stream(0, buf.data_ptr(), 0, nbytes, sink.data_ptr(), sh))
+    out["hbm_read_flat_GBps"] = nbytes / (ms * 1e-3) / 1e9
+    # row pattern over 2048 waves of 128 rows of 10240 bytes (2.5 GiB): two
+    # 4-wave workgroups per CU, all resident at once
+    rbytes = 2048 * 128 * 10240
+    rows = torch.empty(rbytes, dtype=torch.uint8, device=dev)
+    _lib.check(lib.exl3_probe_stream(1, 0, rows.data_ptr(), rbytes, sink.data_ptr(), sh))
+    used = rbytes // (10240 * 128) * (10240 * 128)
+    ms, _ = timed(lambda: lib.exl3_probe_stream(2, rows.data_ptr(), 0, rbytes, sink.data_ptr(), sh))
+    out["hbm_read_rows_GBps"] = used / (ms * 1e-3) / 1e9
+    out["hbm_read_GBps"] = max(out["hbm_read_flat_GBps"], out["hbm_read_rows_GBps"])
+    del rows
+    ms, _ = timed(lambda: lib.exl3_probe_stream(1, 0, buf.data_ptr(), nbytes, sink.data_ptr(), sh))
+    out["hbm_write_GBps"] = nbytes / (ms * 1e-3) / 1e9
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        buf2.copy_(buf)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best or 1e30, e0.elapsed_time(e1))
+    out["hbm_copy_GBps"] = 2 * nbytes / (best * 1e-3) / 1e9
+    del buf, buf2, sink, clocks
+    torch.cuda.empty_cache()
+    if log:
+        log("ceilings measured")
+    return out
 
 
 def bits_sweep() -> str:

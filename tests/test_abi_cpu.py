@@ -145,6 +145,17 @@ def test_logits_validation():
     assert call(M=0) == X.EXL3_OK
 
 
+def test_probe_validation_without_gpu():
+    L = X.lib()
+    assert L.exl3_probe_lds_gather(-1, 0x1000, 0x2000, None) == X.EXL3_EINVAL
+    assert L.exl3_probe_mfma(10, 0, 0x2000, None) == X.EXL3_EINVAL
+    assert L.exl3_probe_stream(0, 0x1000, 0, 24, 0x2000, None) == X.EXL3_EINVAL   # not a multiple of 16
+    assert L.exl3_probe_stream(1, 0x1000, 0, 32, 0x2000, None) == X.EXL3_EINVAL   # write needs dst
+    assert L.exl3_probe_stream(0, 0x1000, 0, 0, 0x2000, None) == X.EXL3_OK        # nothing to stream
+    assert L.exl3_probe_stream(3, 0x1000, 0x1000, 32, 0x2000, None) == X.EXL3_EINVAL  # unknown mode
+    assert L.exl3_probe_stream(2, 0, 0x1000, 32, 0x2000, None) == X.EXL3_EINVAL   # row read needs src
+
+
 def test_kernel_timer_validation_without_gpu():
     L = X.lib()
     ms, n = ctypes.c_double(-1.0), ctypes.c_int64(-1)

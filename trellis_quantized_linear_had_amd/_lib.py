@@ -32,8 +32,13 @@ EXPORTS = (
     "exl3_decode_states",
     "exl3_kernel_timer_enable",
     "exl3_kernel_timer_read",
+    "exl3_probe_lds_gather",
+    "exl3_probe_mfma",
+    "exl3_probe_stream",
     "exl3_strerror",
 )
+PROBE_WORKGROUPS = 256
+PROBE_SINK_BYTES = 256 * 32 * 256 * 4
 
 
 class Exl3Layer(ctypes.Structure):
@@ -79,6 +84,12 @@ def lib() -> ctypes.CDLL:
         L.exl3_kernel_timer_enable.restype = ctypes.c_int
         L.exl3_kernel_timer_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
         L.exl3_kernel_timer_read.restype = ctypes.c_int
+        L.exl3_probe_lds_gather.argtypes = [i64, vp, vp, vp]
+        L.exl3_probe_lds_gather.restype = ctypes.c_int
+        L.exl3_probe_mfma.argtypes = [i64, vp, vp, vp]
+        L.exl3_probe_mfma.restype = ctypes.c_int
+        L.exl3_probe_stream.argtypes = [i32, vp, vp, i64, vp, vp]
+        L.exl3_probe_stream.restype = ctypes.c_int
         L.exl3_strerror.argtypes = [ctypes.c_int]
         L.exl3_strerror.restype = ctypes.c_char_p
         _lib = L

@@ -37,6 +37,10 @@ hipError_t launch_decode_finalize(const float* partials, int32_t ks_count, const
 hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
                            int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream);
 size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K);
+hipError_t launch_probe_lds_gather(int64_t iters, uint32_t* sink, uint64_t* clocks, hipStream_t stream);
+hipError_t launch_probe_mfma(int64_t iters, float* sink, uint64_t* clocks, hipStream_t stream);
+hipError_t launch_probe_stream(int32_t write, const void* src, void* dst, int64_t bytes, uint32_t* sink,
+                               hipStream_t stream);
 hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int64_t n_valid, int64_t n_pad,
                          uint16_t* logits, int64_t ld, int64_t* argmax, float* pv, int32_t* pi, uint16_t* xp,
                          hipStream_t stream);
@@ -522,4 +526,41 @@ int exl3_kernel_timer_read(int kind, double* total_ms, int64_t* count) {
   *total_ms = sum;
   *count = (int64_t)mine.size();
   return st;
+}
+
+int exl3_probe_lds_gather(int64_t iters, uint32_t* sink, uint64_t* clocks, void* stream) {
+  g_msg[0] = 0;
+  if (iters < 0) return fail(EXL3_EINVAL, "iters = %lld is negative", (long long)iters);
+  if (!sink || !clocks || !aligned16(sink) || !aligned16(clocks))
+    return fail(EXL3_EINVAL, "sink or clocks NULL or misaligned");
+  int st = check_device();
+  if (st) return st;
+  EXL3_TRY(launch_probe_lds_gather(iters, sink, clocks, (hipStream_t)stream), "lds gather probe");
+  return EXL3_OK;
+}
+
+int exl3_probe_mfma(int64_t iters, float* sink, uint64_t* clocks, void* stream) {
+  g_msg[0] = 0;
+  if (iters < 0) return fail(EXL3_EINVAL, "iters = %lld is negative", (long long)iters);
+  if (!sink || !clocks || !aligned16(sink) || !aligned16(clocks))
+    return fail(EXL3_EINVAL, "sink or clocks NULL or misaligned");
+  int st = check_device();
+  if (st) return st;
+  EXL3_TRY(launch_probe_mfma(iters, sink, clocks, (hipStream_t)stream), "mfma probe");
+  return EXL3_OK;
+}
+
+int exl3_probe_stream(int32_t write, const void* src, void* dst, int64_t bytes, uint32_t* sink, void* stream) {
+  g_msg[0] = 0;
+  if (bytes < 0 || bytes % 16) return fail(EXL3_EINVAL, "bytes = %lld must be a non-negative multiple of 16",
+                                           (long long)bytes);
+  if (write < 0 || write > 2) return fail(EXL3_EINVAL, "stream mode %d is not 0, 1 or 2", write);
+  const void* buf = write == 1 ? dst : src;
+  if (!buf || !aligned16(buf) || !sink || !aligned16(sink))
+    return fail(EXL3_EINVAL, "stream buffer or sink NULL or misaligned");
+  if (bytes == 0) return EXL3_OK;
+  int st = check_device();
+  if (st) return st;
+  EXL3_TRY(launch_probe_stream(write, src, dst, bytes, sink, (hipStream_t)stream), "stream probe");
+  return EXL3_OK;
 }
