@@ -183,6 +183,33 @@ int64_t logits_padded_width(int64_t n_valid, int64_t w_rows);
  * function. */
 size_t logits_scratch_bytes(int64_t M, int32_t K, int64_t n_valid, int64_t w_rows);
 
+/* Quantized output head: the padded-width logits projection of
+ * logits_pad_mask_argmax with the weight held as a trellis layer instead of
+ * dense fp16 rows [P314 "Verification": the checkpoint's lm_head is a
+ * trellis-quantized matrix; P1046 Summary and review follow-ups: padded
+ * width, pad columns -inf before selection]. With
+ *   n_pad = min(round_up(n_valid, 128), N)   (logits_padded_width(n_valid, N))
+ *   logits[m * ld_logits + n] = exl3_linear(layer, x)[m][n]   for n < n_valid
+ *   logits[m * ld_logits + n] = -inf (0xFC00)                 for n_valid <= n < n_pad
+ *   argmax[m] = the smallest n whose fp16 logit equals the row maximum.
+ * Only the layer's first n_pad columns are computed (the output rotation
+ * mixes columns inside 128-column blocks only, so they equal the full layer's
+ * first n_pad columns); columns n_pad .. ld_logits - 1 of logits are left
+ * untouched and codes of columns past n_pad are never read by the decode
+ * path. Dispatch between the fused and the prefill path is exl3_linear's.
+ * x: M x K fp16; logits: M rows with leading dimension ld_logits (a multiple
+ * of 8, >= n_pad), 16-byte aligned; argmax: M int64, 8-byte aligned. scratch:
+ * at least exl3_head_scratch_bytes(K, N, M, n_valid, prefill_min_m) bytes.
+ * EXL3_EWIDTH for n_valid outside [1, N] or a bad ld_logits; other limits and
+ * statuses as exl3_linear. M = 0 is a no-op. */
+int exl3_head_logits_argmax(const exl3_layer *layer, const uint16_t *x, int64_t M, int64_t n_valid,
+                            uint16_t *logits, int64_t ld_logits, int64_t *argmax, void *scratch,
+                            size_t scratch_bytes, int32_t prefill_min_m, void *stream);
+
+/* Scratch needed by exl3_head_logits_argmax (enough for a layer of any width
+ * 1..8). Pure host function; 0 for invalid arguments or M = 0. */
+size_t exl3_head_scratch_bytes(int32_t K, int32_t N, int64_t M, int64_t n_valid, int32_t prefill_min_m);
+
 /* Test hook: states[k * N + n] = the 16-bit trellis state behind W[k][n]. */
 int exl3_decode_states(const exl3_layer *layer, uint16_t *states, void *stream);
 

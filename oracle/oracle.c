@@ -256,6 +256,24 @@ int64_t oracle_padded_width(int64_t n_valid, int64_t w_rows) {
   return aligned < w_rows ? aligned : w_rows;
 }
 
+/* Pad mask and greedy selection over one row of n_pad fp16 logits whose first
+ * n_valid entries are set [P1046 review follow-ups: every pad column is -inf
+ * before selection]: entries n_valid .. n_pad - 1 become -inf, and the result
+ * is the smallest n whose value equals the row maximum (IEEE comparison). */
+static int64_t mask_and_select(uint16_t *row, int64_t n_valid, int64_t n_pad, const double *tab) {
+  for (int64_t n = n_valid; n < n_pad; ++n) row[n] = 0xFC00; /* -inf */
+  int64_t best = 0;
+  double bv = tab[row[0]];
+  for (int64_t n = 1; n < n_pad; ++n) {
+    double v = tab[row[n]];
+    if (v > bv) {
+      bv = v;
+      best = n;
+    }
+  }
+  return best;
+}
+
 /* For each listed row of x (M x K): logits over the padded width, then argmax.
  *   logits[i, n] = fp16(sum_k x[rows[i], k] * w[n, k])  for n < n_valid
  *   logits[i, n] = -inf                                 for n_valid <= n < n_pad
@@ -279,18 +297,32 @@ void oracle_logits(const uint16_t *x, int64_t M, const int64_t *rows, int64_t n_
       for (int64_t k = 0; k < K; ++k) acc += xd[k] * tab[wn[k]];
       logits[i * n_pad + n] = d2h(acc);
     }
-    for (int64_t n = n_valid; n < n_pad; ++n) logits[i * n_pad + n] = 0xFC00; /* -inf */
-    int64_t best = 0;
-    double bv = tab[logits[i * n_pad]];
-    for (int64_t n = 1; n < n_pad; ++n) {
-      double v = tab[logits[i * n_pad + n]];
-      if (v > bv) {
-        bv = v;
-        best = n;
-      }
-    }
-    argmax[i] = best;
+    argmax[i] = mask_and_select(logits + i * n_pad, n_valid, n_pad, tab);
     free(xd);
   }
+  free(tab);
+}
+
+/* ------------------------------------------------------ quantized head ---- */
+
+/* The output head held as a trellis layer [P314 "Verification": the
+ * checkpoint's lm_head is trellis-quantized; P1046 Summary and review
+ * follow-ups]: for each listed row of x, the layer output (oracle_exl3_linear,
+ * all N columns) is cut to its first n_pad = oracle_padded_width(n_valid, N)
+ * columns, then pad-masked and selected as in oracle_logits. logits is
+ * n_rows x n_pad; argmax has n_rows entries. */
+void oracle_head_logits(const uint16_t *x, int64_t M, const int64_t *rows, int64_t n_rows,
+                        const uint32_t *codes, const uint16_t *cb, const uint16_t *scale,
+                        const uint16_t *sign_k, const uint16_t *sign_n, int64_t K, int64_t N,
+                        int64_t bits, int64_t n_valid, uint16_t *logits, int64_t *argmax) {
+  double *tab = h2d_table();
+  int64_t n_pad = oracle_padded_width(n_valid, N);
+  uint16_t *y = (uint16_t *)malloc((size_t)n_rows * N * sizeof(uint16_t));
+  oracle_exl3_linear(x, M, rows, n_rows, codes, cb, scale, sign_k, sign_n, K, N, bits, y);
+  for (int64_t i = 0; i < n_rows; ++i) {
+    memcpy(logits + i * n_pad, y + i * N, (size_t)n_pad * sizeof(uint16_t));
+    argmax[i] = mask_and_select(logits + i * n_pad, n_valid, n_pad, tab);
+  }
+  free(y);
   free(tab);
 }

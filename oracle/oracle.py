@@ -63,6 +63,8 @@ def lib():
         L.oracle_padded_width.argtypes = [_i64, _i64]
         L.oracle_padded_width.restype = _i64
         L.oracle_logits.argtypes = [_u16p, _i64, _i64p, _i64, _u16p, _i64, _i64, _i64, _u16p, _i64p]
+        L.oracle_head_logits.argtypes = [_u16p, _i64, _i64p, _i64, _u32p, _u16p, _u16p, _u16p, _u16p,
+                                         _i64, _i64, _i64, _i64, _u16p, _i64p]
         _lib = L
     return _lib
 
@@ -159,4 +161,26 @@ def logits(x, w, n_valid: int, rows=None):
     out = np.empty((len(rows), n_pad), np.uint16)
     am = np.empty(len(rows), np.int64)
     lib().oracle_logits(x, M, rows, len(rows), w, w_rows, K, n_valid, out, am)
+    return out, am
+
+
+def head_logits(x, layer: dict, cb, n_valid: int, rows=None):
+    """(logits over the padded width, argmax) of a trellis-quantized head for
+    the listed rows of x: the layer output's first padded_width(n_valid, N)
+    columns, pads -inf, first maximum."""
+    x = _u16(x)
+    M, K = x.shape
+    N = layer["N"]
+    if not 1 <= n_valid <= N:
+        raise ValueError("n_valid = %d outside [1, %d]" % (n_valid, N))
+    if rows is None:
+        rows = np.arange(M, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, np.int64)
+    bits = int(layer.get("bits", 4))
+    n_pad = padded_width(n_valid, N)
+    out = np.empty((len(rows), n_pad), np.uint16)
+    am = np.empty(len(rows), np.int64)
+    lib().oracle_head_logits(x, M, rows, len(rows), _codes(layer["codes"], K, N, bits), _u16(cb),
+                             _u16(layer["scale"]), _u16(layer["sign_k"]), _u16(layer["sign_n"]), K, N, bits,
+                             n_valid, out, am)
     return out, am

@@ -145,6 +145,39 @@ def test_logits_validation():
     assert call(M=0) == X.EXL3_OK
 
 
+def test_head_validation_and_scratch():
+    L = X.lib()
+    lay = _layer(K=256, N=1024)
+
+    def call(M=1, n_valid=777, ld=896, nbytes=1 << 30, x=0x4000, logits=0x5000, argmax=0x8000, pm=128):
+        return L.exl3_head_logits_argmax(ctypes.byref(lay), x, M, n_valid, logits, ld, argmax, 0x6000, nbytes, pm,
+                                         None)
+
+    assert call(n_valid=0) == X.EXL3_EWIDTH
+    assert call(n_valid=1025) == X.EXL3_EWIDTH
+    assert call(ld=888) == X.EXL3_EWIDTH        # below the padded width 896
+    assert call(ld=900) == X.EXL3_EWIDTH        # not a multiple of 8
+    assert call(M=-1) == X.EXL3_EINVAL
+    assert call(x=0) == X.EXL3_EINVAL
+    assert call(logits=0x5008) == X.EXL3_EINVAL  # 16-byte alignment
+    assert call(argmax=0) == X.EXL3_EINVAL
+    assert call(argmax=0x8004) == X.EXL3_EINVAL
+    assert call(nbytes=0) == X.EXL3_ESCRATCH
+    assert call(M=0) == X.EXL3_OK
+    assert _linear(_layer(bits=9)) == X.EXL3_ESHAPE
+    assert L.exl3_head_logits_argmax(ctypes.byref(_layer(N=130)), 0x4000, 1, 100, 0x5000, 256, 0x8000, 0x6000,
+                                     1 << 30, 128, None) == X.EXL3_ESHAPE
+    # scratch: the layer's first n_pad columns (decode partials or one prefill slice)
+    assert L.exl3_head_scratch_bytes(256, 1024, 16, 1024, 128) == L.exl3_linear_scratch_bytes(256, 1024, 16, 128)
+    assert L.exl3_head_scratch_bytes(256, 1024, 16, 777, 128) == L.exl3_linear_scratch_bytes(256, 896, 16, 128)
+    assert L.exl3_head_scratch_bytes(256, 1024, 256, 100, 128) == L.exl3_linear_scratch_bytes(256, 128, 256, 128)
+    head = L.exl3_head_scratch_bytes(5120, 248320, 16, 248077, 128)
+    assert head == L.exl3_linear_scratch_bytes(5120, 248192, 16, 128)
+    assert L.exl3_head_scratch_bytes(256, 1024, 16, 0, 128) == 0
+    assert L.exl3_head_scratch_bytes(256, 1024, 16, 1025, 128) == 0
+    assert L.exl3_head_scratch_bytes(256, 1024, 0, 10, 128) == 0
+
+
 def test_probe_validation_without_gpu():
     L = X.lib()
     assert L.exl3_probe_lds_gather(-1, 0x1000, 0x2000, None) == X.EXL3_EINVAL

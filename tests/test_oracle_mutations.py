@@ -11,7 +11,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = ["tests/test_oracle_fp16.py", "tests/test_oracle_hadamard.py", "tests/test_oracle_trellis.py",
-        "tests/test_oracle_trellis_bits.py", "tests/test_oracle_linear.py", "tests/test_oracle_logits.py"]
+        "tests/test_oracle_trellis_bits.py", "tests/test_oracle_linear.py", "tests/test_oracle_logits.py",
+        "tests/test_oracle_head.py"]
 
 # (name, exact text in oracle.c, replacement): each replaced text occurs once.
 MUTATIONS = [
@@ -38,9 +39,13 @@ MUTATIONS = [
     ("gemm_transposed_operand", "acc[n] += a * tab[wk[n]];", "acc[n] += a * tab[w[(n * N + k) % (K * N)]];"),
     ("xr_not_rounded", "xh[k] = tab[d2h(xh[k])];", "xh[k] = xh[k];"),
     ("yr_not_rounded", "yh[n] = tab[d2h(acc[n])];", "yh[n] = acc[n];"),
-    ("pad_not_masked", "logits[i * n_pad + n] = 0xFC00; /* -inf */", "logits[i * n_pad + n] = 0x0000; /* -inf */"),
+    ("pad_not_masked", "row[n] = 0xFC00; /* -inf */", "row[n] = 0x0000; /* -inf */"),
     ("argmax_last_maximum", "if (v > bv) {", "if (v >= bv) {"),
     ("width_multiple_of_64", "(n_valid + 127) / 128 * 128", "(n_valid + 63) / 64 * 64"),
+    ("head_row_stride", "memcpy(logits + i * n_pad, y + i * N,", "memcpy(logits + i * n_pad, y + i * n_pad,"),
+    ("head_tail_columns", "y + i * N, (size_t)n_pad", "y + i * N + (N - n_pad), (size_t)n_pad"),
+    ("head_mask_skipped", "argmax[i] = mask_and_select(logits + i * n_pad, n_valid, n_pad, tab);\n  }\n  free(y);",
+     "argmax[i] = mask_and_select(logits + i * n_pad, n_pad, n_pad, tab);\n  }\n  free(y);"),
 ]
 
 

@@ -9,6 +9,8 @@ from ._lib import (  # noqa: F401
     Layer,
     decode_states,
     had_r_128,
+    head_logits_argmax,
+    head_scratch_bytes,
     linear,
     linear_scratch_bytes,
     logits_pad_mask_argmax,

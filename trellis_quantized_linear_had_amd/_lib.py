@@ -24,6 +24,8 @@ DEFAULT_PREFILL_MIN_M = 128
 EXPORTS = (
     "exl3_linear",
     "exl3_linear_scratch_bytes",
+    "exl3_head_logits_argmax",
+    "exl3_head_scratch_bytes",
     "exl3_reconstruct",
     "had_r_128",
     "logits_pad_mask_argmax",
@@ -68,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.exl3_linear.restype = ctypes.c_int
         L.exl3_linear_scratch_bytes.argtypes = [i32, i32, i64, i32]
         L.exl3_linear_scratch_bytes.restype = sz
+        L.exl3_head_logits_argmax.argtypes = [ctypes.POINTER(Exl3Layer), vp, i64, i64, vp, i64, vp, vp, sz, i32, vp]
+        L.exl3_head_logits_argmax.restype = ctypes.c_int
+        L.exl3_head_scratch_bytes.argtypes = [i32, i32, i64, i64, i32]
+        L.exl3_head_scratch_bytes.restype = sz
         L.exl3_reconstruct.argtypes = [ctypes.POINTER(Exl3Layer), i32, i32, vp, i64, i32, vp]
         L.exl3_reconstruct.restype = ctypes.c_int
         L.had_r_128.argtypes = [vp, vp, i64, i64, vp, vp, vp]
@@ -190,6 +196,27 @@ def linear(x: torch.Tensor, layer: Layer, prefill_min_m: int = DEFAULT_PREFILL_M
     return out
 
 
+def head_scratch_bytes(K: int, N: int, M: int, n_valid: int, prefill_min_m: int = DEFAULT_PREFILL_MIN_M) -> int:
+    return int(lib().exl3_head_scratch_bytes(K, N, M, n_valid, prefill_min_m))
+
+
+def head_logits_argmax(x: torch.Tensor, layer: Layer, n_valid: int, prefill_min_m: int = DEFAULT_PREFILL_MIN_M,
+                       scratch=None, logits=None, argmax=None, stream=None):
+    """(logits over the padded width, argmax) of a trellis-quantized head."""
+    M = x.shape[0]
+    n_pad = logits_padded_width(n_valid, layer.N)
+    if logits is None:
+        logits = torch.empty((M, max(n_pad, 8)), dtype=x.dtype, device=x.device)
+    if argmax is None:
+        argmax = torch.empty(M, dtype=torch.int64, device=x.device)
+    if scratch is None:
+        need = head_scratch_bytes(layer.K, layer.N, M, n_valid, prefill_min_m)
+        scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    check(lib().exl3_head_logits_argmax(layer.c, _ptr(x), M, n_valid, _ptr(logits), logits.stride(0), _ptr(argmax),
+                                        _ptr(scratch), scratch.numel(), prefill_min_m, _stream(stream)))
+    return logits, argmax
+
+
 def reconstruct(layer: Layer, n0: int = 0, n_count: int | None = None, layout: int = LAYOUT_KN, out=None,
                 ldw: int | None = None, stream=None) -> torch.Tensor:
     if n_count is None:
@@ -231,7 +258,8 @@ def logits_pad_mask_argmax(x: torch.Tensor, w: torch.Tensor, n_valid: int, scrat
     n_pad = logits_padded_width(n_valid, w_rows)
     if logits is None:
         logits = torch.empty((M, max(n_pad, 1)), dtype=x.dtype, device=x.device)
-        ld_logits = max(n_pad, 1)
+    if ld_logits is None:
+        ld_logits = logits.stride(0)
     if argmax is None:
         argmax = torch.empty(M, dtype=torch.int64, device=x.device)
     if scratch is None:

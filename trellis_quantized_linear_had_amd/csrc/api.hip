@@ -30,10 +30,13 @@ hipError_t launch_reconstruct_kn(const uint32_t* codes, const uint16_t* cb, cons
                                  int32_t N, int32_t bits, int32_t n0, int32_t n_count, uint16_t* w, int64_t ldw,
                                  bool states, hipStream_t stream);
 hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const uint32_t* codes, const uint16_t* cb,
-                              float* partials, int32_t K, int32_t N, int32_t M, int32_t bits, const DecodePlan& plan,
-                              hipStream_t stream);
+                              float* partials, int32_t K, int32_t N, int32_t ldt, int32_t M, int32_t bits,
+                              const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_decode_finalize(const float* partials, int32_t ks_count, const uint16_t* scale,
-                                  const uint16_t* sign_n, uint16_t* y, int32_t M, int32_t N, hipStream_t stream);
+                                  const uint16_t* sign_n, uint16_t* y, int64_t ldy, int32_t M, int32_t N,
+                                  hipStream_t stream);
+hipError_t launch_row_mask_argmax(uint16_t* logits, int64_t ld, int64_t M, int64_t n_valid, int64_t n_pad,
+                                  int64_t* argmax, hipStream_t stream);
 hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
                            int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream);
 size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K);
@@ -316,76 +319,137 @@ const char* exl3_strerror(int status) {
   }
 }
 
-size_t exl3_linear_scratch_bytes(int32_t K, int32_t N, int64_t M, int32_t prefill_min_m) {
-  if (K <= 0 || N <= 0 || K % 128 || N % 128 || M < 0) return 0;
-  if (M == 0) return 0;
-  if (use_prefill(M, prefill_min_m)) return prefill_layout(K, N, M).total;
+}  // extern "C"
+
+namespace {
+
+// The layer over its leading ncols columns (ncols a multiple of 128, at most
+// N), written to y with leading dimension ldy. Arguments are validated by the
+// callers; scratch holds linear_cols_scratch_bytes(K, ncols, M, pm).
+size_t linear_cols_scratch_bytes(int32_t K, int32_t ncols, int64_t M, int32_t prefill_min_m) {
+  if (use_prefill(M, prefill_min_m)) return prefill_layout(K, ncols, M).total;
   // the decode path's partial slices depend on the plan, which differs
   // between 4 bits and the other widths: enough for either
-  return std::max(decode_layout(K, N, M, 4).total, decode_layout(K, N, M, 3).total);
+  return std::max(decode_layout(K, ncols, M, 4).total, decode_layout(K, ncols, M, 3).total);
 }
 
-int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* scratch, size_t scratch_bytes,
-                int32_t prefill_min_m, void* stream_) {
-  g_msg[0] = 0;
+int linear_cols(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, int64_t ldy, int32_t ncols,
+                char* sb, int32_t prefill_min_m, hipStream_t stream) {
+  const int32_t K = L->K, N = L->N;
+  if (use_prefill(M, prefill_min_m)) {
+    const PrefillLayout l = prefill_layout(K, ncols, M);
+    uint16_t* xr = (uint16_t*)(sb + l.xr_off);
+    uint16_t* wt = (uint16_t*)(sb + l.w_off);
+    EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
+    for (int32_t n0 = 0; n0 < ncols; n0 += l.chunk) {
+      const int32_t nc = std::min(l.chunk, ncols - n0);
+      timer_begin(kTimerReconstruct, stream);
+      EXL3_TRY(launch_reconstruct_nk(L->codes, L->codebook, L->scale, K, N, L->bits, n0, nc, wt, K, stream),
+               "reconstruct");
+      timer_end(kTimerReconstruct, stream);
+      EXL3_TRY(launch_gemm_had(wt, xr, y, nc, (int32_t)M, K, ldy, n0, L->sign_n, (float*)(sb + l.part_off), stream),
+               "gemm");
+    }
+  } else {
+    const DecodeLayout l = decode_layout(K, ncols, M, L->bits);
+    uint16_t* xr = (uint16_t*)(sb + l.xr_off);
+    float* part = (float*)(sb + l.part_off);
+    if (l.plan.x_in_lds) {
+      timer_begin(kTimerDecode, stream);
+      EXL3_TRY(launch_decode_gemm(x, L->sign_k, L->codes, L->codebook, part, K, ncols, N / 16, (int32_t)M, L->bits,
+                                  l.plan, stream),
+               "decode gemm");
+      timer_end(kTimerDecode, stream);
+    } else {
+      EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
+      timer_begin(kTimerDecode, stream);
+      EXL3_TRY(launch_decode_gemm(xr, nullptr, L->codes, L->codebook, part, K, ncols, N / 16, (int32_t)M, L->bits,
+                                  l.plan, stream),
+               "decode gemm");
+      timer_end(kTimerDecode, stream);
+    }
+    EXL3_TRY(launch_decode_finalize(part, l.plan.ks_count, L->scale, L->sign_n, y, ldy, (int32_t)M, ncols, stream),
+             "decode finalize");
+  }
+  return EXL3_OK;
+}
+
+// Common call checks of exl3_linear and exl3_head_logits_argmax.
+int validate_call(const exl3_layer* L, const uint16_t* x, int64_t M, const void* y, const void* scratch,
+                  int32_t prefill_min_m) {
   int st = validate_layer(L);
   if (st) return st;
   if (M < 0) return fail(EXL3_EINVAL, "M = %lld is negative", (long long)M);
   if (prefill_min_m < 0) return fail(EXL3_EINVAL, "prefill_min_m = %d is negative", prefill_min_m);
   if (M > 0x7FFFFFFF) return fail(EXL3_EINVAL, "M = %lld is too large", (long long)M);
   if (M == 0) return EXL3_OK;
-  if (!x || !y) return fail(EXL3_EINVAL, "x or y is NULL");
+  if (!x || !y) return fail(EXL3_EINVAL, "x or the output is NULL");
   if (!scratch) return fail(EXL3_EINVAL, "scratch is NULL");
   if (!aligned16(x) || !aligned16(y) || ((uintptr_t)scratch & 255u))
-    return fail(EXL3_EINVAL, "x and y must be 16-byte aligned and scratch 256-byte aligned");
-  const int32_t K = L->K, N = L->N;
+    return fail(EXL3_EINVAL, "x and the output must be 16-byte aligned and scratch 256-byte aligned");
   // the prefill GEMM addresses the rotated input (M x K fp16) with 32-bit
   // byte offsets
-  if (use_prefill(M, prefill_min_m) && M * K * 2 > (int64_t)UINT32_MAX)
-    return fail(EXL3_ESHAPE, "M = %lld, K = %d: the prefill path needs M * K * 2 below 4 GiB", (long long)M, K);
-  const size_t need = exl3_linear_scratch_bytes(K, N, M, prefill_min_m);
+  if (use_prefill(M, prefill_min_m) && M * L->K * 2 > (int64_t)UINT32_MAX)
+    return fail(EXL3_ESHAPE, "M = %lld, K = %d: the prefill path needs M * K * 2 below 4 GiB", (long long)M, L->K);
+  return EXL3_OK;
+}
+
+int64_t head_padded_width(int64_t n_valid, int64_t n) {
+  const int64_t aligned = (n_valid + 127) / 128 * 128;
+  return aligned < n ? aligned : n;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t exl3_linear_scratch_bytes(int32_t K, int32_t N, int64_t M, int32_t prefill_min_m) {
+  if (K <= 0 || N <= 0 || K % 128 || N % 128 || M < 0) return 0;
+  if (M == 0) return 0;
+  return linear_cols_scratch_bytes(K, N, M, prefill_min_m);
+}
+
+int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* scratch, size_t scratch_bytes,
+                int32_t prefill_min_m, void* stream_) {
+  g_msg[0] = 0;
+  int st = validate_call(L, x, M, y, scratch, prefill_min_m);
+  if (st || M == 0) return st;
+  const size_t need = exl3_linear_scratch_bytes(L->K, L->N, M, prefill_min_m);
+  if (scratch_bytes < need)
+    return fail(EXL3_ESCRATCH, "scratch has %zu bytes; this call needs %zu", scratch_bytes, need);
+  st = check_device();
+  if (st) return st;
+  return linear_cols(L, x, M, y, L->N, L->N, (char*)scratch, prefill_min_m, (hipStream_t)stream_);
+}
+
+size_t exl3_head_scratch_bytes(int32_t K, int32_t N, int64_t M, int64_t n_valid, int32_t prefill_min_m) {
+  if (K <= 0 || N <= 0 || K % 128 || N % 128 || M <= 0 || n_valid < 1 || n_valid > N) return 0;
+  return linear_cols_scratch_bytes(K, (int32_t)head_padded_width(n_valid, N), M, prefill_min_m);
+}
+
+int exl3_head_logits_argmax(const exl3_layer* L, const uint16_t* x, int64_t M, int64_t n_valid, uint16_t* logits,
+                            int64_t ld_logits, int64_t* argmax, void* scratch, size_t scratch_bytes,
+                            int32_t prefill_min_m, void* stream_) {
+  g_msg[0] = 0;
+  int st = validate_call(L, x, M, logits, scratch, prefill_min_m);
+  if (st) return st;
+  if (n_valid < 1 || n_valid > L->N)
+    return fail(EXL3_EWIDTH, "n_valid = %lld must be in [1, N = %d]", (long long)n_valid, L->N);
+  const int64_t n_pad = head_padded_width(n_valid, L->N);
+  if (ld_logits < n_pad || ld_logits % 8)
+    return fail(EXL3_EWIDTH, "ld_logits = %lld must be >= the padded width %lld and a multiple of 8",
+                (long long)ld_logits, (long long)n_pad);
+  if (M == 0) return EXL3_OK;
+  if (!argmax || ((uintptr_t)argmax & 7u)) return fail(EXL3_EINVAL, "argmax is NULL or misaligned");
+  const size_t need = exl3_head_scratch_bytes(L->K, L->N, M, n_valid, prefill_min_m);
   if (scratch_bytes < need)
     return fail(EXL3_ESCRATCH, "scratch has %zu bytes; this call needs %zu", scratch_bytes, need);
   st = check_device();
   if (st) return st;
   hipStream_t stream = (hipStream_t)stream_;
-  char* sb = (char*)scratch;
-
-  if (use_prefill(M, prefill_min_m)) {
-    const PrefillLayout l = prefill_layout(K, N, M);
-    uint16_t* xr = (uint16_t*)(sb + l.xr_off);
-    uint16_t* wt = (uint16_t*)(sb + l.w_off);
-    EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
-    for (int32_t n0 = 0; n0 < N; n0 += l.chunk) {
-      const int32_t nc = std::min(l.chunk, N - n0);
-      timer_begin(kTimerReconstruct, stream);
-      EXL3_TRY(launch_reconstruct_nk(L->codes, L->codebook, L->scale, K, N, L->bits, n0, nc, wt, K, stream),
-               "reconstruct");
-      timer_end(kTimerReconstruct, stream);
-      EXL3_TRY(launch_gemm_had(wt, xr, y, nc, (int32_t)M, K, N, n0, L->sign_n, (float*)(sb + l.part_off), stream),
-               "gemm");
-    }
-  } else {
-    const DecodeLayout l = decode_layout(K, N, M, L->bits);
-    uint16_t* xr = (uint16_t*)(sb + l.xr_off);
-    float* part = (float*)(sb + l.part_off);
-    if (l.plan.x_in_lds) {
-      timer_begin(kTimerDecode, stream);
-      EXL3_TRY(launch_decode_gemm(x, L->sign_k, L->codes, L->codebook, part, K, N, (int32_t)M, L->bits, l.plan,
-                                  stream),
-               "decode gemm");
-      timer_end(kTimerDecode, stream);
-    } else {
-      EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
-      timer_begin(kTimerDecode, stream);
-      EXL3_TRY(launch_decode_gemm(xr, nullptr, L->codes, L->codebook, part, K, N, (int32_t)M, L->bits, l.plan,
-                                  stream),
-               "decode gemm");
-      timer_end(kTimerDecode, stream);
-    }
-    EXL3_TRY(launch_decode_finalize(part, l.plan.ks_count, L->scale, L->sign_n, y, (int32_t)M, N, stream),
-             "decode finalize");
-  }
+  st = linear_cols(L, x, M, logits, ld_logits, (int32_t)n_pad, (char*)scratch, prefill_min_m, stream);
+  if (st) return st;
+  EXL3_TRY(launch_row_mask_argmax(logits, ld_logits, M, n_valid, n_pad, argmax, stream), "mask and argmax");
   return EXL3_OK;
 }
 

@@ -121,7 +121,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
                                                                   const uint32_t* __restrict__ codes,
                                                                   const uint16_t* __restrict__ cb,
                                                                   float* __restrict__ partials, int32_t K,
-                                                                  int32_t N, int32_t M, DecodePlan plan) {
+                                                                  int32_t N, int32_t ldt, int32_t M,
+                                                                  DecodePlan plan) {
   // One 160 KiB block: the codebook (128 KiB), then either the rotated x
   // slice (XL) or the reduction buffer of the multi-group path. After the
   // last gather the whole block serves as reduction slots.
@@ -130,12 +131,15 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds + 32768);
   float* red = lds + 32768;
 
-  const int ksteps_total = K / 32, ntiles_total = N / 16;
+  // N columns are computed (n-tiles 0 .. N/16 - 1); the codes hold ldt
+  // n-tiles per k-tile row (ldt >= N / 16: a leading column range of a wider
+  // layer)
+  const int ksteps_total = K / 32, ntiles_total = ldt;
   const int ks = blockIdx.x / plan.ns_count, ns = blockIdx.x % plan.ns_count;
   const int s_begin = ks * plan.ksteps_per_wg;
   const int s_end = min(s_begin + plan.ksteps_per_wg, ksteps_total);
   const int t_begin = ns * plan.ntiles_per_wg;
-  const int t_end = min(t_begin + plan.ntiles_per_wg, ntiles_total);
+  const int t_end = min(t_begin + plan.ntiles_per_wg, N / 16);
   if (s_begin >= s_end || t_begin >= t_end) return;  // whole workgroup idle (uniform)
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
   int loff[NW];  // bytes
 #pragma unroll
   for (int j = 0; j < NW; ++j) loff[j] = (ktile_in_step * ntiles_total * TW + (wstart / 32 + j) % TW) * 4;
-  const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((int64_t)K * N * BITS / 8));
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((int64_t)K * ldt * 16 * BITS / 8));
   // Tiles past the wave's range re-read its last tile (no branches in the
   // hot loop); their sums are never stored.
   int tbase[NT];
@@ -334,7 +338,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
 __global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __restrict__ partials, int32_t ks_count,
                                                               const uint16_t* __restrict__ scale,
                                                               const uint16_t* __restrict__ sign_n,
-                                                              uint16_t* __restrict__ y, int32_t M, int32_t N) {
+                                                              uint16_t* __restrict__ y, int64_t ldy, int32_t M,
+                                                              int32_t N) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int q = (int)(gid & 15);
   const int64_t nblocks = (int64_t)M * (N / 128);
@@ -384,15 +389,15 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __res
 #pragma unroll
   for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * EXL3_INV_SQRT128, v[2 * j + 1] * EXL3_INV_SQRT128);
   if (sign_n) o ^= (*reinterpret_cast<const u32x4*>(sign_n + n0) & 0x80008000u);
-  if (blk_raw < nblocks) *reinterpret_cast<u32x4*>(y + m * N + n0) = o;
+  if (blk_raw < nblocks) *reinterpret_cast<u32x4*>(y + m * ldy + n0) = o;
 }
 
 hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const uint32_t* codes, const uint16_t* cb,
-                              float* partials, int32_t K, int32_t N, int32_t M, int32_t bits, const DecodePlan& plan,
-                              hipStream_t stream) {
+                              float* partials, int32_t K, int32_t N, int32_t ldt, int32_t M, int32_t bits,
+                              const DecodePlan& plan, hipStream_t stream) {
   const int grid = plan.ks_count * plan.ns_count;
 #define EXL3_DEC_LAUNCH(nt, xl, g, b)                                                                          \
-  decode_gemm_kernel<nt, xl, g, b><<<grid, DEC_THREADS, 0, stream>>>(xin, sign_k, codes, cb, partials, K, N, M, \
+  decode_gemm_kernel<nt, xl, g, b><<<grid, DEC_THREADS, 0, stream>>>(xin, sign_k, codes, cb, partials, K, N, ldt, M, \
                                                                      plan)
 #define EXL3_DEC_CASE1(nt, b)          \
   case nt:                             \
@@ -472,10 +477,11 @@ hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const
 }
 
 hipError_t launch_decode_finalize(const float* partials, int32_t ks_count, const uint16_t* scale,
-                                  const uint16_t* sign_n, uint16_t* y, int32_t M, int32_t N, hipStream_t stream) {
+                                  const uint16_t* sign_n, uint16_t* y, int64_t ldy, int32_t M, int32_t N,
+                                  hipStream_t stream) {
   const int64_t threads = (int64_t)M * (N / 128) * 16;
   decode_finalize_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(partials, ks_count, scale, sign_n,
-                                                                                y, M, N);
+                                                                                y, ldy, M, N);
   return hipGetLastError();
 }
 

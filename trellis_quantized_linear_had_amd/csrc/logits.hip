@@ -207,4 +207,59 @@ hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t
   return hipGetLastError();
 }
 
+// Pad mask and argmax over logits that another kernel has already written
+// (the quantized head: the layer's first n_pad columns). One workgroup per
+// row scans the row in 16-byte chunks (n_pad and ld are multiples of 8, so a
+// chunk never straddles n_valid's side of the row end), rewrites every chunk
+// that holds columns at or past n_valid with those set to -inf, and reduces
+// (largest value, smallest index) over all n_pad columns, pads included.
+#define MA_THREADS 512
+__global__ __launch_bounds__(MA_THREADS) void row_mask_argmax_kernel(uint16_t* __restrict__ logits, int64_t ld,
+                                                                     int64_t n_valid, int64_t n_pad,
+                                                                     int64_t* __restrict__ out) {
+  __shared__ float sv[MA_THREADS];
+  __shared__ int si[MA_THREADS];
+  const int64_t q = blockIdx.x;
+  uint16_t* row = logits + q * ld;
+  float best = -__builtin_inff();
+  int besti = 0x7FFFFFFF;
+  for (int64_t c = (int64_t)threadIdx.x * 8; c < n_pad; c += MA_THREADS * 8) {
+    u32x4 v = *reinterpret_cast<const u32x4*>(row + c);
+    if (c + 8 > n_valid) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c + j >= n_valid) {
+          const int sh = 16 * (j & 1);
+          v[j >> 1] = (v[j >> 1] & ~(0xFFFFu << sh)) | (0xFC00u << sh);
+        }
+      *reinterpret_cast<u32x4*>(row + c) = v;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint16_t h = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+      argmax_combine(best, besti, (float)__builtin_bit_cast(f16, h), (int)(c + j));
+    }
+  }
+  sv[threadIdx.x] = best;
+  si[threadIdx.x] = besti;
+  __syncthreads();
+  for (int s = MA_THREADS / 2; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      float b = sv[threadIdx.x];
+      int bi = si[threadIdx.x];
+      argmax_combine(b, bi, sv[threadIdx.x + s], si[threadIdx.x + s]);
+      sv[threadIdx.x] = b;
+      si[threadIdx.x] = bi;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[q] = si[0];
+}
+
+hipError_t launch_row_mask_argmax(uint16_t* logits, int64_t ld, int64_t M, int64_t n_valid, int64_t n_pad,
+                                  int64_t* argmax, hipStream_t stream) {
+  row_mask_argmax_kernel<<<(unsigned)M, MA_THREADS, 0, stream>>>(logits, ld, n_valid, n_pad, argmax);
+  return hipGetLastError();
+}
+
 }  // namespace exl3
