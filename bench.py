@@ -65,6 +65,10 @@ def parse():
                     help="instead of the bench line: time decode (M = 1, 16) and prefill (M = 2048) calls and the "
                          "decode and reconstruct kernels at every width 1..8 bits per weight, K5120 x N17408, and "
                          "print a markdown summary")
+    ap.add_argument("--head", action="store_true",
+                    help="instead of the bench line: time the trellis-quantized output head (the padded-logits "
+                         "geometry, 4 and 6 bits per weight) at M = 1, 4, 16, 64 beside the dense fp16 logits "
+                         "projection, and print a markdown summary")
     ap.add_argument("--pmc-workload", choices=("logits", "gemm", "decode", "reconstruct"), default=None,
                     help="run only a counter-collection workload: two 1 GiB device copies (calibration) then "
                          "three calls of the named path; prints nothing else")
@@ -94,6 +98,9 @@ def main():
         return
     if args.bits_sweep:
         print(bits_sweep())
+        return
+    if args.head:
+        print(head_sweep())
         return
     if args.ceilings:
         c = ceilings()
@@ -656,6 +663,92 @@ def bits_sweep() -> str:
         print("[bench] bits-sweep %d done (%d weight sets)" % (bits, nsets), file=sys.stderr, flush=True)
         del layers
         torch.cuda.empty_cache()
+    return "\n".join(out)
+
+
+def head_sweep() -> str:
+    """The output head of the padded-logits geometry (K5120, n_valid 248077
+    inside 248320 rows, padded width 248192) held as trellis codes at 4 and 6
+    bits per weight: the head call (decode path: decode GEMM over the first
+    n_pad columns, output stage, pad mask and argmax) and its decode kernel
+    alone, at M = 1, 4, 16, 64, beside the dense fp16 logits projection of
+    the same geometry at M = 16. Each code set (636 / 953 MB) exceeds the
+    256 MB MALL by itself. Rates use the packed codes of the first n_pad
+    columns."""
+    import torch
+
+    import trellis_quantized_linear_had_amd as X
+    from trellis_quantized_linear_had_amd import _lib
+
+    lib = _lib.lib()
+    dev = torch.device("cuda:0")
+    sh = torch.cuda.current_stream().cuda_stream
+    cb = W.codebook()
+    lc = W.LOGITS
+    n_valid, rows = lc["n_valid"], lc["w_rows"]
+    n_pad = X.logits_padded_width(n_valid, rows)
+    assert lc["K"] == K
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    out = ["| bits | M | code bytes (n_pad cols) | head call µs | GB/s | decode kernel µs | GB/s | of 8 TB/s | "
+           "of LDS-gather roof | output stage + mask + argmax µs |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for bits in (4, 6):
+        lay = X.Layer.from_numpy(W.layer(lc["seed"], K, rows, 0, bits), cb)
+        code_bytes = K * n_pad * bits // 8
+        roof = LDS_GATHER_ROOF_GBPS * bits / 4
+        for M in (1, 4, 16, 64):
+            x = _lib.to_device_u16(W.activations(lc["seed"], M, K))
+            lg = torch.empty((M, n_pad), dtype=torch.int16, device=dev)
+            am = torch.empty(M, dtype=torch.int64, device=dev)
+            scr = torch.empty(X.head_scratch_bytes(K, rows, M, n_valid), dtype=torch.uint8, device=dev)
+
+            def call():
+                _lib.check(lib.exl3_head_logits_argmax(lay.c, x.data_ptr(), M, n_valid, lg.data_ptr(), n_pad,
+                                                       am.data_ptr(), scr.data_ptr(), scr.numel(), 128, sh))
+            call_us = timed(call, 20)
+            _lib.kernel_timer(True)
+            try:
+                for _ in range(20):
+                    call()
+                ms, n = _lib.kernel_timer_read(_lib.TIMER_DECODE)
+            finally:
+                _lib.kernel_timer(False)
+            dk = ms / n * 1e3
+            out.append("| %d | %d | %d | %.1f | %.0f | %.1f | %.0f | %.1f %% | %.1f %% | %.1f |" % (
+                bits, M, code_bytes, call_us, code_bytes / call_us / 1e3, dk, code_bytes / dk / 1e3,
+                100 * code_bytes / dk / 1e3 / HBM_PEAK_GBPS, 100 * code_bytes / dk / 1e3 / roof, call_us - dk))
+            print("[bench] head bits=%d M=%d done" % (bits, M), file=sys.stderr, flush=True)
+            del x, lg, am, scr
+        del lay
+        torch.cuda.empty_cache()
+    # the dense fp16 projection of the same geometry, for comparison
+    M = LOGITS_M
+    wl = _lib.to_device_u16(W.logits_weights(lc["seed"], rows, K, threads=16))
+    x = _lib.to_device_u16(W.activations(lc["seed"], M, K))
+    lg = torch.empty((M, n_pad), dtype=torch.int16, device=dev)
+    am = torch.empty(M, dtype=torch.int64, device=dev)
+    scr = torch.empty(X.logits_scratch_bytes(M, K, n_valid, rows), dtype=torch.uint8, device=dev)
+
+    def dense():
+        _lib.check(lib.logits_pad_mask_argmax(x.data_ptr(), M, K, wl.data_ptr(), rows, n_valid, lg.data_ptr(), n_pad,
+                                              am.data_ptr(), scr.data_ptr(), scr.numel(), sh))
+    dense_us = timed(dense, 20)
+    wbytes = n_pad * K * 2
+    out.append("")
+    out.append("Dense fp16 logits projection, same geometry, M = %d: %.1f µs per call (%d weight bytes, %.0f GB/s)."
+               % (M, dense_us, wbytes, wbytes / dense_us / 1e3))
     return "\n".join(out)
 
 

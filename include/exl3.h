@@ -206,8 +206,10 @@ int exl3_head_logits_argmax(const exl3_layer *layer, const uint16_t *x, int64_t 
                             uint16_t *logits, int64_t ld_logits, int64_t *argmax, void *scratch,
                             size_t scratch_bytes, int32_t prefill_min_m, void *stream);
 
-/* Scratch needed by exl3_head_logits_argmax (enough for a layer of any width
- * 1..8). Pure host function; 0 for invalid arguments or M = 0. */
+/* Scratch needed by exl3_head_logits_argmax: exl3_linear's scratch for the
+ * first n_pad columns (enough for a layer of any width 1..8), then one
+ * (fp32 maximum, int32 index) pair per row and 4096-column piece of the
+ * argmax. Pure host function; 0 for invalid arguments or M = 0. */
 size_t exl3_head_scratch_bytes(int32_t K, int32_t N, int64_t M, int64_t n_valid, int32_t prefill_min_m);
 
 /* Test hook: states[k * N + n] = the 16-bit trellis state behind W[k][n]. */

@@ -167,12 +167,21 @@ def test_head_validation_and_scratch():
     assert _linear(_layer(bits=9)) == X.EXL3_ESHAPE
     assert L.exl3_head_logits_argmax(ctypes.byref(_layer(N=130)), 0x4000, 1, 100, 0x5000, 256, 0x8000, 0x6000,
                                      1 << 30, 128, None) == X.EXL3_ESHAPE
-    # scratch: the layer's first n_pad columns (decode partials or one prefill slice)
-    assert L.exl3_head_scratch_bytes(256, 1024, 16, 1024, 128) == L.exl3_linear_scratch_bytes(256, 1024, 16, 128)
-    assert L.exl3_head_scratch_bytes(256, 1024, 16, 777, 128) == L.exl3_linear_scratch_bytes(256, 896, 16, 128)
-    assert L.exl3_head_scratch_bytes(256, 1024, 256, 100, 128) == L.exl3_linear_scratch_bytes(256, 128, 256, 128)
+    # scratch: the layer's first n_pad columns (decode partials or one prefill
+    # slice), then one (fp32 max, int32 index) pair per row and 4096-column piece
+    def extra(M, n_pad):
+        pairs = M * -(-n_pad // 4096)
+        return 2 * (-(-pairs * 4 // 256) * 256)
+
+    def lin(n, M):
+        return -(-L.exl3_linear_scratch_bytes(256, n, M, 128) // 256) * 256
+
+    assert L.exl3_head_scratch_bytes(256, 1024, 16, 1024, 128) == lin(1024, 16) + extra(16, 1024)
+    assert L.exl3_head_scratch_bytes(256, 1024, 16, 777, 128) == lin(896, 16) + extra(16, 896)
+    assert L.exl3_head_scratch_bytes(256, 1024, 256, 100, 128) == lin(128, 256) + extra(256, 128)
     head = L.exl3_head_scratch_bytes(5120, 248320, 16, 248077, 128)
-    assert head == L.exl3_linear_scratch_bytes(5120, 248192, 16, 128)
+    base = L.exl3_linear_scratch_bytes(5120, 248192, 16, 128)
+    assert base < head <= base + 256 + extra(16, 248192)
     assert L.exl3_head_scratch_bytes(256, 1024, 16, 0, 128) == 0
     assert L.exl3_head_scratch_bytes(256, 1024, 16, 1025, 128) == 0
     assert L.exl3_head_scratch_bytes(256, 1024, 0, 10, 128) == 0

@@ -35,8 +35,9 @@ hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const
 hipError_t launch_decode_finalize(const float* partials, int32_t ks_count, const uint16_t* scale,
                                   const uint16_t* sign_n, uint16_t* y, int64_t ldy, int32_t M, int32_t N,
                                   hipStream_t stream);
-hipError_t launch_row_mask_argmax(uint16_t* logits, int64_t ld, int64_t M, int64_t n_valid, int64_t n_pad,
-                                  int64_t* argmax, hipStream_t stream);
+hipError_t launch_head_mask_argmax(uint16_t* logits, int64_t ld, int64_t M, int64_t n_valid, int64_t n_pad,
+                                   int64_t* argmax, float* pv, int32_t* pi, hipStream_t stream);
+int64_t head_argmax_items(int64_t n_pad);
 hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
                            int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream);
 size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K);
@@ -399,6 +400,22 @@ int64_t head_padded_width(int64_t n_valid, int64_t n) {
   return aligned < n ? aligned : n;
 }
 
+// The linear's scratch over the first n_pad columns, then the per-piece
+// (max, index) pairs of the argmax: floats, then int32s.
+struct HeadLayout {
+  size_t pv_off, pi_off, total;
+};
+
+HeadLayout head_layout(int32_t K, int32_t N, int64_t M, int64_t n_valid, int32_t prefill_min_m) {
+  const int64_t n_pad = head_padded_width(n_valid, N);
+  const size_t pairs = (size_t)M * head_argmax_items(n_pad);
+  HeadLayout h;
+  h.pv_off = align256(linear_cols_scratch_bytes(K, (int32_t)n_pad, M, prefill_min_m));
+  h.pi_off = h.pv_off + align256(pairs * sizeof(float));
+  h.total = h.pi_off + align256(pairs * sizeof(int32_t));
+  return h;
+}
+
 }  // namespace
 
 extern "C" {
@@ -424,7 +441,7 @@ int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
 
 size_t exl3_head_scratch_bytes(int32_t K, int32_t N, int64_t M, int64_t n_valid, int32_t prefill_min_m) {
   if (K <= 0 || N <= 0 || K % 128 || N % 128 || M <= 0 || n_valid < 1 || n_valid > N) return 0;
-  return linear_cols_scratch_bytes(K, (int32_t)head_padded_width(n_valid, N), M, prefill_min_m);
+  return head_layout(K, N, M, n_valid, prefill_min_m).total;
 }
 
 int exl3_head_logits_argmax(const exl3_layer* L, const uint16_t* x, int64_t M, int64_t n_valid, uint16_t* logits,
@@ -447,9 +464,13 @@ int exl3_head_logits_argmax(const exl3_layer* L, const uint16_t* x, int64_t M, i
   st = check_device();
   if (st) return st;
   hipStream_t stream = (hipStream_t)stream_;
-  st = linear_cols(L, x, M, logits, ld_logits, (int32_t)n_pad, (char*)scratch, prefill_min_m, stream);
+  char* sb = (char*)scratch;
+  const HeadLayout h = head_layout(L->K, L->N, M, n_valid, prefill_min_m);
+  st = linear_cols(L, x, M, logits, ld_logits, (int32_t)n_pad, sb, prefill_min_m, stream);
   if (st) return st;
-  EXL3_TRY(launch_row_mask_argmax(logits, ld_logits, M, n_valid, n_pad, argmax, stream), "mask and argmax");
+  EXL3_TRY(launch_head_mask_argmax(logits, ld_logits, M, n_valid, n_pad, argmax, (float*)(sb + h.pv_off),
+                                   (int32_t*)(sb + h.pi_off), stream),
+           "mask and argmax");
   return EXL3_OK;
 }
 
