@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: time the fused and prefill paths over M on both MLP "
                          "geometries (crossover) and the wide projection, and print a markdown summary")
+    ap.add_argument("--sweep-bits", type=int, default=4, choices=range(1, 9), metavar="BITS",
+                    help="width of the --sweep layers; other than 4 adds a K5120 x N5120 projection and stops at "
+                         "M = 1024")
     ap.add_argument("--ceilings", action="store_true",
                     help="instead of the bench line: run the library's probes (LDS gathers, MFMA loop, HBM "
                          "streams) and print the measured ceilings")
@@ -94,7 +97,7 @@ def main():
         pmc_workload(args.pmc_workload)
         return
     if args.sweep:
-        print(sweep())
+        print(sweep(args.sweep_bits))
         return
     if args.bits_sweep:
         print(bits_sweep())
@@ -445,13 +448,16 @@ def pmc_workload(kind: str):
     print("[bench] pmc workload %s done" % kind, file=sys.stderr, flush=True)
 
 
-def sweep() -> str:
-    """Fused (decode-GEMM) and prefill (reconstruct + GEMM) paths over M on
-    both MLP geometries, forced through prefill_min_m (0: fused at every M;
-    1: prefill at every M), 6 rotating weight sets (267 MB of codes, above the
-    256 MB MALL); then the wide projection K5120 x N32768 at M = 2048 (one
-    32768-column slice) with its scratch bytes. Back-to-back calls between one
-    event pair per cell."""
+def sweep(bits: int = 4) -> str:
+    """Fused (decode-GEMM) and prefill (reconstruct + GEMM) paths over M,
+    forced through prefill_min_m (0: fused at every M; 1: prefill at every M),
+    6 rotating weight sets per geometry (267 MB of 4-bit codes at the MLP
+    geometries, above the 256 MB MALL), back-to-back calls between one event
+    pair per cell. At 4 bits: both MLP geometries, then the wide projection
+    K5120 x N32768 at M = 2048 (one 32768-column slice) with its scratch
+    bytes. At another width: the MLP geometries and a square K5120 x N5120
+    projection (attention-sized), M up to 1024, to locate that width's
+    crossover."""
     import torch
 
     import trellis_quantized_linear_had_amd as X
@@ -477,11 +483,15 @@ def sweep() -> str:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e3
 
-    out = ["| geometry | M | fused µs | prefill µs | faster | prefill TFLOP/s |", "|---|---|---|---|---|---|"]
+    out = ["| geometry | bits | M | fused µs | prefill µs | faster | prefill TFLOP/s |",
+           "|---|---|---|---|---|---|---|"]
     cross = {}
-    for gi, (Kg, Ng) in enumerate(((5120, 17408), (17408, 5120))):
-        layers = [X.Layer.from_numpy(W.layer(W.SEED_PREFILL, Kg, Ng, 2 * s + gi), cb) for s in range(6)]
-        for M in (16, 32, 64, 96, 128, 192, 256, 512, 1024, 2048, 4096):
+    geoms = ((5120, 17408), (17408, 5120)) if bits == 4 else ((5120, 17408), (17408, 5120), (5120, 5120))
+    Ms = (16, 32, 64, 96, 128, 192, 256, 512, 1024, 2048, 4096) if bits == 4 else (16, 32, 64, 96, 128, 192, 256,
+                                                                                    512, 1024)
+    for gi, (Kg, Ng) in enumerate(geoms):
+        layers = [X.Layer.from_numpy(W.layer(W.SEED_PREFILL, Kg, Ng, 2 * s + gi, bits), cb) for s in range(6)]
+        for M in Ms:
             x = _lib.to_device_u16(W.activations(W.SEED_PREFILL, M, Kg, gi))
             y = torch.empty((M, Ng), dtype=torch.int16, device=dev)
             scr = torch.empty(max(X.linear_scratch_bytes(Kg, Ng, M, 0), X.linear_scratch_bytes(Kg, Ng, M, 1)),
@@ -490,8 +500,8 @@ def sweep() -> str:
             pre = time_calls(layers, x, M, y, scr, 1, 6)
             if fused is not None and pre < fused and (Kg, Ng) not in cross:
                 cross[(Kg, Ng)] = M
-            out.append("| K%d×N%d | %d | %s | %.1f | %s | %.1f |" % (
-                Kg, Ng, M, "%.1f" % fused if fused is not None else "—", pre,
+            out.append("| K%d×N%d | %d | %d | %s | %.1f | %s | %.1f |" % (
+                Kg, Ng, bits, M, "%.1f" % fused if fused is not None else "—", pre,
                 "—" if fused is None else ("prefill" if pre < fused else "fused"), 2 * M * Kg * Ng / pre / 1e6))
             print("[bench] sweep K%d N%d M%d done" % (Kg, Ng, M), file=sys.stderr, flush=True)
             del x, y, scr
@@ -499,7 +509,10 @@ def sweep() -> str:
         torch.cuda.empty_cache()
     lines = ["\n".join(out), ""]
     for (Kg, Ng), M in cross.items():
-        lines.append("Crossover K%d×N%d: prefill is faster from M = %d on (among the M measured)." % (Kg, Ng, M))
+        lines.append("Crossover K%d×N%d, %d bits: prefill is faster from M = %d on (among the M measured)." % (
+            Kg, Ng, bits, M))
+    if bits != 4:
+        return "\n".join(lines)
     Kw, Nw, Mw = 5120, 32768, 2048
     layers = [X.Layer.from_numpy(W.layer(W.SEED_WIDE, Kw, Nw, s), cb) for s in range(3)]
     x = _lib.to_device_u16(W.activations(W.SEED_WIDE, Mw, Kw))

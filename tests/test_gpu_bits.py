@@ -80,7 +80,7 @@ def test_reconstruct_nk_over_several_launches(T, X, cb, bits):
 
 
 @pytest.mark.parametrize("bits", BITS)
-@pytest.mark.parametrize("M", [1, 16, 40])
+@pytest.mark.parametrize("M", [1, 16, 40, 100])
 def test_linear_both_paths(T, X, cb, bits, M):
     H.announce("linear bits=%d K256 N384 M=%d" % (bits, M))
     K, N = 256, 384
@@ -110,7 +110,7 @@ def test_linear_deterministic_other_width(T, X, cb):
     K, N = 1024, 2048
     L = WL.layer(36, K, N, 0, 5)
     lay = X.Layer.from_numpy(L, cb)
-    for M in (8, 300):
+    for M in (8, 70, 300):
         x = dev16(WL.activations(36, M, K))
         first = host16(X.linear(x, lay))
         for _ in range(3):

@@ -185,14 +185,20 @@ static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, i
   const int ksteps = K / 32, ntiles = N / 16;
   const int64_t passes = (M + 16 * G - 1) / (16 * G);
   const double gfac = 1.0 + 0.05 * (G - 1);
-  const int32_t* inst = !four_bits ? kDecodeNtInstancesOther
-                        : G == 1    ? kDecodeNtInstances
-                        : G == 2    ? kDecodeNtInstancesG2
-                                    : kDecodeNtInstancesG4;
-  const int ninst = !four_bits ? (int)(sizeof(kDecodeNtInstancesOther) / sizeof(int32_t))
-                    : G == 1   ? (int)(sizeof(kDecodeNtInstances) / sizeof(int32_t))
-                    : G == 2   ? (int)(sizeof(kDecodeNtInstancesG2) / sizeof(int32_t))
-                               : (int)(sizeof(kDecodeNtInstancesG4) / sizeof(int32_t));
+  const int32_t* inst = nullptr;
+  int ninst = 0;
+  auto pick = [&](const int32_t* list, size_t bytes) {
+    inst = list;
+    ninst = (int)(bytes / sizeof(int32_t));
+  };
+  if (four_bits)
+    G == 1 ? pick(kDecodeNtInstances, sizeof(kDecodeNtInstances))
+    : G == 2 ? pick(kDecodeNtInstancesG2, sizeof(kDecodeNtInstancesG2))
+             : pick(kDecodeNtInstancesG4, sizeof(kDecodeNtInstancesG4));
+  else
+    G == 1 ? pick(kDecodeNtInstancesOther, sizeof(kDecodeNtInstancesOther))
+    : G == 2 ? pick(kDecodeNtInstancesOtherG2, sizeof(kDecodeNtInstancesOtherG2))
+             : pick(kDecodeNtInstancesOtherG4, sizeof(kDecodeNtInstancesOtherG4));
   bool found = false;
   const int wns[5] = {1, 2, 4, 8, 16};
   for (int wi = 0; wi < 5; ++wi) {
@@ -236,15 +242,15 @@ static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, i
   return found;
 }
 
-// The 4-bit kernel is compiled for more tile counts and for 2 or 4 row
-// groups per pass; the other widths share one smaller instance set.
+// The 4-bit kernel is compiled for more tile counts; the other widths share
+// smaller instance sets. Both have 2 and 4 row groups per pass.
 DecodePlan plan_decode(int32_t K, int32_t N, int64_t M, bool four_bits) {
   DecodePlan p{1, 1, K / 32, 1, 1, 16, four_bits ? 1 : 2, 0, 1};
   double cost = 1e300;
   if (M <= 16 && plan_decode_search(K, N, M, true, 1, four_bits, p, cost)) return p;
   cost = 1e300;
   for (int G : {1, 2, 4})
-    if (G == 1 || (four_bits && 16 * (G / 2) < M)) plan_decode_search(K, N, M, false, G, four_bits, p, cost);
+    if (G == 1 || 16 * (G / 2) < M) plan_decode_search(K, N, M, false, G, four_bits, p, cost);
   return p;
 }
 

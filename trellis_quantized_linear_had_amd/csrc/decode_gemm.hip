@@ -410,16 +410,39 @@ hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const
   case nt:                            \
     EXL3_DEC_LAUNCH(nt, false, g, 4); \
     break;
+#define EXL3_DEC_CASEGB(nt, g, b)      \
+  case nt:                             \
+    EXL3_DEC_LAUNCH(nt, false, g, b);  \
+    break;
 #define EXL3_DEC_OTHER(b)                                               \
   case b:                                                               \
-    if (plan.groups != 1) return hipErrorInvalidValue;                  \
-    switch (plan.nt_wave) {                                             \
-      EXL3_DEC_CASE1(2, b)                                              \
-      EXL3_DEC_CASE1(3, b)                                              \
-      EXL3_DEC_CASE1(5, b)                                              \
-      EXL3_DEC_CASE1(6, b)                                              \
-      default:                                                          \
-        return hipErrorInvalidValue;                                    \
+    if (plan.groups == 1) {                                             \
+      switch (plan.nt_wave) {                                           \
+        EXL3_DEC_CASE1(2, b)                                            \
+        EXL3_DEC_CASE1(3, b)                                            \
+        EXL3_DEC_CASE1(5, b)                                            \
+        EXL3_DEC_CASE1(6, b)                                            \
+        default:                                                        \
+          return hipErrorInvalidValue;                                  \
+      }                                                                 \
+    } else if (plan.groups == 2 && !plan.x_in_lds) {                    \
+      switch (plan.nt_wave) {                                           \
+        EXL3_DEC_CASEGB(2, 2, b)                                        \
+        EXL3_DEC_CASEGB(3, 2, b)                                        \
+        EXL3_DEC_CASEGB(4, 2, b)                                        \
+        EXL3_DEC_CASEGB(5, 2, b)                                        \
+        default:                                                        \
+          return hipErrorInvalidValue;                                  \
+      }                                                                 \
+    } else if (plan.groups == 4 && !plan.x_in_lds) {                    \
+      switch (plan.nt_wave) {                                           \
+        EXL3_DEC_CASEGB(1, 4, b)                                        \
+        EXL3_DEC_CASEGB(2, 4, b)                                        \
+        default:                                                        \
+          return hipErrorInvalidValue;                                  \
+      }                                                                 \
+    } else {                                                            \
+      return hipErrorInvalidValue;                                      \
     }                                                                   \
     break;
   if (bits != 4) {
@@ -470,6 +493,7 @@ hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const
     return hipErrorInvalidValue;
   }
 #undef EXL3_DEC_OTHER
+#undef EXL3_DEC_CASEGB
 #undef EXL3_DEC_CASEG
 #undef EXL3_DEC_CASE1
 #undef EXL3_DEC_LAUNCH

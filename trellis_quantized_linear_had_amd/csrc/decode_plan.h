@@ -34,8 +34,10 @@ static const int32_t kDecodeNtInstances[] = {1, 2, 3, 4, 5, 6, 8, 9, 10};
 // ... and with 2 or 4 row groups per pass (accumulators grow with the groups)
 static const int32_t kDecodeNtInstancesG2[] = {1, 2, 3, 4, 5};
 static const int32_t kDecodeNtInstancesG4[] = {1, 2, 3};
-// ... and at widths other than 4 bits (one row group per pass; up to three
-// code words per tile and lane)
+// ... and at widths other than 4 bits (up to three code words per tile and
+// lane): one, two or four row groups per pass
 static const int32_t kDecodeNtInstancesOther[] = {2, 3, 5, 6};
+static const int32_t kDecodeNtInstancesOtherG2[] = {2, 3, 4, 5};
+static const int32_t kDecodeNtInstancesOtherG4[] = {1, 2};
 
 }  // namespace exl3
