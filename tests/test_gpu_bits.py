@@ -115,3 +115,17 @@ def test_linear_deterministic_other_width(T, X, cb):
         first = host16(X.linear(x, lay))
         for _ in range(3):
             assert np.array_equal(host16(X.linear(x, lay)), first)
+
+
+@pytest.mark.parametrize("bits,M", [(4, 8), (4, 16), (6, 16)])
+def test_linear_wide_layer_small_m(T, X, cb, bits, M):
+    """K5120 x N32768 at M <= 16: the planner takes the decode plan without
+    the prologue rotation here (a separate rotation pass, no k-split), the
+    one wide layers get; sampled rows against the oracle."""
+    H.announce("linear bits=%d K5120 N32768 M=%d (sampled rows)" % (bits, M))
+    K, N = 5120, 32768
+    L = WL.layer(37, K, N, 0, bits)
+    x = WL.activations(37, M, K)
+    rows = np.array([0, M - 1], np.int64)
+    y = host16(X.linear(dev16(x), X.Layer.from_numpy(L, cb)))
+    H.assert_rows_close(y[rows], O.exl3_linear(x, L, cb, rows))

@@ -244,11 +244,18 @@ static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, i
 
 // The 4-bit kernel is compiled for more tile counts; the other widths share
 // smaller instance sets. Both have 2 and 4 row groups per pass.
+// For M <= 16 the rotation in the prologue saves a launch, but it bounds the
+// workgroup's k range (the slice must fit DEC_XS_BYTES), which forces a
+// k-split and its partial traffic on wide layers; the plan with a separate
+// rotation pass competes with a penalty for that pass (a launch plus M x K
+// fp16 read and written, in the model's units).
 DecodePlan plan_decode(int32_t K, int32_t N, int64_t M, bool four_bits) {
   DecodePlan p{1, 1, K / 32, 1, 1, 16, four_bits ? 1 : 2, 0, 1};
   double cost = 1e300;
-  if (M <= 16 && plan_decode_search(K, N, M, true, 1, four_bits, p, cost)) return p;
-  cost = 1e300;
+  if (M <= 16 && plan_decode_search(K, N, M, true, 1, four_bits, p, cost))
+    cost -= 6000.0 + (double)M * K * 4.0 / 2083.0;
+  else
+    cost = 1e300;
   for (int G : {1, 2, 4})
     if (G == 1 || 16 * (G / 2) < M) plan_decode_search(K, N, M, false, G, four_bits, p, cost);
   return p;
