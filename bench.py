@@ -508,6 +508,30 @@ def sweep(bits: int = 4) -> str:
         del layers
         torch.cuda.empty_cache()
     lines = ["\n".join(out), ""]
+    if bits == 4:
+        # context: the vendor library's fp16 GEMM alone (torch.matmul, fp32
+        # accumulation) at the same shapes, with W^T as the N x K operand the
+        # prefill GEMM reads; no rotations, no reconstruct
+        lines.append("| library GEMM alone (torch.matmul fp16) | M | µs | TFLOP/s |")
+        lines.append("|---|---|---|---|")
+        for Kg, Ng in geoms:
+            wt = (0.05 * torch.randn(Ng, Kg, device=dev)).half()
+            for M in (2048, 4096):
+                xa = (0.05 * torch.randn(M, Kg, device=dev)).half()
+                for _ in range(3):
+                    xa @ wt.t()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    xa @ wt.t()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / 10 * 1e3
+                lines.append("| K%d×N%d | %d | %.1f | %.1f |" % (Kg, Ng, M, us, 2 * M * Kg * Ng / us / 1e6))
+                del xa
+            del wt
+        lines.append("")
     for (Kg, Ng), M in cross.items():
         lines.append("Crossover K%d×N%d, %d bits: prefill is faster from M = %d on (among the M measured)." % (
             Kg, Ng, bits, M))

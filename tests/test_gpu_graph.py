@@ -110,3 +110,33 @@ def test_logits_graph_replay_bit_identical(T):
         return [_lib.to_device_u16((0.05 * r.standard_normal((M, K))).astype(np.float16).view(np.uint16))]
 
     _replays_match_eager(torch, call, [x], [lg, am], fresh, lambda: torch.cuda.synchronize())
+
+
+@pytest.mark.parametrize("M,pm", [(1, 128), (16, 128), (256, 128)])
+def test_head_graph_replay_bit_identical(T, M, pm):
+    import torch
+
+    import trellis_quantized_linear_had_amd as X
+    from trellis_quantized_linear_had_amd import _lib
+
+    H.announce("graph capture exl3_head_logits_argmax K512 N2048 n_valid 1500 M=%d" % M)
+    K, N, n_valid = 512, 2048, 1500
+    cb = WL.codebook()
+    layer = X.Layer.from_numpy(WL.layer(32, K, N, 0, 6), cb)
+    x = _lib.to_device_u16(WL.activations(32, M, K))
+    n_pad = X.logits_padded_width(n_valid, N)
+    lg = torch.empty((M, n_pad), dtype=torch.int16, device="cuda")
+    am = torch.empty(M, dtype=torch.int64, device="cuda")
+    scratch = torch.empty(X.head_scratch_bytes(K, N, M, n_valid, pm), dtype=torch.uint8, device="cuda")
+    y2 = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    s2 = torch.empty(X.linear_scratch_bytes(K, N, M, pm), dtype=torch.uint8, device="cuda")
+    L = _lib.lib()
+
+    def call():
+        return L.exl3_head_logits_argmax(layer.c, x.data_ptr(), M, n_valid, lg.data_ptr(), n_pad, am.data_ptr(),
+                                         scratch.data_ptr(), scratch.numel(), pm,
+                                         torch.cuda.current_stream().cuda_stream)
+
+    other = _linear_call(torch, L, layer, x, y2, s2, M, pm)
+    fresh = lambda rep: [_lib.to_device_u16(WL.activations(32, M, K, 200 + rep))]
+    _replays_match_eager(torch, call, [x], [lg, am], fresh, lambda: _lib.check(other()))

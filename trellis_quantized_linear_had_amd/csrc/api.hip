@@ -21,6 +21,8 @@
 #include "timer.h"
 
 namespace exl3 {
+hipError_t launch_had128_frag(const uint16_t* in, uint16_t* out, int64_t M, int32_t K, const uint16_t* sign_pre,
+                              hipStream_t stream);
 hipError_t launch_had128(const uint16_t* in, uint16_t* out, int64_t rows, int64_t cols, const uint16_t* sign_pre,
                          const uint16_t* sign_post, hipStream_t stream);
 hipError_t launch_reconstruct_nk(const uint32_t* codes, const uint16_t* cb, const uint16_t* scale, int32_t K,
@@ -274,7 +276,8 @@ PrefillLayout prefill_layout(int32_t K, int32_t N, int64_t M) {
   PrefillLayout l;
   l.chunk = std::min<int32_t>(N, EXL3_MAX_CHUNK_COLS);
   l.xr_off = 0;
-  l.w_off = align256((size_t)M * K * 2);
+  // the rotated input in the GEMM's fragment order: rows padded to 32
+  l.w_off = align256((size_t)((M + 31) / 32 * 32) * K * 2);
   l.part_off = l.w_off + align256((size_t)l.chunk * K * 2);
   // fp32 k-piece tiles of the GEMM's last round, for the widest slice and the
   // trailing one (the only two widths the slice loop uses)
@@ -354,7 +357,7 @@ int linear_cols(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
     const PrefillLayout l = prefill_layout(K, ncols, M);
     uint16_t* xr = (uint16_t*)(sb + l.xr_off);
     uint16_t* wt = (uint16_t*)(sb + l.w_off);
-    EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
+    EXL3_TRY(launch_had128_frag(x, xr, M, K, L->sign_k, stream), "input rotation");
     for (int32_t n0 = 0; n0 < ncols; n0 += l.chunk) {
       const int32_t nc = std::min(l.chunk, ncols - n0);
       timer_begin(kTimerReconstruct, stream);

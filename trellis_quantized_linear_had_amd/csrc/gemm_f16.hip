@@ -11,17 +11,23 @@
 // registers: six of its seven butterfly stages run in registers and one
 // crosses lanes 32 apart.
 //
-// Tiling: 256 (p) x 256 (q) per workgroup, 64-wide k steps. Operands go from
-// global memory straight into LDS (global_load_lds_dwordx4, no register
-// staging), two stages, one barrier per k step. Inside a stage each 128-byte
-// row is cut in 16-byte chunks XOR-swizzled by ((row >> 1) & 7): the LDS
-// serves a 16-byte read 16 lanes at a time over 64 banks, and this key makes
-// every group of 16 consecutive rows hit 16 distinct bank groups (measured:
-// zero bank-conflict cycles). The swizzle is applied on the global side,
-// because a direct-to-LDS load writes lane i's 16 bytes at base + 16 i. 8
-// waves form 2 (p) x 4 (q); each owns 128 p-rows (one rotation block, 4
+// Tiling: 256 (p) x 256 (q) per workgroup, 64-wide k steps. 8 waves form
+// 2 (p) x 4 (q); each owns 128 p-rows (one rotation block, 4
 // v_mfma_f32_32x32x16_f16 row tiles) and 2 32-wide q tiles; two waves per
-// SIMD.
+// SIMD. A (W^T, shared by the 4 waves of a p half) goes from global memory
+// straight into LDS (global_load_lds_dwordx4, no register staging), two
+// stages, one barrier per k step. Inside a stage each 128-byte row is cut in
+// 16-byte chunks XOR-swizzled by ((row >> 1) & 7): the LDS serves a 16-byte
+// read 16 lanes at a time over 64 banks, and this key makes every group of 16
+// consecutive rows hit 16 distinct bank groups (zero bank-conflict cycles).
+// The swizzle is applied on the global side, because a direct-to-LDS load
+// writes lane i's 16 bytes at base + 16 i. B (the rotated x, shared by only
+// the 2 waves of a q quarter) does not pass through the LDS: the input
+// rotation stores it in MFMA fragment order (had128_frag_kernel: 32 rows x 16 k
+// per 1 KiB block, lane l holding row l % 32, k 8 (l / 32) .. + 8), so each
+// wave loads its B fragments straight into registers, one contiguous 1 KiB per
+// load instruction, one k step ahead. With both operands in LDS its reads and
+// writes matched the MFMA time per k step; without B they take 5/8 of it.
 //
 // Tail balance: tiles are dealt to the 256 CUs in rounds. The largest
 // multiple of 256 tiles runs whole; the k-steps of the remaining tiles are
@@ -46,8 +52,8 @@ namespace exl3 {
 #define G_WQ 4
 #define G_QT 2
 #define G_THREADS 512
-#define G_STAGE ((G_BP + G_BQ) * G_BK)  // halves per stage
-#define G_LPS 8                         // load instructions per wave per stage
+#define G_STAGE (G_BP * G_BK)  // halves per stage (A only)
+#define G_FRAG 512             // halves per 32 x 16 B fragment block (1 KiB)
 #define G_CUS 256
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -77,6 +83,21 @@ __device__ __forceinline__ void load_rows_lds(const uint16_t* __restrict__ g, in
   for (int i = 0; i < 4; ++i)
     __builtin_amdgcn_global_load_lds((const void*)(base + off[i]), (lds_void*)(lds_stage + (wave_row0 + 8 * i) * G_BK),
                                      16, 0, 0);
+}
+
+// One B fragment (16 bytes per lane) straight into registers. The load is
+// issued through inline assembly so that the compiler does not track it: its
+// waits cannot count register loads and the direct-to-LDS loads of A in one
+// sequence and would fall back to waiting for all of them (vmcnt(0)) at the
+// top of every k step. The kernel waits for these loads itself, and every
+// wait also guards the registers: the compiler takes the destination as
+// written at issue, so a slot's previous load must have landed before the
+// slot is read or its registers are reused (for the refill's address), and
+// all of them before the registers outlive the k loop.
+__device__ __forceinline__ f16x8 load_frag(const uint16_t* p) {
+  f16x8 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
 }
 
 // Output rotation + signs + fp16 store of one 128 (p) x 32 (q) block of a
@@ -194,49 +215,51 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
   const int lrow = lane & 31, lhalf = lane >> 5;
 
   f32x16 acc[4][G_QT];
-  // fragments of one k16 sub-step: 4 A tiles and 2 B tiles, two register sets
-  f16x8 af[2][4], bf[2][G_QT];
+  // A fragments of one k16 sub-step, two register sets; B fragments of the 4
+  // sub-steps of one k step: slot s is refilled with the next k step's
+  // sub-step s as soon as this k step's MFMAs of sub-step s are issued
+  f16x8 af[2][4], bq[4][G_QT];
   auto read_frags = [&](int stage, int s, int buf) {
     const uint16_t* As = smem + stage * G_STAGE;
-    const uint16_t* Bs = As + G_BP * G_BK;
     const int ch = 2 * s + lhalf;
-    // B first: the first MFMAs of a sub-step use both B tiles and A tile 0
-#pragma unroll
-    for (int j = 0; j < G_QT; ++j)
-      bf[buf][j] = *reinterpret_cast<const f16x8*>(&Bs[swz(32 * G_QT * wq + 32 * j + lrow, ch)]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) af[buf][i] = *reinterpret_cast<const f16x8*>(&As[swz(128 * wp + 32 * i + lrow, ch)]);
   };
-  auto mfmas = [&](int buf) {
+  auto mfmas = [&](int buf, int s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < G_QT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[buf][i], bf[buf][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[buf][i], bq[s][j], acc[i][j], 0, 0, 0);
   };
-  // Pins the order inside one sub-step: the 6 fragment reads of the next
-  // sub-step are all issued in its first half (read, MFMA three times, then
-  // three reads), so they land under the remaining five MFMAs instead of
-  // after them.
+  // Pins the order inside one sub-step: the 4 A-fragment reads of the next
+  // sub-step and the 2 B-fragment loads of the next k step go out between
+  // the first MFMAs, so they land under the remaining ones.
   auto interleave = [&]() {
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
+    for (int k = 0; k < 4; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
+#pragma unroll
+    for (int k = 0; k < G_QT; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8 - 4 - G_QT, 0);
   };
 
   // acc = sum over k-steps [kb0, kb1) of one tile. Schedule per k step kb
   // (stage buffer b = (kb - kb0) & 1):
-  //   sub-steps 0..2: read the next sub-step's fragments, then MFMAs;
-  //   sub-step 3: its fragments are in registers; wait for this wave's loads of
-  //   stage kb+1, barrier (every wave is done reading buffer b and stage kb+1
-  //   has landed), issue the loads of stage kb+2 into buffer b, read sub-step 0
-  //   of stage kb+1, and only then run sub-step 3's MFMAs, which cover the
-  //   barrier and the fragment-read latency.
-  // Ends with a barrier, so the stage buffers may be refilled at once.
+  //   sub-steps 0..2: read the next sub-step's A fragments, MFMAs, then load
+  //   B(kb + 1, s) into slot s;
+  //   sub-step 3: its A fragments are in registers; wait for this wave's A
+  //   loads of stage kb+1, barrier (every wave is done reading buffer b and
+  //   stage kb+1 has landed), issue the A loads of stage kb+2 into buffer b,
+  //   read sub-step 0 of stage kb+1, and only then run sub-step 3's MFMAs,
+  //   which cover the barrier and the fragment-read latency.
+  // B loads past the range re-read the last k step (never used). Ends with a
+  // barrier, so the stage buffers may be refilled at once.
   auto run_tile = [&](int p_base, int q_base, int kb0, int kb1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -244,45 +267,73 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
       for (int j = 0; j < G_QT; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    uint32_t offa[4], offb[4];
+    uint32_t offa[4];
     lane_offsets(K, p_base, P, 32 * wave, lane, offa);
-    lane_offsets(K, q_base, Q, 32 * wave, lane, offb);
-    auto issue_loads = [&](int stage, int k0) {
-      uint16_t* st = smem + stage * G_STAGE;
-      load_rows_lds(A, k0, offa, st, 32 * wave);
-      load_rows_lds(B, k0, offb, st + G_BP * G_BK, 32 * wave);
+    // this wave's B blocks: q rows q_base + 64 wq + 32 j (clamped to the last
+    // block; rows past Q are never stored)
+    const int nqb = (Q + 31) / 32, ksub = K / 16;
+    const uint16_t* bsrc[G_QT];
+#pragma unroll
+    for (int j = 0; j < G_QT; ++j) {
+      const int qb = min((q_base + 32 * G_QT * wq + 32 * j) / 32, nqb - 1);
+      bsrc[j] = B + ((int64_t)qb * ksub * 64 + lane) * 8;
+    }
+    auto load_b = [&](int kb, int sub) {
+#pragma unroll
+      for (int j = 0; j < G_QT; ++j)
+        bq[sub][j] = load_frag(bsrc[j] + (int64_t)(4 * kb + sub) * G_FRAG);
     };
+    auto issue_loads = [&](int stage, int k0) { load_rows_lds(A, k0, offa, smem + stage * G_STAGE, 32 * wave); };
     const int nk = kb1 - kb0;
     if (nk <= 0) return;
     issue_loads(0, kb0 * G_BK);
     if (nk > 1) issue_loads(1, (kb0 + 1) * G_BK);
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) load_b(kb0, sub);
+    // stage 0 landed (the 4 loads of stage 1, if any, and the 8 B loads may not have)
     if (nk > 1)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G_LPS) : "memory");  // stage 0 landed, stage 1 may not have
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     __syncthreads();
     read_frags(0, 0, 0);
     for (int kk = 0; kk < nk; ++kk) {
       const int b = kk & 1;
+      const int kn = kb0 + min(kk + 1, nk - 1);  // the k step the B slots are refilled with
+      // B slot s of this k step has landed once at most 6 loads are
+      // outstanding: at least 6 B loads (and possibly 4 A loads) were issued
+      // after it, in every iteration
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
       read_frags(b, 1, 1);
-      mfmas(0);
+      mfmas(0, 0);
+      load_b(kn, 0);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
       read_frags(b, 2, 0);
-      mfmas(1);
+      mfmas(1, 1);
+      load_b(kn, 1);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
       read_frags(b, 3, 1);
-      mfmas(0);
+      mfmas(0, 2);
+      load_b(kn, 2);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // at most the 6 B loads just issued outstanding: this wave's A loads of
+      // stage kk+1 and slot 3 (both issued before them) have landed
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
       __syncthreads();
       if (kk + 2 < nk) issue_loads(b, (kb0 + kk + 2) * G_BK);
       if (kk + 1 < nk) read_frags(b ^ 1, 0, 0);
-      mfmas(1);
+      mfmas(1, 3);
+      load_b(kn, 3);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // the last B loads (of the last k step again) must land before their
+    // registers are reused: the compiler does not know they are in flight
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
   if (MODE == 0) {

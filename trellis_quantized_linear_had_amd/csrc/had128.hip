@@ -42,6 +42,57 @@ __global__ __launch_bounds__(256) void had128_kernel(const uint16_t* in, uint16_
   if (blk_raw < nblocks) *reinterpret_cast<u32x4*>(out + blk * 128 + 8 * q) = o;
 }
 
+// The prefill GEMM's B operand: the same rotation of x (M x K), stored in
+// MFMA fragment order for Mpad = ceil(M / 32) * 32 rows, rows past M zero.
+// Block (qb, t) of 32 rows x 16 k is 1 KiB at halves (qb * K/16 + t) * 512;
+// lane l = row % 32 + 32 * ((k % 16) / 8) of it holds k .. k + 7 of its row.
+// Items (128-column block b, row) run row-fastest, so the four 16-lane groups
+// of a wave are four consecutive rows of one block and every store
+// instruction writes 64 contiguous bytes per fragment position.
+template <bool PRE>
+__global__ __launch_bounds__(256) void had128_frag_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                          int32_t M, int32_t Mpad, int32_t K,
+                                                          const uint16_t* __restrict__ sign_pre) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q = (int)(gid & 15);
+  const int64_t nitems = (int64_t)Mpad * (K / 128);
+  const int64_t item_raw = gid >> 4;
+  // groups past the end compute a valid item and do not store
+  const int64_t item = item_raw < nitems ? item_raw : nitems - 1;
+  const int row = (int)(item % Mpad), b = (int)(item / Mpad);
+  const int64_t col0 = (int64_t)b * 128 + 8 * q;
+  // rows past M read row M - 1 and store zeros
+  u32x4 d = *reinterpret_cast<const u32x4*>(in + (int64_t)min(row, M - 1) * K + col0);
+  if (PRE) d ^= (*reinterpret_cast<const u32x4*>(sign_pre + col0) & 0x80008000u);
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = bits_lo_f16(d[j]);
+    v[2 * j + 1] = bits_hi_f16(d[j]);
+  }
+  wht128_16(v, q);
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * EXL3_INV_SQRT128, v[2 * j + 1] * EXL3_INV_SQRT128);
+  if (row >= M) o = (u32x4){0u, 0u, 0u, 0u};
+  const int64_t t = col0 / 16;
+  const int lf = row % 32 + 32 * (q & 1);
+  if (item_raw < nitems) *reinterpret_cast<u32x4*>(out + (((int64_t)(row / 32) * (K / 16) + t) * 64 + lf) * 8) = o;
+}
+
+hipError_t launch_had128_frag(const uint16_t* in, uint16_t* out, int64_t M, int32_t K, const uint16_t* sign_pre,
+                              hipStream_t stream) {
+  const int64_t Mpad = (M + 31) / 32 * 32;
+  const int64_t threads = Mpad * (K / 128) * 16;
+  if (threads == 0) return hipSuccess;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (sign_pre)
+    had128_frag_kernel<true><<<grid, 256, 0, stream>>>(in, out, (int32_t)M, (int32_t)Mpad, K, sign_pre);
+  else
+    had128_frag_kernel<false><<<grid, 256, 0, stream>>>(in, out, (int32_t)M, (int32_t)Mpad, K, sign_pre);
+  return hipGetLastError();
+}
+
 hipError_t launch_had128(const uint16_t* in, uint16_t* out, int64_t rows, int64_t cols, const uint16_t* sign_pre,
                          const uint16_t* sign_post, hipStream_t stream) {
   const int64_t nblocks = rows * (cols / 128);
