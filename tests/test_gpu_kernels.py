@@ -163,6 +163,27 @@ def test_linear_deterministic(T, X, cb):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("K,N,M", [(5120, 17408, 2048), (2560, 3328, 200)])
+def test_prefill_gemm_repeatable(T, X, cb, K, N, M):
+    """Back-to-back prefill calls (full tiles plus stream-K pieces at the
+    first shape, pieces straddling tiles at the second) give the same bits
+    every time: the GEMM's operand loads and their waits leave no call
+    reading a stage or fragment before it has landed."""
+    H.announce("prefill repeatable K%d N%d M%d" % (K, N, M))
+    import torch
+
+    L = WL.layer(26, K, N)
+    lay = X.Layer.from_numpy(L, cb)
+    x = dev16(WL.activations(26, M, K))
+    scr = torch.empty(X.linear_scratch_bytes(K, N, M), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((M, N), dtype=torch.int16, device="cuda") for _ in range(8)]
+    for o in outs:
+        X.linear(x, lay, scratch=scr, out=o)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
 def test_linear_two_slices(T, X, cb):
     H.announce("linear two 32768-column slices K128 N33024 M130")
     K, N, M = 128, 33024, 130

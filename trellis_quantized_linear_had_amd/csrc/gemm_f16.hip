@@ -93,7 +93,9 @@ __device__ __forceinline__ void load_rows_lds(const uint16_t* __restrict__ g, in
 // wait also guards the registers: the compiler takes the destination as
 // written at issue, so a slot's previous load must have landed before the
 // slot is read or its registers are reused (for the refill's address), and
-// all of them before the registers outlive the k loop.
+// all of them before the registers outlive the k loop. The counts rely on
+// vector memory loads returning in issue order, direct-to-LDS loads
+// included.
 __device__ __forceinline__ f16x8 load_frag(const uint16_t* p) {
   f16x8 v;
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
