@@ -335,7 +335,7 @@ CSRC = os.path.join(ROOT, "trellis_quantized_linear_had_amd", "csrc")
 PMC_KERNELS = {
     "logits": ("exl3::logits_kernel", "logits_kernel M=16", ("logits.hip", "common.h")),
     "gemm": ("exl3::gemm_had_kernel<0>", "gemm_had_kernel<0> M=2048", ("gemm_f16.hip", "common.h")),
-    "decode": ("exl3::decode_gemm_kernel<6, true>", "decode_gemm_kernel M=16",
+    "decode": ("exl3::decode_gemm_kernel<6, true, 1, 4>", "decode_gemm_kernel M=16",
                ("decode_gemm.hip", "decode_plan.h", "trellis.h", "common.h")),
     "reconstruct": ("exl3::reconstruct_nk_kernel", "reconstruct_nk_kernel K5120xN17408",
                     ("reconstruct.hip", "trellis.h", "common.h")),
