@@ -337,7 +337,7 @@ PMC_KERNELS = {
     "gemm": ("exl3::gemm_had_kernel<0>", "gemm_had_kernel<0> M=2048", ("gemm_f16.hip", "common.h")),
     "decode": ("exl3::decode_gemm_kernel<6, true, 1, 4>", "decode_gemm_kernel M=16",
                ("decode_gemm.hip", "decode_plan.h", "trellis.h", "common.h")),
-    "reconstruct": ("exl3::reconstruct_nk_kernel", "reconstruct_nk_kernel K5120xN17408",
+    "reconstruct": ("exl3::reconstruct_nk_kernel<4>", "reconstruct_nk_kernel K5120xN17408",
                     ("reconstruct.hip", "trellis.h", "common.h")),
 }
 

@@ -129,3 +129,15 @@ def test_linear_wide_layer_small_m(T, X, cb, bits, M):
     rows = np.array([0, M - 1], np.int64)
     y = host16(X.linear(dev16(x), X.Layer.from_numpy(L, cb)))
     H.assert_rows_close(y[rows], O.exl3_linear(x, L, cb, rows))
+
+
+@pytest.mark.parametrize("bits,M", [(6, 1), (6, 4), (6, 16), (3, 4)])
+def test_linear_four_tile_waves(T, X, cb, bits, M):
+    """K512 x N12800: the planner gives each wave four n-tiles at these
+    widths (the prologue rotation included); every row against the oracle."""
+    H.announce("linear bits=%d K512 N12800 M=%d" % (bits, M))
+    K, N = 512, 12800
+    L = WL.layer(38, K, N, 0, bits)
+    x = WL.activations(38, M, K)
+    y = host16(X.linear(dev16(x), X.Layer.from_numpy(L, cb)))
+    H.assert_rows_close(y, O.exl3_linear(x, L, cb))

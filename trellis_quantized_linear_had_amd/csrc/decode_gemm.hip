@@ -420,6 +420,7 @@ hipError_t launch_decode_gemm(const uint16_t* xin, const uint16_t* sign_k, const
       switch (plan.nt_wave) {                                           \
         EXL3_DEC_CASE1(2, b)                                            \
         EXL3_DEC_CASE1(3, b)                                            \
+        EXL3_DEC_CASE1(4, b)                                            \
         EXL3_DEC_CASE1(5, b)                                            \
         EXL3_DEC_CASE1(6, b)                                            \
         default:                                                        \

@@ -36,7 +36,7 @@ static const int32_t kDecodeNtInstancesG2[] = {1, 2, 3, 4, 5};
 static const int32_t kDecodeNtInstancesG4[] = {1, 2, 3};
 // ... and at widths other than 4 bits (up to three code words per tile and
 // lane): one, two or four row groups per pass
-static const int32_t kDecodeNtInstancesOther[] = {2, 3, 5, 6};
+static const int32_t kDecodeNtInstancesOther[] = {2, 3, 4, 5, 6};
 static const int32_t kDecodeNtInstancesOtherG2[] = {2, 3, 4, 5};
 static const int32_t kDecodeNtInstancesOtherG4[] = {1, 2};
 
