@@ -333,8 +333,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
 // Output stage: y[m][128b + i] = fp16(s_N * (1/sqrt128) * sum_j H[i][j] *
 // scale[n_j] * sum_ks partials[ks][m][n_j]); 16 lanes per (row, 128-column
 // block), 8 columns per lane. The partials are summed in ks order; the loads
-// of up to 8 slices are issued before their sums so one memory round trip
-// serves them.
+// of the column scales and signs and of up to 8 slices are all issued before
+// any of them is used, so one memory round trip serves them.
 __global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __restrict__ partials, int32_t ks_count,
                                                               const uint16_t* __restrict__ scale,
                                                               const uint16_t* __restrict__ sign_n,
@@ -348,18 +348,17 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __res
   const int64_t m = blk / (N / 128);
   const int64_t n0 = (blk % (N / 128)) * 128 + 8 * q;
   const int64_t slice = (int64_t)M * N;
+  const u32x4 sc = *reinterpret_cast<const u32x4*>(scale + n0);
+  // without signs the scales are read again and masked to zero (no branch
+  // between the loads and their use)
+  const u32x4 sg = *reinterpret_cast<const u32x4*>((sign_n ? sign_n : scale) + n0);
+  const uint32_t smask = sign_n ? 0x80008000u : 0u;
 
   float v[8];
   const f32x4* src = reinterpret_cast<const f32x4*>(partials + m * N + n0);
-  {
-    const f32x4 p0 = src[0], p1 = src[1];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[j] = p0[j];
-      v[4 + j] = p1[j];
-    }
-  }
-  for (int k0 = 1; k0 < ks_count; k0 += 8) {
+  // slices 0 .. 7 in one batch (slice 0 assigned, the rest added in order),
+  // then further batches of 8
+  auto batch = [&](int k0) {
     f32x4 p[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -369,7 +368,13 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __res
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (k0 + i < ks_count) {
+      if (k0 + i == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] = p[i][0][j];
+          v[4 + j] = p[i][1][j];
+        }
+      } else if (k0 + i < ks_count) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           v[j] += p[i][0][j];
@@ -377,8 +382,9 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __res
         }
       }
     }
-  }
-  const u32x4 sc = *reinterpret_cast<const u32x4*>(scale + n0);
+  };
+  batch(0);
+  for (int k0 = 8; k0 < ks_count; k0 += 8) batch(k0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     v[2 * j] *= bits_lo_f16(sc[j]);
@@ -388,7 +394,7 @@ __global__ __launch_bounds__(256) void decode_finalize_kernel(const float* __res
   u32x4 o;
 #pragma unroll
   for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * EXL3_INV_SQRT128, v[2 * j + 1] * EXL3_INV_SQRT128);
-  if (sign_n) o ^= (*reinterpret_cast<const u32x4*>(sign_n + n0) & 0x80008000u);
+  o ^= sg & smask;
   if (blk_raw < nblocks) *reinterpret_cast<u32x4*>(y + m * ldy + n0) = o;
 }
 
