@@ -111,6 +111,18 @@ __device__ __forceinline__ void rotate_store_block(f32x16 (&a)[4], int lane, int
                                                    uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
                                                    const uint16_t* __restrict__ sign_n) {
   const int lrow = lane & 31, lhalf = lane >> 5;
+  // The 16 sign words go out before the butterflies and are used after them:
+  // one memory round trip, under the arithmetic, and no wait between the
+  // stores. Without signs, row 0 of y (in bounds, then masked off) is read.
+  u32x2 sg[4][4];
+  const uint32_t smask = sign_n ? 0x80008000u : 0u;
+  if (pw < P) {  // uniform over the wave
+    const uint16_t* sp = (sign_n ? sign_n : y) + n0 + pw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) sg[i][g] = *reinterpret_cast<const u32x2*>(sp + 32 * i + 8 * g + 4 * lhalf);
+  }
 #pragma unroll
   for (int h = 1; h <= 8; h <<= 1) {  // register bits r&1, r&2, r&4, r&8
 #pragma unroll
@@ -155,7 +167,7 @@ __device__ __forceinline__ void rotate_store_block(f32x16 (&a)[4], int lane, int
       u32x2 o;
       o[0] = pack_f16x2(a[i][4 * g] * EXL3_INV_SQRT128, a[i][4 * g + 1] * EXL3_INV_SQRT128);
       o[1] = pack_f16x2(a[i][4 * g + 2] * EXL3_INV_SQRT128, a[i][4 * g + 3] * EXL3_INV_SQRT128);
-      if (sign_n) o ^= (*reinterpret_cast<const u32x2*>(sign_n + n0 + pw + p) & 0x80008000u);
+      o ^= sg[i][g] & smask;
       *reinterpret_cast<u32x2*>(yrow + p) = o;
     }
 }
