@@ -300,46 +300,49 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
     auto issue_loads = [&](int stage, int k0) { load_rows_lds(A, k0, offa, smem + stage * G_STAGE, 32 * wave); };
     const int nk = kb1 - kb0;
     if (nk <= 0) return;
+    // Every k step issues the same loads in the same order, so the waits are
+    // fixed counts: A loads of a stage past the range re-load the last k step
+    // into a buffer no later k step reads. The prologue issues its loads in
+    // the steady state's order: B slots 0..2, A stage 1, B slot 3.
     issue_loads(0, kb0 * G_BK);
-    if (nk > 1) issue_loads(1, (kb0 + 1) * G_BK);
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) load_b(kb0, sub);
-    // stage 0 landed (the 4 loads of stage 1, if any, and the 8 B loads may not have)
-    if (nk > 1)
-      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    for (int sub = 0; sub < 3; ++sub) load_b(kb0, sub);
+    issue_loads(1, (kb0 + min(1, nk - 1)) * G_BK);
+    load_b(kb0, 3);
+    // stage 0 landed (the 12 loads after it may not have)
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     __syncthreads();
     read_frags(0, 0, 0);
     for (int kk = 0; kk < nk; ++kk) {
       const int b = kk & 1;
       const int kn = kb0 + min(kk + 1, nk - 1);  // the k step the B slots are refilled with
-      // B slot s of this k step has landed once at most 6 loads are
-      // outstanding: at least 6 B loads (and possibly 4 A loads) were issued
-      // after it, in every iteration
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      // Slot s of this k step has landed once at most 10 loads are
+      // outstanding: issued after it are the later slots, the 4 A loads of
+      // stage kk+1 and this k step's refills, 10 in all, for s = 0, 1, 2; the
+      // A loads themselves get the whole k step to land.
+      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
       read_frags(b, 1, 1);
       mfmas(0, 0);
       load_b(kn, 0);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
       read_frags(b, 2, 0);
       mfmas(1, 1);
       load_b(kn, 1);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
       read_frags(b, 3, 1);
       mfmas(0, 2);
       load_b(kn, 2);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
-      // at most the 6 B loads just issued outstanding: this wave's A loads of
-      // stage kk+1 and slot 3 (both issued before them) have landed
+      // at most the 6 B loads just issued outstanding: slot 3 and this
+      // wave's A loads of stage kk+1 (issued before it) have landed
       asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
       __syncthreads();
-      if (kk + 2 < nk) issue_loads(b, (kb0 + kk + 2) * G_BK);
+      issue_loads(b, (kb0 + min(kk + 2, nk - 1)) * G_BK);
       if (kk + 1 < nk) read_frags(b ^ 1, 0, 0);
       mfmas(1, 3);
       load_b(kn, 3);
