@@ -61,7 +61,7 @@ def require_gpu():
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    # On a GPU machine the native library must be there: import failures are errors.
+    # Where a GPU is present the native library must be there: import failures are errors.
     from trellis_quantized_linear_had_amd import _lib
 
     _lib.lib()
