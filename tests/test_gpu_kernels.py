@@ -329,3 +329,16 @@ def test_logits_aligned_width_mask_is_noop(T, X):
     assert not np.any(lg == 0xFC00)
     ref_lg, ref_am = O.logits(x, w, 384)
     assert np.array_equal(am, ref_am)
+
+
+@pytest.mark.parametrize("M,pm", [(1, 128), (16, 128), (130, 128)])
+def test_linear_largest_k(T, X, cb, M, pm):
+    """K = 65408, the largest K the library takes (an fp16 weight slice of
+    K x 32768 columns stays within 32-bit byte offsets), on both paths."""
+    H.announce("linear K65408 N256 M=%d pm=%d" % (M, pm))
+    K, N = 65408, 256
+    L = WL.layer(27, K, N)
+    x = WL.activations(27, M, K)
+    y = run_linear(X, L, cb, x, pm)
+    rows = np.unique(np.array([0, M // 2, M - 1], np.int64))
+    H.assert_rows_close(y[rows], O.exl3_linear(x, L, cb, rows))
