@@ -13,7 +13,8 @@
  *   [P314] vLLM PR #314, "[EXL3] allow CUDA-graph decode for dense
  *          checkpoints by priming exl3_gemm autotune": section "Problem"
  *          (a lazily allocated buffer on first call breaks graph capture;
- *          fail closed and name the failing condition).
+ *          fail closed and name the failing condition), "Verification" (the
+ *          checkpoint's lm_head is itself a trellis-quantized matrix).
  *   [P1046] pegainfer PR #1046, "perf(qwen35): align the logits GEMM width":
  *          Summary (round the decodable width up to a multiple of 128, clamp
  *          by the weight rows), the review follow-ups (pad columns forced to
@@ -58,9 +59,9 @@
  *         Xr = had(X * sign_k),  Yr = Xr . W,  Y = had(Yr) * sign_n,
  *     i.e. the pages' y = had_r_128(W . had_r_128(x)) with their W equal to
  *     the transpose of this W, plus random +-1 signs on both rotations.
- *   - Every width 1..8 uses the same 65536-entry codebook. The fused path is
- *     compiled for more tile shapes and for 2 or 4 row groups per pass at
- *     4 bits; the other widths take one row group per pass.
+ *   - Every width 1..8 uses the same 65536-entry codebook. The fused path
+ *     shares each decoded tile between 1, 2 or 4 groups of 16 rows per pass
+ *     at every width; 4 bits is compiled for more tile counts per wave.
  */
 #ifndef EXL3_H
 #define EXL3_H
