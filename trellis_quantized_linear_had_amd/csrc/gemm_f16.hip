@@ -205,12 +205,29 @@ __device__ __forceinline__ void store_partial(const f32x16 (&acc)[4][G_QT], f32x
 // multiples of sdiv = units / gcd(nk, units): slot = v + t - t / sdiv.
 __device__ __forceinline__ int partial_slot(int v, int t, int sdiv) { return v + t - t / sdiv; }
 
+// Tail tile t -> tile index. Pieces v and v + nk / gcd(nk, units) sit at the
+// same k offsets of tiles t and t + sdiv, so with grp = sdiv (the tail whole
+// p-strips, a whole number of sdiv-strip groups) the order
+// t = grp (sg tiles_q + q) + i  <->  (strip p0 + grp sg + i, column block q)
+// gives the pieces in one phase tiles that share a W^T strip (same sg, i) or
+// an x~ block (same q) at the same k step, read once through their XCD's L2.
+// grp = 0: the tiles in plain order (with one column block they still share
+// x~).
+__device__ __forceinline__ int tail_tile(int t, int tile_base, int tiles_q, int grp) {
+  if (grp == 0) return tile_base + t;
+  const int i = t % grp, r = t / grp, q = r % tiles_q, sg = r / tiles_q;
+  return (tile_base / tiles_q + grp * sg + i) * tiles_q + q;
+}
+
 // MODE 0: workgroup w computes tile tile_base + t (t in XCD order, t < count)
 // over all of K and runs the rotation epilogue. MODE 1 (stream-K tail): the
 // count tiles' k-steps, tile-major, are dealt in runs of `units` to the
-// workgroups; piece v (the workgroup's place in XCD order) covers
-// [v units, (v + 1) units), at most two tiles (units <= K / G_BK), and
-// writes one partial per tile it touches (slot partial_slot(v, tile)).
+// workgroups; piece v covers [v units, (v + 1) units), at most two tiles
+// (units <= K / G_BK), and writes one partial per tile it touches (slot
+// partial_slot(v, tile)). Piece v is workgroup v: workgroups are dealt
+// round-robin over the 8 XCDs, so pieces v and v + 8 j share an XCD, and
+// with a phase period nk / gcd(nk, units) that is a multiple of 8 the pieces
+// in one phase (the same k offsets at every step) all run on one XCD.
 template <int MODE>
 __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __restrict__ A,
                                                              const uint16_t* __restrict__ B,
@@ -218,7 +235,7 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
                                                              int32_t K, int64_t ldy, int32_t n0,
                                                              const uint16_t* __restrict__ sign_n, int32_t tile_base,
                                                              int32_t count, int32_t units, int32_t sdiv,
-                                                             f32x4* __restrict__ partial) {
+                                                             int32_t grp, f32x4* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * G_STAGE];
 
   const int tiles_q = (Q + G_BQ - 1) / G_BQ;
@@ -362,17 +379,15 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
     run_tile(p_base, q_base, 0, nk_all);
     rotate_store(acc, lane, p_base + 128 * wp, q_base + 32 * G_QT * wq, P, Q, y, ldy, n0, sign_n);
   } else {
-    // piece v = the workgroup's place in XCD order, as for whole tiles: each
-    // XCD walks a contiguous run of units
     const int total = count * nk_all;
     const int pieces = (total + units - 1) / units;
-    const int v = (int)(blockIdx.x % 8) * ((pieces + 7) / 8) + (int)(blockIdx.x / 8);
+    const int v = (int)blockIdx.x;
     if (v >= pieces) return;  // whole workgroup (uniform)
     int unit = v * units;
     const int end = min(unit + units, total);
     for (int seg = 0; seg < 2 && unit < end; ++seg) {
       const int t = unit / nk_all, kb0 = unit - t * nk_all, kb1 = min(nk_all, kb0 + (end - unit));
-      const int tile = tile_base + t;
+      const int tile = tail_tile(t, tile_base, tiles_q, grp);
       run_tile((tile / tiles_q) * G_BP, (tile % tiles_q) * G_BQ, kb0, kb1);
       store_partial(acc, partial + (int64_t)partial_slot(v, t, sdiv) * (G_BP * G_BQ / 4));
       unit += kb1 - kb0;
@@ -385,14 +400,14 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
 // tile, wave, 32-wide q block) spreads the partial reads over the CUs; the
 // loads of two pieces are in flight together.
 __global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict__ partial, int32_t units,
-                                                        int32_t sdiv, int32_t tile_base, int32_t P, int32_t Q,
-                                                        int32_t K,
+                                                        int32_t sdiv, int32_t grp, int32_t tile_base, int32_t P,
+                                                        int32_t Q, int32_t K,
                                                         uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
                                                         const uint16_t* __restrict__ sign_n) {
   const int per_tile = (G_THREADS / 64) * G_QT;
   const int item = blockIdx.x / per_tile, wave = (blockIdx.x % per_tile) / G_QT, j = blockIdx.x % G_QT;
   const int tiles_q = (Q + G_BQ - 1) / G_BQ;
-  const int tile = tile_base + item;
+  const int tile = tail_tile(item, tile_base, tiles_q, grp);
   const int p_base = (tile / tiles_q) * G_BP, q_base = (tile % tiles_q) * G_BQ;
   const int lane = threadIdx.x;
   const int tid = 64 * wave + lane;  // the thread of the k-piece workgroup this lane stands for
@@ -446,9 +461,10 @@ __global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict_
 // Round plan: `full` tiles (whole rounds of 256) run whole; the `rem` tiles
 // after them are spread stream-K style, `units` k-steps per workgroup over
 // `pieces` workgroups, when that beats one more whole round with idle CUs
-// (rem <= 224); otherwise they also run whole.
+// (rem <= 224); otherwise they also run whole. grp > 0 selects the grouped
+// tail order (tail_tile).
 struct GemmPlan {
-  int tiles, full, rem, units, pieces, sdiv, slots;
+  int tiles, full, rem, units, pieces, sdiv, slots, grp;
 };
 
 static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
@@ -460,6 +476,7 @@ static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
   g.pieces = 0;
   g.sdiv = 1;
   g.slots = 0;
+  g.grp = 0;
   const int nk = K / G_BK;
   if (g.rem > 0 && g.rem <= 224 && nk >= 2) {
     const int64_t total = (int64_t)g.rem * nk;
@@ -474,6 +491,8 @@ static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
     g.sdiv = g.units / a;
     const int t_last = g.rem - 1;
     g.slots = g.pieces + t_last - t_last / g.sdiv;  // one past the last slot
+    const int tiles_q = (Q + G_BQ - 1) / G_BQ;
+    if (g.full % tiles_q == 0 && g.rem % (tiles_q * g.sdiv) == 0) g.grp = g.sdiv;
   } else {
     g.full = g.tiles;
     g.rem = 0;
@@ -493,14 +512,14 @@ hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, in
   if (g.full > 0) {
     timer_begin(kTimerGemm, stream);
     gemm_had_kernel<0><<<8 * ((g.full + 7) / 8), G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, 0, g.full,
-                                                                         0, 1, part);
+                                                                         0, 1, 0, part);
     timer_end(kTimerGemm, stream);
   }
   if (g.rem > 0) {
     gemm_had_kernel<1><<<8 * ((g.pieces + 7) / 8), G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, g.full,
-                                                                           g.rem, g.units, g.sdiv, part);
-    gemm_fixup_kernel<<<g.rem * (G_THREADS / 64) * G_QT, 64, 0, stream>>>(part, g.units, g.sdiv, g.full, P, Q, K, y,
-                                                                          ldy, n0, sign_n);
+                                                                           g.rem, g.units, g.sdiv, g.grp, part);
+    gemm_fixup_kernel<<<g.rem * (G_THREADS / 64) * G_QT, 64, 0, stream>>>(part, g.units, g.sdiv, g.grp, g.full, P,
+                                                                          Q, K, y, ldy, n0, sign_n);
   }
   return hipGetLastError();
 }
