@@ -72,7 +72,7 @@ def parse():
                     help="instead of the bench line: time the trellis-quantized output head (the padded-logits "
                          "geometry, 4 and 6 bits per weight) at M = 1, 4, 16, 64 beside the dense fp16 logits "
                          "projection, and print a markdown summary")
-    ap.add_argument("--pmc-workload", choices=("logits", "gemm", "decode", "reconstruct"), default=None,
+    ap.add_argument("--pmc-workload", choices=("logits", "gemm", "decode", "reconstruct", "gemm_tail"), default=None,
                     help="run only a counter-collection workload: two 1 GiB device copies (calibration) then "
                          "three calls of the named path; prints nothing else")
     return ap.parse_args()
@@ -339,6 +339,8 @@ PMC_KERNELS = {
                ("decode_gemm.hip", "decode_plan.h", "trellis.h", "common.h")),
     "reconstruct": ("exl3::reconstruct_nk_kernel<4>", "reconstruct_nk_kernel K5120xN17408",
                     ("reconstruct.hip", "trellis.h", "common.h")),
+    # the down-projection geometry, where all 160 tiles run as stream-K pieces
+    "gemm_tail": ("exl3::gemm_had_kernel<1>", "gemm_had_kernel<1> K17408xN5120 M=2048", ("gemm_f16.hip", "common.h")),
 }
 
 
@@ -436,12 +438,13 @@ def pmc_workload(kind: str):
             _lib.check(lib.logits_pad_mask_argmax(xl.data_ptr(), LOGITS_M, K, wl.data_ptr(), w_rows, n_valid,
                                                   lg.data_ptr(), n_pad, am.data_ptr(), scr.data_ptr(), scr.numel(), sh))
     else:
-        pre = kind in ("gemm", "reconstruct")  # both run inside the prefill call
+        pre = kind in ("gemm", "reconstruct", "gemm_tail")  # these run inside the prefill call
         M = PREFILL_M if pre else max(DEC_M)
-        layer = X.Layer.from_numpy(W.layer(W.SEED_PREFILL if pre else W.SEED_DECODE, K, N, 0), cb)
-        x = _lib.to_device_u16(W.activations(W.SEED_PREFILL if pre else W.SEED_DECODE, M, K, 0))
-        y = torch.empty((M, N), dtype=torch.int16, device=dev)
-        scr = torch.empty(X.linear_scratch_bytes(K, N, M), dtype=torch.uint8, device=dev)
+        Kw, Nw = (N, K) if kind == "gemm_tail" else (K, N)
+        layer = X.Layer.from_numpy(W.layer(W.SEED_PREFILL if pre else W.SEED_DECODE, Kw, Nw, 0), cb)
+        x = _lib.to_device_u16(W.activations(W.SEED_PREFILL if pre else W.SEED_DECODE, M, Kw, 0))
+        y = torch.empty((M, Nw), dtype=torch.int16, device=dev)
+        scr = torch.empty(X.linear_scratch_bytes(Kw, Nw, M), dtype=torch.uint8, device=dev)
         for _ in range(3):
             _lib.check(lib.exl3_linear(layer.c, x.data_ptr(), M, y.data_ptr(), scr.data_ptr(), scr.numel(), 128, sh))
     torch.cuda.synchronize()
