@@ -198,6 +198,7 @@ def test_linear_two_slices(T, X, cb):
 @pytest.mark.parametrize("K,N,M", [
     (2560, 3328, 200),    # 13 tiles < 256 CUs: every tile in stream-K pieces of 3 k-steps over 40 (pieces straddle tiles)
     (1024, 4352, 4096),   # 272 tiles: one whole round + 16 tiles split along K
+    (1024, 4608, 300),    # 36 tiles in two column blocks, the last ragged: grouped tail order (3-strip groups)
 ])
 def test_linear_prefill_gemm_tail(T, X, cb, K, N, M):
     H.announce("linear prefill GEMM tail K%d N%d M%d" % (K, N, M))
