@@ -208,3 +208,25 @@ def test_kernel_timer_validation_without_gpu():
     assert L.exl3_kernel_timer_read(2, ctypes.byref(ms), ctypes.byref(n)) == X.EXL3_OK
     assert (ms.value, n.value) == (0.0, 0)
     assert L.exl3_kernel_timer_enable(0) == X.EXL3_OK
+
+
+def test_missing_library_fails_loudly():
+    """Without libexl3.so the binding raises at first use: there is no CPU or
+    PyTorch fallback behind the entry points."""
+    import subprocess
+    import sys
+
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from trellis_quantized_linear_had_amd import _lib\n"
+        "_lib.LIB_PATH = '/nonexistent/libexl3.so'\n"
+        "import trellis_quantized_linear_had_amd as T\n"
+        "try:\n"
+        "    T.logits_padded_width(248077, 248320)\n"
+        "except ImportError as e:\n"
+        "    print('raised:', e)\n"
+        "    sys.exit(0)\n"
+        "sys.exit(3)\n" % ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "not built" in r.stdout
