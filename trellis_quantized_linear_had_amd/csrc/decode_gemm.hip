@@ -311,16 +311,21 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
       f16x8 a0[G], a1[G];
       const int last = ws_end - 1;
       decode_load_step<NT, XL, G, NW, BITS>(crs, ntiles_total, ws_begin, tbase, loff, xsrc, s_begin, mok, w0, a0);
-      for (int step = ws_begin; step < ws_end; step += 2) {
-        decode_load_step<NT, XL, G, NW, BITS>(crs, ntiles_total, min(step + 1, last), tbase, loff, xsrc, s_begin,
-                                              mok, w1, a1);
+      // Pairs of k steps with no branch inside: each step's code words are
+      // requested before the previous step decodes. (With the second half of
+      // a pair under a branch, the compiler sank the loads of w1 into it, past
+      // the decode of w0, so every other step waited a full memory round trip
+      // for its words.) An odd step count ends with one step whose words are
+      // already in w0.
+      int step = ws_begin;
+      for (; step + 1 < ws_end; step += 2) {
+        decode_load_step<NT, XL, G, NW, BITS>(crs, ntiles_total, step + 1, tbase, loff, xsrc, s_begin, mok, w1, a1);
         decode_mfma_step<NT, G, NW, BITS>(cb_lds, w0, woff, a0, acc);
-        if (step + 1 < ws_end) {
-          decode_load_step<NT, XL, G, NW, BITS>(crs, ntiles_total, min(step + 2, last), tbase, loff, xsrc, s_begin,
-                                                mok, w0, a0);
-          decode_mfma_step<NT, G, NW, BITS>(cb_lds, w1, woff, a1, acc);
-        }
+        decode_load_step<NT, XL, G, NW, BITS>(crs, ntiles_total, min(step + 2, last), tbase, loff, xsrc, s_begin,
+                                              mok, w0, a0);
+        decode_mfma_step<NT, G, NW, BITS>(cb_lds, w1, woff, a1, acc);
       }
+      if (step < ws_end) decode_mfma_step<NT, G, NW, BITS>(cb_lds, w0, woff, a0, acc);
     }
 
     const bool dead = m0 + 16 * G >= M;  // last pass: the codebook is no longer read
