@@ -91,7 +91,7 @@ def main():
     import torch
 
     import trellis_quantized_linear_had_amd as X
-    from trellis_quantized_linear_had_amd import _lib
+    from trellis_quantized_linear_had_amd import _lib, _measure
 
     if args.pmc_workload:
         pmc_workload(args.pmc_workload)
@@ -215,26 +215,26 @@ def main():
     # records never sit inside the timed region.
     reps = 12
     kern_us = {}
-    _lib.kernel_timer(True)
+    kt = _measure.KernelTimer()
     try:
         for M in DEC_M:
             for r in range(reps):
-                call_linear(dec_layers[r % 12], xs[M], M, ys[M], dec_scratch)
-            ms, n = _lib.kernel_timer_read(_lib.TIMER_DECODE)
+                kt.linear(dec_layers[r % 12], xs[M], M, ys[M], dec_scratch, 128, sh, _measure.DECODE)
+            ms, n = kt.read(_measure.DECODE)
             kern_us["decode_gemm_kernel M=%d" % M] = ms / n * 1e3
-        for r in range(reps // 2):
-            call_linear(pre_layers[r % 6], xp, PREFILL_M, yp, pre_scratch)
-        ms, n = _lib.kernel_timer_read(_lib.TIMER_GEMM)
-        kern_us["gemm_had_kernel<0> M=2048"] = ms / n * 1e3
-        ms, n = _lib.kernel_timer_read(_lib.TIMER_RECONSTRUCT)
-        kern_us["reconstruct_nk_kernel K5120xN17408"] = ms / n * 1e3
+        for kind, key in ((_measure.GEMM, "gemm_had_kernel<0> M=2048"),
+                          (_measure.RECONSTRUCT, "reconstruct_nk_kernel K5120xN17408")):
+            for r in range(reps // 2):
+                kt.linear(pre_layers[r % 6], xp, PREFILL_M, yp, pre_scratch, 128, sh, kind)
+            ms, n = kt.read(kind)
+            kern_us[key] = ms / n * 1e3
         if not args.no_logits:
             for r in range(reps // 2):
-                call_logits()
-            ms, n = _lib.kernel_timer_read(_lib.TIMER_LOGITS)
+                kt.logits(xl, LOGITS_M, K, wl, w_rows, n_valid, lg, n_pad, am, lg_scratch, sh)
+            ms, n = kt.read(_measure.LOGITS)
             kern_us["logits_kernel M=16"] = ms / n * 1e3
     finally:
-        _lib.kernel_timer(False)
+        kt.close()
     torch.cuda.synchronize()
 
     # Algorithmic work per launch: packed codes read by the decode GEMM; 2MNK
@@ -566,20 +566,20 @@ def ceilings(log=None) -> dict:
     clock their loops ran at (s_memtime cycles over s_memrealtime time)."""
     import torch
 
-    from trellis_quantized_linear_had_amd import _lib
+    from trellis_quantized_linear_had_amd import _measure
 
-    lib = _lib.lib()
+    lib = _measure.mlib()
     sh = torch.cuda.current_stream().cuda_stream
     dev = torch.device("cuda:0")
-    sink = torch.empty(_lib.PROBE_SINK_BYTES, dtype=torch.uint8, device=dev)
-    clocks = torch.zeros(4 * _lib.PROBE_WORKGROUPS, dtype=torch.int64, device=dev)
+    sink = torch.empty(_measure.PROBE_SINK_BYTES, dtype=torch.uint8, device=dev)
+    clocks = torch.zeros(4 * _measure.PROBE_WORKGROUPS, dtype=torch.int64, device=dev)
 
     def timed(fn, reps=3):
         best, best_clk = None, None
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            _lib.check(fn())
+            _measure.check(fn())
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1)
@@ -592,33 +592,33 @@ def ceilings(log=None) -> dict:
 
     out = {}
     it = 4000
-    ms, (cyc, ghz) = timed(lambda: lib.exl3_probe_lds_gather(it, sink.data_ptr(), clocks.data_ptr(), sh))
+    ms, (cyc, ghz) = timed(lambda: lib.exl3m_probe_lds_gather(it, sink.data_ptr(), clocks.data_ptr(), sh))
     per_wg = 1024 * 16 * it
     out["lds_gather_lookups_per_cu_clk"] = per_wg / cyc
     out["lds_gather_clock_GHz"] = ghz
-    out["lds_gather_lookups_per_s"] = _lib.PROBE_WORKGROUPS * per_wg / (ms * 1e-3)
+    out["lds_gather_lookups_per_s"] = _measure.PROBE_WORKGROUPS * per_wg / (ms * 1e-3)
     out["lds_gather_GBps_4bit_codes"] = out["lds_gather_lookups_per_s"] * 0.5 / 1e9
     it = 100000
-    ms, (cyc, ghz) = timed(lambda: lib.exl3_probe_mfma(it, sink.data_ptr(), clocks.data_ptr(), sh))
-    out["mfma_f16_TFLOPs"] = _lib.PROBE_WORKGROUPS * 8 * 8 * it * 32768 / (ms * 1e-3) / 1e12
+    ms, (cyc, ghz) = timed(lambda: lib.exl3m_probe_mfma(it, sink.data_ptr(), clocks.data_ptr(), sh))
+    out["mfma_f16_TFLOPs"] = _measure.PROBE_WORKGROUPS * 8 * 8 * it * 32768 / (ms * 1e-3) / 1e12
     out["mfma_clock_GHz"] = ghz
     nbytes = 1 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf2 = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    _lib.check(lib.exl3_probe_stream(1, 0, buf.data_ptr(), nbytes, sink.data_ptr(), sh))
-    ms, _ = timed(lambda: lib.exl3_probe_stream(0, buf.data_ptr(), 0, nbytes, sink.data_ptr(), sh))
+    _measure.check(lib.exl3m_probe_stream(1, 0, buf.data_ptr(), nbytes, sink.data_ptr(), sh))
+    ms, _ = timed(lambda: lib.exl3m_probe_stream(0, buf.data_ptr(), 0, nbytes, sink.data_ptr(), sh))
     out["hbm_read_flat_GBps"] = nbytes / (ms * 1e-3) / 1e9
     # row pattern over 2048 waves of 128 rows of 10240 bytes (2.5 GiB): two
     # 4-wave workgroups per CU, all resident at once
     rbytes = 2048 * 128 * 10240
     rows = torch.empty(rbytes, dtype=torch.uint8, device=dev)
-    _lib.check(lib.exl3_probe_stream(1, 0, rows.data_ptr(), rbytes, sink.data_ptr(), sh))
+    _measure.check(lib.exl3m_probe_stream(1, 0, rows.data_ptr(), rbytes, sink.data_ptr(), sh))
     used = rbytes // (10240 * 128) * (10240 * 128)
-    ms, _ = timed(lambda: lib.exl3_probe_stream(2, rows.data_ptr(), 0, rbytes, sink.data_ptr(), sh))
+    ms, _ = timed(lambda: lib.exl3m_probe_stream(2, rows.data_ptr(), 0, rbytes, sink.data_ptr(), sh))
     out["hbm_read_rows_GBps"] = used / (ms * 1e-3) / 1e9
     out["hbm_read_GBps"] = max(out["hbm_read_flat_GBps"], out["hbm_read_rows_GBps"])
     del rows
-    ms, _ = timed(lambda: lib.exl3_probe_stream(1, 0, buf.data_ptr(), nbytes, sink.data_ptr(), sh))
+    ms, _ = timed(lambda: lib.exl3m_probe_stream(1, 0, buf.data_ptr(), nbytes, sink.data_ptr(), sh))
     out["hbm_write_GBps"] = nbytes / (ms * 1e-3) / 1e9
     best = None
     for _ in range(3):
@@ -647,7 +647,7 @@ def bits_sweep() -> str:
     import torch
 
     import trellis_quantized_linear_had_amd as X
-    from trellis_quantized_linear_had_amd import _lib
+    from trellis_quantized_linear_had_amd import _lib, _measure
 
     lib = _lib.lib()
     dev = torch.device("cuda:0")
@@ -668,13 +668,15 @@ def bits_sweep() -> str:
         e1.record()
         torch.cuda.synchronize()
         call_us = e0.elapsed_time(e1) / reps * 1e3
-        _lib.kernel_timer(True)
+        kt = _measure.KernelTimer()
+        kern = {}
         try:
-            for i in range(reps):
-                one(i)
-            kern = {k: _lib.kernel_timer_read(k) for k in (_lib.TIMER_DECODE, _lib.TIMER_RECONSTRUCT)}
+            for kind in (_measure.DECODE, _measure.RECONSTRUCT):
+                for i in range(reps):
+                    kt.linear(layers[i % len(layers)], x, M, y, scr, 128, sh, kind)
+                kern[kind] = kt.read(kind)
         finally:
-            _lib.kernel_timer(False)
+            kt.close()
         kern_us = {k: (ms / n * 1e3 if n else None) for k, (ms, n) in kern.items()}
         return call_us, kern_us
 
@@ -693,8 +695,8 @@ def bits_sweep() -> str:
             row[M] = time_calls(layers, x, M, y, scr, 24 if M < 128 else 6)
             del x, y, scr
         roof = LDS_GATHER_ROOF_GBPS * bits / 4  # one gather per weight: bits / 8 bytes of codes
-        dk = row[1][1][_lib.TIMER_DECODE]
-        rk = row[PREFILL_M][1][_lib.TIMER_RECONSTRUCT]
+        dk = row[1][1][_measure.DECODE]
+        rk = row[PREFILL_M][1][_measure.RECONSTRUCT]
         rbytes = K * N * bits // 8 + K * N * 2 + N * 2
         out.append("| %d | %d | %.1f | %.0f | %.1f | %.0f | %.1f %% | %.1f %% | %.1f | %.1f | %.1f | %.1f | %.2f |" % (
             bits, code_bytes, row[1][0], code_bytes / row[1][0] / 1e3, dk, code_bytes / dk / 1e3,
@@ -718,7 +720,7 @@ def head_sweep() -> str:
     import torch
 
     import trellis_quantized_linear_had_amd as X
-    from trellis_quantized_linear_had_amd import _lib
+    from trellis_quantized_linear_had_amd import _lib, _measure
 
     lib = _lib.lib()
     dev = torch.device("cuda:0")
@@ -758,13 +760,13 @@ def head_sweep() -> str:
                 _lib.check(lib.exl3_head_logits_argmax(lay.c, x.data_ptr(), M, n_valid, lg.data_ptr(), n_pad,
                                                        am.data_ptr(), scr.data_ptr(), scr.numel(), 128, sh))
             call_us = timed(call, 20)
-            _lib.kernel_timer(True)
+            kt = _measure.KernelTimer()
             try:
                 for _ in range(20):
-                    call()
-                ms, n = _lib.kernel_timer_read(_lib.TIMER_DECODE)
+                    kt.head(lay, x, M, n_valid, lg, n_pad, am, scr, 128, sh, _measure.DECODE)
+                ms, n = kt.read(_measure.DECODE)
             finally:
-                _lib.kernel_timer(False)
+                kt.close()
             dk = ms / n * 1e3
             out.append("| %d | %d | %d | %.1f | %.0f | %.1f | %.0f | %.1f %% | %.1f %% | %.1f |" % (
                 bits, M, code_bytes, call_us, code_bytes / call_us / 1e3, dk, code_bytes / dk / 1e3,

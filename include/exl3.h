@@ -216,43 +216,6 @@ size_t exl3_head_scratch_bytes(int32_t K, int32_t N, int64_t M, int64_t n_valid,
 /* Test hook: states[k * N + n] = the 16-bit trellis state behind W[k][n]. */
 int exl3_decode_states(const exl3_layer *layer, uint16_t *states, void *stream);
 
-/* Measurement hook (for benchmarks; not used by the hot path). While enabled
- * (on != 0), every later call records a pair of HIP events on its stream
- * around one kernel: kind 0 the decode GEMM of exl3_linear, kind 1 the
- * full-tile launch of the prefill GEMM (one per column slice), kind 2 the
- * logits GEMM (one per 16-row group), kind 3 the prefill path's reconstruct
- * of one column slice (its one or more launches). Enabling costs an event creation per
- * timed launch; leave it off under graph capture. */
-int exl3_kernel_timer_enable(int on);
-
-/* Waits for the recorded event pairs of one kind, returns their summed
- * milliseconds and their count, and forgets them. EXL3_EINVAL for an unknown
- * kind or NULL outputs; EXL3_EHIP if an event fails. */
-int exl3_kernel_timer_read(int kind, double *total_ms, int64_t *count);
-
-/* Measured ceilings (for benchmarks; not used by the hot path). Each probe
- * launches EXL3_PROBE_WORKGROUPS workgroups on `stream` and returns at once.
- *   exl3_probe_lds_gather: every lane issues `iters` x 16 random 16-bit reads
- *     from a 128 KiB LDS table (the codebook gathers of the trellis kernels);
- *   exl3_probe_mfma: 8 waves per workgroup each issue `iters` x 8 independent
- *     v_mfma_f32_32x32x16_f16 (32768 FLOP each);
- *   exl3_probe_stream: write = 0 reads `bytes` of src in 16-byte accesses,
- *     1 fills `bytes` of dst, 2 reads src as rows of 10240 bytes in the
- *     padded-logits GEMM's pattern (each 16-byte load instruction reads 64
- *     bytes of each of 16 rows; whole groups of 128 rows only, so
- *     floor(bytes / 1310720) * 1310720 bytes); bytes a multiple of 16.
- * sink: device buffer of EXL3_PROBE_SINK_BYTES that keeps the results live.
- * clocks (compute probes): device buffer of 4 x EXL3_PROBE_WORKGROUPS uint64:
- * per workgroup the shader-clock counter (s_memtime) before and after its
- * loop, then the 100 MHz real-time counter (s_memrealtime) before and after.
- * EXL3_EINVAL for NULL or misaligned pointers, negative sizes, an unknown
- * stream mode or a byte count that is not a multiple of 16. */
-#define EXL3_PROBE_WORKGROUPS 256
-#define EXL3_PROBE_SINK_BYTES (256 * 32 * 256 * 4)
-int exl3_probe_lds_gather(int64_t iters, uint32_t *sink, uint64_t *clocks, void *stream);
-int exl3_probe_mfma(int64_t iters, float *sink, uint64_t *clocks, void *stream);
-int exl3_probe_stream(int32_t write, const void *src, void *dst, int64_t bytes, uint32_t *sink, void *stream);
-
 /* Human-readable text for a status; for EXL3_EHIP and validation failures it
  * names the condition of the most recent failing call on this thread. */
 const char *exl3_strerror(int status);

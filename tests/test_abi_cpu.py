@@ -187,27 +187,52 @@ def test_head_validation_and_scratch():
     assert L.exl3_head_scratch_bytes(256, 1024, 0, 10, 128) == 0
 
 
-def test_probe_validation_without_gpu():
-    L = X.lib()
-    assert L.exl3_probe_lds_gather(-1, 0x1000, 0x2000, None) == X.EXL3_EINVAL
-    assert L.exl3_probe_mfma(10, 0, 0x2000, None) == X.EXL3_EINVAL
-    assert L.exl3_probe_stream(0, 0x1000, 0, 24, 0x2000, None) == X.EXL3_EINVAL   # not a multiple of 16
-    assert L.exl3_probe_stream(1, 0x1000, 0, 32, 0x2000, None) == X.EXL3_EINVAL   # write needs dst
-    assert L.exl3_probe_stream(0, 0x1000, 0, 0, 0x2000, None) == X.EXL3_OK        # nothing to stream
-    assert L.exl3_probe_stream(3, 0x1000, 0x1000, 32, 0x2000, None) == X.EXL3_EINVAL  # unknown mode
-    assert L.exl3_probe_stream(2, 0, 0x1000, 32, 0x2000, None) == X.EXL3_EINVAL   # row read needs src
+def measure_declared_functions():
+    src = open(os.path.join(ROOT, "trellis_quantized_linear_had_amd", "measure", "measure.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
 
 
-def test_kernel_timer_validation_without_gpu():
-    L = X.lib()
-    ms, n = ctypes.c_double(-1.0), ctypes.c_int64(-1)
-    assert L.exl3_kernel_timer_read(4, ctypes.byref(ms), ctypes.byref(n)) == X.EXL3_EINVAL
-    assert L.exl3_kernel_timer_read(-1, ctypes.byref(ms), ctypes.byref(n)) == X.EXL3_EINVAL
-    assert L.exl3_kernel_timer_read(0, None, ctypes.byref(n)) == X.EXL3_EINVAL
-    # nothing recorded: no HIP call, zero launches
-    assert L.exl3_kernel_timer_read(2, ctypes.byref(ms), ctypes.byref(n)) == X.EXL3_OK
-    assert (ms.value, n.value) == (0.0, 0)
-    assert L.exl3_kernel_timer_enable(0) == X.EXL3_OK
+def test_product_library_holds_no_measurement_code():
+    """The product library exports the C ABI of exl3.h and no timing hook or
+    probe; those live in the separate measurement library."""
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", X.LIB_PATH], capture_output=True, text=True).stdout
+    names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    c_names = {n for n in names if not n.startswith("_")}
+    assert c_names == set(X.EXPORTS), sorted(c_names ^ set(X.EXPORTS))
+    assert not any("probe" in n or "timer" in n for n in names)
+
+
+def test_measure_library_exports_and_validation_without_gpu():
+    from trellis_quantized_linear_had_amd import _measure as MS
+
+    decl = measure_declared_functions()
+    assert set(decl) == set(MS.EXPORTS), decl
+    L = MS.mlib()
+    for name in decl:
+        assert hasattr(L, name), name
+    assert L.exl3m_probe_lds_gather(-1, 0x1000, 0x2000, None) == X.EXL3_EINVAL
+    assert L.exl3m_probe_mfma(10, 0, 0x2000, None) == X.EXL3_EINVAL
+    assert L.exl3m_probe_stream(0, 0x1000, 0, 24, 0x2000, None) == X.EXL3_EINVAL   # not a multiple of 16
+    assert L.exl3m_probe_stream(1, 0x1000, 0, 32, 0x2000, None) == X.EXL3_EINVAL   # write needs dst
+    assert L.exl3m_probe_stream(0, 0x1000, 0, 0, 0x2000, None) == X.EXL3_OK        # nothing to stream
+    assert L.exl3m_probe_stream(3, 0x1000, 0x1000, 32, 0x2000, None) == X.EXL3_EINVAL  # unknown mode
+    assert L.exl3m_probe_stream(2, 0, 0x1000, 32, 0x2000, None) == X.EXL3_EINVAL   # row read needs src
+    assert "misaligned" in L.exl3m_strerror(X.EXL3_EINVAL).decode()
+    used = ctypes.c_int(-1)
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    # an unknown mark kind, and event arrays missing: refused before the library call
+    assert L.exl3m_linear_marked(None, None, 1, None, None, 0, 128, None, 7, 0, None, None,
+                                 ctypes.byref(used)) == X.EXL3_EINVAL
+    assert L.exl3m_linear_marked(None, None, 1, None, None, 0, 128, None, 0, 4, None, None,
+                                 ctypes.byref(used)) == X.EXL3_EINVAL
+    # valid marks, then the library's own validation (NULL layer) speaks
+    assert L.exl3m_linear_marked(None, None, 1, None, None, 0, 128, None, 0, 0, vpp(), vpp(),
+                                 ctypes.byref(used)) == X.EXL3_EINVAL
+    assert used.value == 0
+    assert "layer is NULL" in L.exl3m_strerror(X.EXL3_EINVAL).decode()
 
 
 def test_missing_library_fails_loudly():

@@ -32,15 +32,8 @@ EXPORTS = (
     "logits_padded_width",
     "logits_scratch_bytes",
     "exl3_decode_states",
-    "exl3_kernel_timer_enable",
-    "exl3_kernel_timer_read",
-    "exl3_probe_lds_gather",
-    "exl3_probe_mfma",
-    "exl3_probe_stream",
     "exl3_strerror",
 )
-PROBE_WORKGROUPS = 256
-PROBE_SINK_BYTES = 256 * 32 * 256 * 4
 
 
 class Exl3Layer(ctypes.Structure):
@@ -86,36 +79,10 @@ def lib() -> ctypes.CDLL:
         L.logits_scratch_bytes.restype = sz
         L.exl3_decode_states.argtypes = [ctypes.POINTER(Exl3Layer), vp, vp]
         L.exl3_decode_states.restype = ctypes.c_int
-        L.exl3_kernel_timer_enable.argtypes = [ctypes.c_int]
-        L.exl3_kernel_timer_enable.restype = ctypes.c_int
-        L.exl3_kernel_timer_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
-        L.exl3_kernel_timer_read.restype = ctypes.c_int
-        L.exl3_probe_lds_gather.argtypes = [i64, vp, vp, vp]
-        L.exl3_probe_lds_gather.restype = ctypes.c_int
-        L.exl3_probe_mfma.argtypes = [i64, vp, vp, vp]
-        L.exl3_probe_mfma.restype = ctypes.c_int
-        L.exl3_probe_stream.argtypes = [i32, vp, vp, i64, vp, vp]
-        L.exl3_probe_stream.restype = ctypes.c_int
         L.exl3_strerror.argtypes = [ctypes.c_int]
         L.exl3_strerror.restype = ctypes.c_char_p
         _lib = L
     return _lib
-
-
-TIMER_DECODE, TIMER_GEMM, TIMER_LOGITS, TIMER_RECONSTRUCT = 0, 1, 2, 3
-
-
-def kernel_timer(on: bool) -> None:
-    """Enable or disable the library's per-kernel event timing hook."""
-    check(lib().exl3_kernel_timer_enable(1 if on else 0))
-
-
-def kernel_timer_read(kind: int):
-    """(summed milliseconds, launch count) of the kernels of one kind timed
-    since the last read."""
-    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
-    check(lib().exl3_kernel_timer_read(kind, ctypes.byref(ms), ctypes.byref(n)))
-    return ms.value, n.value
 
 
 def check(status: int) -> None:

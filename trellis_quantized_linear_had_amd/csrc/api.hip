@@ -18,7 +18,8 @@
 
 #include "exl3.h"
 #include "decode_plan.h"
-#include "timer.h"
+#include "internal.h"
+#include "marks.h"
 
 namespace exl3 {
 hipError_t launch_had128_frag(const uint16_t* in, uint16_t* out, int64_t M, int32_t K, const uint16_t* sign_pre,
@@ -41,60 +42,14 @@ hipError_t launch_head_mask_argmax(uint16_t* logits, int64_t ld, int64_t M, int6
                                    int64_t* argmax, float* pv, int32_t* pi, hipStream_t stream);
 int64_t head_argmax_items(int64_t n_pad);
 hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
-                           int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream);
+                           int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream,
+                           Marks* marks);
 size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K);
-hipError_t launch_probe_lds_gather(int64_t iters, uint32_t* sink, uint64_t* clocks, hipStream_t stream);
-hipError_t launch_probe_mfma(int64_t iters, float* sink, uint64_t* clocks, hipStream_t stream);
-hipError_t launch_probe_stream(int32_t write, const void* src, void* dst, int64_t bytes, uint32_t* sink,
-                               hipStream_t stream);
 hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int64_t n_valid, int64_t n_pad,
                          uint16_t* logits, int64_t ld, int64_t* argmax, float* pv, int32_t* pi, uint16_t* xp,
-                         hipStream_t stream);
+                         hipStream_t stream, Marks* marks);
 int64_t logits_items(int64_t n_pad);
 size_t logits_xperm_bytes(int64_t M, int32_t K);
-}  // namespace exl3
-
-// Measurement hook state. Events are created only while the hook is on.
-namespace exl3 {
-namespace {
-struct TimedLaunch {
-  int kind;
-  hipEvent_t start, stop;
-};
-std::mutex g_timer_mu;
-std::vector<TimedLaunch> g_timed;
-std::atomic<bool> g_timer_on{false};
-thread_local hipEvent_t t_open[kTimerKinds] = {};
-}  // namespace
-
-void timer_begin(int kind, hipStream_t stream) {
-  if (t_open[kind]) {  // an earlier launch of this kind failed before its end
-    (void)hipEventDestroy(t_open[kind]);
-    t_open[kind] = nullptr;
-  }
-  if (!g_timer_on.load(std::memory_order_relaxed)) return;
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return;
-  if (hipEventRecord(e, stream) != hipSuccess) {
-    (void)hipEventDestroy(e);
-    return;
-  }
-  t_open[kind] = e;
-}
-
-void timer_end(int kind, hipStream_t stream) {
-  hipEvent_t a = t_open[kind];
-  if (!a) return;
-  t_open[kind] = nullptr;
-  hipEvent_t b = nullptr;
-  if (hipEventCreate(&b) != hipSuccess || hipEventRecord(b, stream) != hipSuccess) {
-    (void)hipEventDestroy(a);
-    if (b) (void)hipEventDestroy(b);
-    return;
-  }
-  std::lock_guard<std::mutex> lk(g_timer_mu);
-  g_timed.push_back(TimedLaunch{kind, a, b});
-}
 }  // namespace exl3
 
 using namespace exl3;
@@ -351,7 +306,7 @@ size_t linear_cols_scratch_bytes(int32_t K, int32_t ncols, int64_t M, int32_t pr
 }
 
 int linear_cols(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, int64_t ldy, int32_t ncols,
-                char* sb, int32_t prefill_min_m, hipStream_t stream) {
+                char* sb, int32_t prefill_min_m, hipStream_t stream, Marks* marks) {
   const int32_t K = L->K, N = L->N;
   if (use_prefill(M, prefill_min_m)) {
     const PrefillLayout l = prefill_layout(K, ncols, M);
@@ -360,31 +315,24 @@ int linear_cols(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
     EXL3_TRY(launch_had128_frag(x, xr, M, K, L->sign_k, stream), "input rotation");
     for (int32_t n0 = 0; n0 < ncols; n0 += l.chunk) {
       const int32_t nc = std::min(l.chunk, ncols - n0);
-      timer_begin(kTimerReconstruct, stream);
+      EXL3_TRY(mark_begin(marks, kMarkReconstruct, stream), "event record");
       EXL3_TRY(launch_reconstruct_nk(L->codes, L->codebook, L->scale, K, N, L->bits, n0, nc, wt, K, stream),
                "reconstruct");
-      timer_end(kTimerReconstruct, stream);
-      EXL3_TRY(launch_gemm_had(wt, xr, y, nc, (int32_t)M, K, ldy, n0, L->sign_n, (float*)(sb + l.part_off), stream),
+      EXL3_TRY(mark_end(marks, kMarkReconstruct, stream), "event record");
+      EXL3_TRY(launch_gemm_had(wt, xr, y, nc, (int32_t)M, K, ldy, n0, L->sign_n, (float*)(sb + l.part_off), stream,
+                               marks),
                "gemm");
     }
   } else {
     const DecodeLayout l = decode_layout(K, ncols, M, L->bits);
     uint16_t* xr = (uint16_t*)(sb + l.xr_off);
     float* part = (float*)(sb + l.part_off);
-    if (l.plan.x_in_lds) {
-      timer_begin(kTimerDecode, stream);
-      EXL3_TRY(launch_decode_gemm(x, L->sign_k, L->codes, L->codebook, part, K, ncols, N / 16, (int32_t)M, L->bits,
-                                  l.plan, stream),
-               "decode gemm");
-      timer_end(kTimerDecode, stream);
-    } else {
-      EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
-      timer_begin(kTimerDecode, stream);
-      EXL3_TRY(launch_decode_gemm(xr, nullptr, L->codes, L->codebook, part, K, ncols, N / 16, (int32_t)M, L->bits,
-                                  l.plan, stream),
-               "decode gemm");
-      timer_end(kTimerDecode, stream);
-    }
+    if (!l.plan.x_in_lds) EXL3_TRY(launch_had128(x, xr, M, K, L->sign_k, nullptr, stream), "input rotation");
+    EXL3_TRY(mark_begin(marks, kMarkDecode, stream), "event record");
+    EXL3_TRY(launch_decode_gemm(l.plan.x_in_lds ? x : xr, l.plan.x_in_lds ? L->sign_k : nullptr, L->codes,
+                                L->codebook, part, K, ncols, N / 16, (int32_t)M, L->bits, l.plan, stream),
+             "decode gemm");
+    EXL3_TRY(mark_end(marks, kMarkDecode, stream), "event record");
     EXL3_TRY(launch_decode_finalize(part, l.plan.ks_count, L->scale, L->sign_n, y, ldy, (int32_t)M, ncols, stream),
              "decode finalize");
   }
@@ -434,16 +382,10 @@ HeadLayout head_layout(int32_t K, int32_t N, int64_t M, int64_t n_valid, int32_t
 
 }  // namespace
 
-extern "C" {
+namespace exl3 {
 
-size_t exl3_linear_scratch_bytes(int32_t K, int32_t N, int64_t M, int32_t prefill_min_m) {
-  if (K <= 0 || N <= 0 || K % 128 || N % 128 || M < 0) return 0;
-  if (M == 0) return 0;
-  return linear_cols_scratch_bytes(K, N, M, prefill_min_m);
-}
-
-int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* scratch, size_t scratch_bytes,
-                int32_t prefill_min_m, void* stream_) {
+int linear_entry(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* scratch, size_t scratch_bytes,
+                 int32_t prefill_min_m, hipStream_t stream, Marks* marks) {
   g_msg[0] = 0;
   int st = validate_call(L, x, M, y, scratch, prefill_min_m);
   if (st || M == 0) return st;
@@ -452,17 +394,44 @@ int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
     return fail(EXL3_ESCRATCH, "scratch has %zu bytes; this call needs %zu", scratch_bytes, need);
   st = check_device();
   if (st) return st;
-  return linear_cols(L, x, M, y, L->N, L->N, (char*)scratch, prefill_min_m, (hipStream_t)stream_);
+  return linear_cols(L, x, M, y, L->N, L->N, (char*)scratch, prefill_min_m, stream, marks);
 }
 
-size_t exl3_head_scratch_bytes(int32_t K, int32_t N, int64_t M, int64_t n_valid, int32_t prefill_min_m) {
-  if (K <= 0 || N <= 0 || K % 128 || N % 128 || M <= 0 || n_valid < 1 || n_valid > N) return 0;
-  return head_layout(K, N, M, n_valid, prefill_min_m).total;
+int logits_entry(const uint16_t* x, int64_t M, int32_t K, const uint16_t* w, int64_t w_rows, int64_t n_valid,
+                 uint16_t* logits, int64_t ld_logits, int64_t* argmax, void* scratch, size_t scratch_bytes,
+                 hipStream_t stream, Marks* marks) {
+  g_msg[0] = 0;
+  if (M < 0 || w_rows < 0) return fail(EXL3_EINVAL, "M = %lld, w_rows = %lld", (long long)M, (long long)w_rows);
+  if (M > 0x7FFFFFFF || w_rows > 0x7FFFFFFF) return fail(EXL3_EINVAL, "M or w_rows too large");
+  if (K <= 0 || K % 128) return fail(EXL3_ESHAPE, "K = %d must be a positive multiple of 128", K);
+  const int64_t n_pad = logits_padded_width(n_valid, w_rows);
+  if (n_pad < 0)
+    return fail(EXL3_EWIDTH, "n_valid = %lld must be in [1, w_rows = %lld]", (long long)n_valid, (long long)w_rows);
+  if (ld_logits < n_pad)
+    return fail(EXL3_EWIDTH, "ld_logits = %lld is below the padded width %lld", (long long)ld_logits,
+                (long long)n_pad);
+  if (M == 0) return EXL3_OK;
+  if (!x || !w || !logits || !argmax || !scratch) return fail(EXL3_EINVAL, "a required pointer is NULL");
+  if (!aligned16(x) || !aligned16(w) || ((uintptr_t)logits & 1) || ((uintptr_t)argmax & 7) ||
+      ((uintptr_t)scratch & 255u))
+    return fail(EXL3_EINVAL, "misaligned pointer");
+  const size_t need = logits_scratch_bytes(M, K, n_valid, w_rows);
+  if (scratch_bytes < need)
+    return fail(EXL3_ESCRATCH, "scratch has %zu bytes; this call needs %zu", scratch_bytes, need);
+  int st = check_device();
+  if (st) return st;
+  const int64_t items = logits_items(n_pad);
+  float* pv = (float*)scratch;
+  int32_t* pi = (int32_t*)((char*)scratch + align256((size_t)items * M * 4));
+  uint16_t* xp = (uint16_t*)((char*)scratch + align256((size_t)items * M * 4) * 2);
+  EXL3_TRY(launch_logits(x, (int32_t)M, K, w, n_valid, n_pad, logits, ld_logits, argmax, pv, pi, xp, stream, marks),
+           "logits");
+  return EXL3_OK;
 }
 
-int exl3_head_logits_argmax(const exl3_layer* L, const uint16_t* x, int64_t M, int64_t n_valid, uint16_t* logits,
-                            int64_t ld_logits, int64_t* argmax, void* scratch, size_t scratch_bytes,
-                            int32_t prefill_min_m, void* stream_) {
+int head_entry(const exl3_layer* L, const uint16_t* x, int64_t M, int64_t n_valid, uint16_t* logits,
+               int64_t ld_logits, int64_t* argmax, void* scratch, size_t scratch_bytes, int32_t prefill_min_m,
+               hipStream_t stream, Marks* marks) {
   g_msg[0] = 0;
   int st = validate_call(L, x, M, logits, scratch, prefill_min_m);
   if (st) return st;
@@ -479,15 +448,41 @@ int exl3_head_logits_argmax(const exl3_layer* L, const uint16_t* x, int64_t M, i
     return fail(EXL3_ESCRATCH, "scratch has %zu bytes; this call needs %zu", scratch_bytes, need);
   st = check_device();
   if (st) return st;
-  hipStream_t stream = (hipStream_t)stream_;
   char* sb = (char*)scratch;
   const HeadLayout h = head_layout(L->K, L->N, M, n_valid, prefill_min_m);
-  st = linear_cols(L, x, M, logits, ld_logits, (int32_t)n_pad, sb, prefill_min_m, stream);
+  st = linear_cols(L, x, M, logits, ld_logits, (int32_t)n_pad, sb, prefill_min_m, stream, marks);
   if (st) return st;
   EXL3_TRY(launch_head_mask_argmax(logits, ld_logits, M, n_valid, n_pad, argmax, (float*)(sb + h.pv_off),
                                    (int32_t*)(sb + h.pi_off), stream),
            "mask and argmax");
   return EXL3_OK;
+}
+
+}  // namespace exl3
+
+extern "C" {
+
+size_t exl3_linear_scratch_bytes(int32_t K, int32_t N, int64_t M, int32_t prefill_min_m) {
+  if (K <= 0 || N <= 0 || K % 128 || N % 128 || M < 0) return 0;
+  if (M == 0) return 0;
+  return linear_cols_scratch_bytes(K, N, M, prefill_min_m);
+}
+
+int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* scratch, size_t scratch_bytes,
+                int32_t prefill_min_m, void* stream_) {
+  return exl3::linear_entry(L, x, M, y, scratch, scratch_bytes, prefill_min_m, (hipStream_t)stream_, nullptr);
+}
+
+size_t exl3_head_scratch_bytes(int32_t K, int32_t N, int64_t M, int64_t n_valid, int32_t prefill_min_m) {
+  if (K <= 0 || N <= 0 || K % 128 || N % 128 || M <= 0 || n_valid < 1 || n_valid > N) return 0;
+  return head_layout(K, N, M, n_valid, prefill_min_m).total;
+}
+
+int exl3_head_logits_argmax(const exl3_layer* L, const uint16_t* x, int64_t M, int64_t n_valid, uint16_t* logits,
+                            int64_t ld_logits, int64_t* argmax, void* scratch, size_t scratch_bytes,
+                            int32_t prefill_min_m, void* stream_) {
+  return exl3::head_entry(L, x, M, n_valid, logits, ld_logits, argmax, scratch, scratch_bytes, prefill_min_m,
+                          (hipStream_t)stream_, nullptr);
 }
 
 int exl3_reconstruct(const exl3_layer* L, int32_t n0, int32_t n_count, uint16_t* w, int64_t ldw, int32_t layout,
@@ -563,105 +558,8 @@ size_t logits_scratch_bytes(int64_t M, int32_t K, int64_t n_valid, int64_t w_row
 int logits_pad_mask_argmax(const uint16_t* x, int64_t M, int32_t K, const uint16_t* w, int64_t w_rows,
                            int64_t n_valid, uint16_t* logits, int64_t ld_logits, int64_t* argmax, void* scratch,
                            size_t scratch_bytes, void* stream_) {
-  g_msg[0] = 0;
-  if (M < 0 || w_rows < 0) return fail(EXL3_EINVAL, "M = %lld, w_rows = %lld", (long long)M, (long long)w_rows);
-  if (M > 0x7FFFFFFF || w_rows > 0x7FFFFFFF) return fail(EXL3_EINVAL, "M or w_rows too large");
-  if (K <= 0 || K % 128) return fail(EXL3_ESHAPE, "K = %d must be a positive multiple of 128", K);
-  const int64_t n_pad = logits_padded_width(n_valid, w_rows);
-  if (n_pad < 0)
-    return fail(EXL3_EWIDTH, "n_valid = %lld must be in [1, w_rows = %lld]", (long long)n_valid, (long long)w_rows);
-  if (ld_logits < n_pad)
-    return fail(EXL3_EWIDTH, "ld_logits = %lld is below the padded width %lld", (long long)ld_logits,
-                (long long)n_pad);
-  if (M == 0) return EXL3_OK;
-  if (!x || !w || !logits || !argmax || !scratch) return fail(EXL3_EINVAL, "a required pointer is NULL");
-  if (!aligned16(x) || !aligned16(w) || ((uintptr_t)logits & 1) || ((uintptr_t)argmax & 7) ||
-      ((uintptr_t)scratch & 255u))
-    return fail(EXL3_EINVAL, "misaligned pointer");
-  const size_t need = logits_scratch_bytes(M, K, n_valid, w_rows);
-  if (scratch_bytes < need)
-    return fail(EXL3_ESCRATCH, "scratch has %zu bytes; this call needs %zu", scratch_bytes, need);
-  int st = check_device();
-  if (st) return st;
-  const int64_t items = logits_items(n_pad);
-  float* pv = (float*)scratch;
-  int32_t* pi = (int32_t*)((char*)scratch + align256((size_t)items * M * 4));
-  uint16_t* xp = (uint16_t*)((char*)scratch + align256((size_t)items * M * 4) * 2);
-  EXL3_TRY(launch_logits(x, (int32_t)M, K, w, n_valid, n_pad, logits, ld_logits, argmax, pv, pi, xp,
-                         (hipStream_t)stream_),
-           "logits");
-  return EXL3_OK;
+  return exl3::logits_entry(x, M, K, w, w_rows, n_valid, logits, ld_logits, argmax, scratch, scratch_bytes,
+                            (hipStream_t)stream_, nullptr);
 }
 
 }  // extern "C"
-
-int exl3_kernel_timer_enable(int on) {
-  g_timer_on.store(on != 0);
-  return EXL3_OK;
-}
-
-int exl3_kernel_timer_read(int kind, double* total_ms, int64_t* count) {
-  g_msg[0] = 0;
-  if (kind < 0 || kind >= kTimerKinds) return fail(EXL3_EINVAL, "timer kind %d is not 0, 1, 2 or 3", kind);
-  if (!total_ms || !count) return fail(EXL3_EINVAL, "total_ms or count is NULL");
-  std::vector<TimedLaunch> mine;
-  {
-    std::lock_guard<std::mutex> lk(g_timer_mu);
-    std::vector<TimedLaunch> rest;
-    for (const TimedLaunch& t : g_timed) (t.kind == kind ? mine : rest).push_back(t);
-    g_timed.swap(rest);
-  }
-  double sum = 0.0;
-  int st = EXL3_OK;
-  for (const TimedLaunch& t : mine) {
-    float ms = 0.f;
-    if (st == EXL3_OK) {
-      hipError_t e = hipEventSynchronize(t.stop);
-      if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
-      if (e != hipSuccess) st = fail(EXL3_EHIP, "timer event: %s", hipGetErrorString(e));
-    }
-    sum += ms;
-    (void)hipEventDestroy(t.start);
-    (void)hipEventDestroy(t.stop);
-  }
-  *total_ms = sum;
-  *count = (int64_t)mine.size();
-  return st;
-}
-
-int exl3_probe_lds_gather(int64_t iters, uint32_t* sink, uint64_t* clocks, void* stream) {
-  g_msg[0] = 0;
-  if (iters < 0) return fail(EXL3_EINVAL, "iters = %lld is negative", (long long)iters);
-  if (!sink || !clocks || !aligned16(sink) || !aligned16(clocks))
-    return fail(EXL3_EINVAL, "sink or clocks NULL or misaligned");
-  int st = check_device();
-  if (st) return st;
-  EXL3_TRY(launch_probe_lds_gather(iters, sink, clocks, (hipStream_t)stream), "lds gather probe");
-  return EXL3_OK;
-}
-
-int exl3_probe_mfma(int64_t iters, float* sink, uint64_t* clocks, void* stream) {
-  g_msg[0] = 0;
-  if (iters < 0) return fail(EXL3_EINVAL, "iters = %lld is negative", (long long)iters);
-  if (!sink || !clocks || !aligned16(sink) || !aligned16(clocks))
-    return fail(EXL3_EINVAL, "sink or clocks NULL or misaligned");
-  int st = check_device();
-  if (st) return st;
-  EXL3_TRY(launch_probe_mfma(iters, sink, clocks, (hipStream_t)stream), "mfma probe");
-  return EXL3_OK;
-}
-
-int exl3_probe_stream(int32_t write, const void* src, void* dst, int64_t bytes, uint32_t* sink, void* stream) {
-  g_msg[0] = 0;
-  if (bytes < 0 || bytes % 16) return fail(EXL3_EINVAL, "bytes = %lld must be a non-negative multiple of 16",
-                                           (long long)bytes);
-  if (write < 0 || write > 2) return fail(EXL3_EINVAL, "stream mode %d is not 0, 1 or 2", write);
-  const void* buf = write == 1 ? dst : src;
-  if (!buf || !aligned16(buf) || !sink || !aligned16(sink))
-    return fail(EXL3_EINVAL, "stream buffer or sink NULL or misaligned");
-  if (bytes == 0) return EXL3_OK;
-  int st = check_device();
-  if (st) return st;
-  EXL3_TRY(launch_probe_stream(write, src, dst, bytes, sink, (hipStream_t)stream), "stream probe");
-  return EXL3_OK;
-}

@@ -42,7 +42,7 @@
 // share one 256-row strip of W^T run together on one XCD and read it through
 // that XCD's L2.
 #include "common.h"
-#include "timer.h"
+#include "marks.h"
 
 namespace exl3 {
 
@@ -506,14 +506,19 @@ size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K) {
 }
 
 hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
-                           int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream) {
+                           int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream,
+                           Marks* marks) {
   const GemmPlan g = gemm_plan(P, Q, K);
   f32x4* part = reinterpret_cast<f32x4*>(partial);
   if (g.full > 0) {
-    timer_begin(kTimerGemm, stream);
+    hipError_t e = mark_begin(marks, kMarkGemm, stream);
+    if (e != hipSuccess) return e;
     gemm_had_kernel<0><<<8 * ((g.full + 7) / 8), G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, 0, g.full,
                                                                          0, 1, 0, part);
-    timer_end(kTimerGemm, stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = mark_end(marks, kMarkGemm, stream);
+    if (e != hipSuccess) return e;
   }
   if (g.rem > 0) {
     gemm_had_kernel<1><<<8 * ((g.pieces + 7) / 8), G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, g.full,

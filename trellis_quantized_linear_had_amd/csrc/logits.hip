@@ -17,7 +17,7 @@
 // slower per call at M = 16 (the row-strided lines crowd a few L2 channels).
 // The loads of the next chunk are issued before the MFMAs of the current one.
 #include "common.h"
-#include "timer.h"
+#include "marks.h"
 
 namespace exl3 {
 
@@ -187,7 +187,7 @@ size_t logits_xperm_bytes(int64_t M, int32_t K) { return (size_t)((M + 15) / 16)
 
 hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int64_t n_valid, int64_t n_pad,
                          uint16_t* logits, int64_t ld, int64_t* argmax, float* pv, int32_t* pi, uint16_t* xp,
-                         hipStream_t stream) {
+                         hipStream_t stream, Marks* marks) {
   const int64_t n_items = logits_items(n_pad);
   const bool vec = (ld % 4) == 0 && ((uintptr_t)logits % 8) == 0;
   const int64_t xchunks = (int64_t)logits_xperm_bytes(M, K) / 16;
@@ -196,11 +196,13 @@ hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t
   if (e0 != hipSuccess) return e0;
   const unsigned grid = (unsigned)((n_items + LG_WAVES - 1) / LG_WAVES);
   for (int32_t m0 = 0; m0 < M; m0 += 16) {
-    timer_begin(kTimerLogits, stream);
+    hipError_t e = mark_begin(marks, kMarkLogits, stream);
+    if (e != hipSuccess) return e;
     logits_kernel<<<grid, 64 * LG_WAVES, 0, stream>>>(xp, M, K, w, n_valid, n_pad, logits, ld, vec, pv, pi, n_items,
                                                       m0);
-    timer_end(kTimerLogits, stream);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = mark_end(marks, kMarkLogits, stream);
     if (e != hipSuccess) return e;
   }
   argmax_final_kernel<<<M, 256, 0, stream>>>(pv, pi, n_items, M, argmax);
