@@ -165,7 +165,10 @@ int had_r_128(const uint16_t *in, uint16_t *out, int64_t rows, int64_t cols, con
  *   n_pad = logits_padded_width(n_valid, w_rows);
  *   logits[m * ld_logits + n] = fp16(sum_k x[m][k] * w[n][k])  for n < n_valid
  *   logits[m * ld_logits + n] = -inf (0xFC00)                  for n_valid <= n < n_pad
- *   argmax[m] = the smallest n whose fp16 logit equals the row maximum.
+ *   argmax[m] = the smallest n whose fp16 logit equals the row maximum, with
+ *               NumPy's and torch's NaN rule: a NaN ranks above every number,
+ *               so the first NaN wins; -0 equals +0. The pad columns come
+ *               after every decodable one, so argmax[m] < n_valid always.
  * x: M x K row-major fp16; w: w_rows x K row-major fp16 (only rows < n_pad are
  * read; the GEMM runs over whole 128-row tiles up to n_pad); fp32 accumulation.
  * The GEMM and the mask are one call: there is no way to obtain padded logits
@@ -179,7 +182,7 @@ int logits_pad_mask_argmax(const uint16_t *x, int64_t M, int32_t K, const uint16
  * [P1046 Summary]. Pure host function. */
 int64_t logits_padded_width(int64_t n_valid, int64_t w_rows);
 
-/* Scratch needed by logits_pad_mask_argmax: per-wave (max, index) pairs and a
+/* Scratch needed by logits_pad_mask_argmax: per-wave (key, index) pairs and a
  * copy of x in MFMA fragment order. 0 for invalid arguments. Pure host
  * function. */
 size_t logits_scratch_bytes(int64_t M, int32_t K, int64_t n_valid, int64_t w_rows);
@@ -192,7 +195,8 @@ size_t logits_scratch_bytes(int64_t M, int32_t K, int64_t n_valid, int64_t w_row
  *   n_pad = min(round_up(n_valid, 128), N)   (logits_padded_width(n_valid, N))
  *   logits[m * ld_logits + n] = exl3_linear(layer, x)[m][n]   for n < n_valid
  *   logits[m * ld_logits + n] = -inf (0xFC00)                 for n_valid <= n < n_pad
- *   argmax[m] = the smallest n whose fp16 logit equals the row maximum.
+ *   argmax[m] = the smallest n whose fp16 logit equals the row maximum (the
+ *               NaN rule of logits_pad_mask_argmax; argmax[m] < n_valid).
  * Only the layer's first n_pad columns are computed (the output rotation
  * mixes columns inside 128-column blocks only, so they equal the full layer's
  * first n_pad columns); columns n_pad .. ld_logits - 1 of logits are left
@@ -209,7 +213,7 @@ int exl3_head_logits_argmax(const exl3_layer *layer, const uint16_t *x, int64_t 
 
 /* Scratch needed by exl3_head_logits_argmax: exl3_linear's scratch for the
  * first n_pad columns (enough for a layer of any width 1..8), then one
- * (fp32 maximum, int32 index) pair per row and 4096-column piece of the
+ * (int32 order key, int32 index) pair per row and 4096-column piece of the
  * argmax. Pure host function; 0 for invalid arguments or M = 0. */
 size_t exl3_head_scratch_bytes(int32_t K, int32_t N, int64_t M, int64_t n_valid, int32_t prefill_min_m);
 

@@ -259,14 +259,19 @@ int64_t oracle_padded_width(int64_t n_valid, int64_t w_rows) {
 /* Pad mask and greedy selection over one row of n_pad fp16 logits whose first
  * n_valid entries are set [P1046 review follow-ups: every pad column is -inf
  * before selection]: entries n_valid .. n_pad - 1 become -inf, and the result
- * is the smallest n whose value equals the row maximum (IEEE comparison). */
+ * is the smallest n whose value equals the row maximum (IEEE comparison, so
+ * -0 equals +0). The pages do not say how a NaN logit is ranked; this follows
+ * NumPy's and torch's argmax, where a NaN is the maximum and the first NaN
+ * wins. */
 static int64_t mask_and_select(uint16_t *row, int64_t n_valid, int64_t n_pad, const double *tab) {
   for (int64_t n = n_valid; n < n_pad; ++n) row[n] = 0xFC00; /* -inf */
+  /* The first index of the largest value, where a NaN counts as larger than
+   * every number (so the first NaN is selected): NumPy's and torch's argmax. */
   int64_t best = 0;
   double bv = tab[row[0]];
-  for (int64_t n = 1; n < n_pad; ++n) {
+  for (int64_t n = 1; n < n_pad && !isnan(bv); ++n) {
     double v = tab[row[n]];
-    if (v > bv) {
+    if (isnan(v) || v > bv) {
       bv = v;
       best = n;
     }
@@ -279,7 +284,8 @@ static int64_t mask_and_select(uint16_t *row, int64_t n_valid, int64_t n_pad, co
  *   logits[i, n] = -inf                                 for n_valid <= n < n_pad
  * Rows of w at or beyond n_valid are never read: their values cannot reach the
  * result. argmax[i] is the smallest n whose fp16 logit equals the row maximum
- * (IEEE comparison). logits is n_rows x n_pad. */
+ * (IEEE comparison; a NaN counts as the maximum, the first NaN wins). logits
+ * is n_rows x n_pad. */
 void oracle_logits(const uint16_t *x, int64_t M, const int64_t *rows, int64_t n_rows,
                    const uint16_t *w, int64_t w_rows, int64_t K, int64_t n_valid, uint16_t *logits,
                    int64_t *argmax) {

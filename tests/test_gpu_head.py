@@ -122,6 +122,28 @@ def test_head_leading_columns_equal_linear(T, X, cb):
     assert np.all(lg[:, n_valid:] == 0xFC00)
 
 
+@pytest.mark.parametrize("pm", [0, 1])
+def test_head_nan_rule(T, X, cb, pm):
+    """NaN logits in the head on both paths: a NaN column scale makes its
+    whole rotation block NaN, a NaN row of x its whole output; the first NaN
+    wins (NumPy's and torch's argmax) and a pad column is never selected.
+    Same inputs as the oracle's pin."""
+    H.announce("head NaN rule pm=%d" % pm)
+    L = WL.layer(31, 128, 512)
+    L = dict(L, scale=L["scale"].copy())
+    L["scale"][300] = 0x7E00
+    x = WL.activations(31, 3, 128).copy()
+    x[1] = 0x7E00
+    for extra in (None, 5):
+        if extra is not None:
+            L["scale"][extra] = 0x7E00
+        _, ref_am = O.head_logits(x, L, cb, 400)
+        lg, am = run_head(T, X, x, X.Layer.from_numpy(L, cb), 400, 3, 512, pm)
+        assert np.array_equal(am, ref_am), (am, ref_am)
+        assert np.array_equal(am, np.argmax(H.val(lg), axis=1))
+        assert np.all(lg[:, 400:] == 0xFC00)
+
+
 def test_head_empty_batch_is_a_no_op(T, X, cb):
     H.announce("head M=0")
     K, N = 256, 512

@@ -320,6 +320,23 @@ def test_logits_planted_pad_row_nan_poison_and_ties(T, X):
         assert am2[i] == np.min(np.nonzero(v[i] == v[i].max())[0])
 
 
+def test_logits_nan_rule(T, X):
+    """NaN logits: the first NaN wins (NumPy's and torch's argmax), also over
+    +inf; a row whose decodable logits are all NaN selects column 0, never a
+    pad column. Same inputs as the oracle's pin."""
+    from tests.test_oracle_logits import nan_logits_case
+
+    H.announce("logits NaN rule")
+    x, w = nan_logits_case()
+    for wv in (w, np.concatenate([np.full((1, w.shape[1]), 0x7E00, np.uint16), w[1:]]),
+               np.concatenate([np.full((300, w.shape[1]), 0x7E00, np.uint16), w[300:]])):
+        lg, am = run_logits(X, x, wv, 300)
+        _, ref_am = O.logits(x, wv, 300)
+        assert np.array_equal(am, ref_am), (am, ref_am)
+        assert np.array_equal(am, np.argmax(H.val(lg), axis=1))
+        assert np.all(am < 300) and np.all(lg[:, 300:] == 0xFC00)
+
+
 def test_logits_aligned_width_mask_is_noop(T, X):
     H.announce("logits aligned width")
     r = np.random.default_rng(6)

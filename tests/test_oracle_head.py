@@ -109,3 +109,23 @@ def test_head_rejects_bad_widths():
         O.head_logits(x, L, WL.codebook(), 0)
     with pytest.raises(ValueError):
         O.head_logits(x, L, WL.codebook(), N + 1)
+
+
+def test_nan_head_logits_follow_numpy_argmax():
+    """A NaN column scale makes the whole 128-column rotation block NaN in
+    every row; a NaN row of x makes its whole output NaN. The first NaN
+    wins (NumPy's and torch's argmax); pads are never selected."""
+    cb = WL.codebook()
+    L = WL.layer(31, 128, 512)
+    L = dict(L, scale=L["scale"].copy())
+    L["scale"][300] = 0x7E00           # block 2 (columns 256..383) NaN
+    x = WL.activations(31, 3, 128).copy()
+    x[1] = 0x7E00
+    lg, am = O.head_logits(x, L, cb, 400)   # n_pad = 512
+    v = val(lg)
+    assert np.all(np.isnan(v[:, 256:384])) and np.all(np.isnan(v[1, :400]))
+    assert np.array_equal(am, np.argmax(v, axis=1))
+    assert list(am) == [256, 0, 256]
+    L["scale"][5] = 0x7E00             # block 0 NaN as well: column 0 first
+    lg, am = O.head_logits(x, L, cb, 400)
+    assert np.all(am == 0) and np.all(lg[:, 400:] == 0xFC00)

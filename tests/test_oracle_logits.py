@@ -76,3 +76,35 @@ def test_ties_resolve_to_lowest_index():
     for i in range(2):
         m = np.max(val(lg2[i]))
         assert am2[i] == np.min(np.nonzero(val(lg2[i]) == m)[0])
+
+
+def nan_logits_case():
+    """Inputs whose logits hold NaNs: a NaN weight row makes its column NaN in
+    every row of x, a NaN row of x makes every logit of that row NaN, and a
+    huge weight row overflows one logit to +inf (a NaN must still beat it)."""
+    x, w = _case(4, 4, 64, 400, 300)   # n_pad = 384
+    x, w = x.copy(), w.copy()
+    w[137] = 0x7E00                    # column 137: NaN everywhere
+    w[50] = f16(np.sign(val(x[0])) * 60000.0)  # row 0, column 50: +inf
+    x[2] = 0x7E00                      # row 2: every logit NaN
+    return x, w
+
+
+def test_nan_logits_follow_numpy_argmax():
+    """NaN rule (NumPy's and torch's argmax): a NaN ranks above every number
+    and the first NaN wins; selection never reaches the pad columns."""
+    x, w = nan_logits_case()
+    lg, am = O.logits(x, w, 300)
+    v = val(lg)
+    assert np.isinf(v[0, 50]) and v[0, 50] > 0
+    assert np.all(np.isnan(v[:, 137])) and np.all(np.isnan(v[2, :300]))
+    assert np.array_equal(am, np.argmax(v, axis=1))
+    assert list(am) == [137, 137, 0, 137]
+    w0 = w.copy()
+    w0[0] = 0x7E00                     # a NaN in column 0 wins at once
+    lg0, am0 = O.logits(x, w0, 300)
+    assert np.array_equal(am0, np.argmax(val(lg0), axis=1)) and np.all(am0 == 0)
+    wall = w.copy()
+    wall[:300] = 0x7E00                # every decodable logit NaN: still column 0, never a pad
+    lga, ama = O.logits(x, wall, 300)
+    assert np.all(ama == 0) and np.all(lga[:, 300:] == 0xFC00)

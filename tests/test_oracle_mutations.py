@@ -40,7 +40,9 @@ MUTATIONS = [
     ("xr_not_rounded", "xh[k] = tab[d2h(xh[k])];", "xh[k] = xh[k];"),
     ("yr_not_rounded", "yh[n] = tab[d2h(acc[n])];", "yh[n] = acc[n];"),
     ("pad_not_masked", "row[n] = 0xFC00; /* -inf */", "row[n] = 0x0000; /* -inf */"),
-    ("argmax_last_maximum", "if (v > bv) {", "if (v >= bv) {"),
+    ("argmax_last_maximum", "if (isnan(v) || v > bv) {", "if (isnan(v) || v >= bv) {"),
+    ("argmax_nan_never_selected", "if (isnan(v) || v > bv) {", "if (v > bv) {"),
+    ("argmax_last_nan_wins", "n < n_pad && !isnan(bv); ++n", "n < n_pad; ++n"),
     ("width_multiple_of_64", "(n_valid + 127) / 128 * 128", "(n_valid + 63) / 64 * 64"),
     ("head_row_stride", "memcpy(logits + i * n_pad, y + i * N,", "memcpy(logits + i * n_pad, y + i * n_pad,"),
     ("head_tail_columns", "y + i * N, (size_t)n_pad", "y + i * N + (N - n_pad), (size_t)n_pad"),

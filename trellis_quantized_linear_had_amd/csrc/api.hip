@@ -39,14 +39,14 @@ hipError_t launch_decode_finalize(const float* partials, int32_t ks_count, const
                                   const uint16_t* sign_n, uint16_t* y, int64_t ldy, int32_t M, int32_t N,
                                   hipStream_t stream);
 hipError_t launch_head_mask_argmax(uint16_t* logits, int64_t ld, int64_t M, int64_t n_valid, int64_t n_pad,
-                                   int64_t* argmax, float* pv, int32_t* pi, hipStream_t stream);
+                                   int64_t* argmax, int32_t* pk, int32_t* pi, hipStream_t stream);
 int64_t head_argmax_items(int64_t n_pad);
 hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
                            int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream,
                            Marks* marks);
 size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K);
 hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int64_t n_valid, int64_t n_pad,
-                         uint16_t* logits, int64_t ld, int64_t* argmax, float* pv, int32_t* pi, uint16_t* xp,
+                         uint16_t* logits, int64_t ld, int64_t* argmax, int32_t* pk, int32_t* pi, uint16_t* xp,
                          hipStream_t stream, Marks* marks);
 int64_t logits_items(int64_t n_pad);
 size_t logits_xperm_bytes(int64_t M, int32_t K);
@@ -365,17 +365,17 @@ int64_t head_padded_width(int64_t n_valid, int64_t n) {
 }
 
 // The linear's scratch over the first n_pad columns, then the per-piece
-// (max, index) pairs of the argmax: floats, then int32s.
+// (order key, index) pairs of the argmax: two int32 arrays.
 struct HeadLayout {
-  size_t pv_off, pi_off, total;
+  size_t pk_off, pi_off, total;
 };
 
 HeadLayout head_layout(int32_t K, int32_t N, int64_t M, int64_t n_valid, int32_t prefill_min_m) {
   const int64_t n_pad = head_padded_width(n_valid, N);
   const size_t pairs = (size_t)M * head_argmax_items(n_pad);
   HeadLayout h;
-  h.pv_off = align256(linear_cols_scratch_bytes(K, (int32_t)n_pad, M, prefill_min_m));
-  h.pi_off = h.pv_off + align256(pairs * sizeof(float));
+  h.pk_off = align256(linear_cols_scratch_bytes(K, (int32_t)n_pad, M, prefill_min_m));
+  h.pi_off = h.pk_off + align256(pairs * sizeof(int32_t));
   h.total = h.pi_off + align256(pairs * sizeof(int32_t));
   return h;
 }
@@ -421,10 +421,10 @@ int logits_entry(const uint16_t* x, int64_t M, int32_t K, const uint16_t* w, int
   int st = check_device();
   if (st) return st;
   const int64_t items = logits_items(n_pad);
-  float* pv = (float*)scratch;
+  int32_t* pk = (int32_t*)scratch;
   int32_t* pi = (int32_t*)((char*)scratch + align256((size_t)items * M * 4));
   uint16_t* xp = (uint16_t*)((char*)scratch + align256((size_t)items * M * 4) * 2);
-  EXL3_TRY(launch_logits(x, (int32_t)M, K, w, n_valid, n_pad, logits, ld_logits, argmax, pv, pi, xp, stream, marks),
+  EXL3_TRY(launch_logits(x, (int32_t)M, K, w, n_valid, n_pad, logits, ld_logits, argmax, pk, pi, xp, stream, marks),
            "logits");
   return EXL3_OK;
 }
@@ -452,7 +452,7 @@ int head_entry(const exl3_layer* L, const uint16_t* x, int64_t M, int64_t n_vali
   const HeadLayout h = head_layout(L->K, L->N, M, n_valid, prefill_min_m);
   st = linear_cols(L, x, M, logits, ld_logits, (int32_t)n_pad, sb, prefill_min_m, stream, marks);
   if (st) return st;
-  EXL3_TRY(launch_head_mask_argmax(logits, ld_logits, M, n_valid, n_pad, argmax, (float*)(sb + h.pv_off),
+  EXL3_TRY(launch_head_mask_argmax(logits, ld_logits, M, n_valid, n_pad, argmax, (int32_t*)(sb + h.pk_off),
                                    (int32_t*)(sb + h.pi_off), stream),
            "mask and argmax");
   return EXL3_OK;

@@ -98,4 +98,24 @@ __device__ __forceinline__ void wht128_16(float (&v)[8], int q) {
   for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(s8, v[j], lane_xor8(v[j]));
 }
 
+// Order key of an fp16 logit for the argmax, which follows NumPy's and
+// torch's rule: a NaN ranks above every number (all NaNs tie, so the first
+// NaN wins), -0 ties with +0, and otherwise keys follow the values. Integer
+// compares on these keys replace float compares, which would never select a
+// NaN.
+#define EXL3_KEY_NONE (-0x7FFFFFFF - 1)  // below every key: no candidate yet
+__device__ __forceinline__ int argmax_key(uint16_t h) {
+  const int mag = h & 0x7FFF;
+  if (mag > 0x7C00) return 0x7C01;
+  return (h & 0x8000) ? -mag : mag;
+}
+
+// (largest key, smallest index): any combination order gives the same pair.
+__device__ __forceinline__ void argmax_combine(int& bk, int& bi, int k, int i) {
+  if (k > bk || (k == bk && i < bi)) {
+    bk = k;
+    bi = i;
+  }
+}
+
 }  // namespace exl3

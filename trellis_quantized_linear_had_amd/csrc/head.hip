@@ -8,17 +8,8 @@
 
 namespace exl3 {
 
-hipError_t launch_argmax_final(const float* pv, const int32_t* pi, int64_t n_items, int64_t M, int64_t* out,
+hipError_t launch_argmax_final(const int32_t* pk, const int32_t* pi, int64_t n_items, int64_t M, int64_t* out,
                                hipStream_t stream);
-
-// (largest value, smallest index): the same order as the logits projection's
-// argmax, so any combination order gives the same pair.
-__device__ __forceinline__ void head_argmax_combine(float& bv, int& bi, float v, int i) {
-  if (v > bv || (v == bv && i < bi)) {
-    bv = v;
-    bi = i;
-  }
-}
 
 // Pad mask and argmax over logits that another kernel has already written
 // (the quantized head: the layer's first n_pad columns), in two stages like
@@ -32,13 +23,13 @@ __device__ __forceinline__ void head_argmax_combine(float& bv, int& bi, float v,
 #define MA_COLS (MA_THREADS * 16)
 __global__ __launch_bounds__(MA_THREADS) void head_mask_argmax_kernel(uint16_t* __restrict__ logits, int64_t ld,
                                                                       int64_t n_valid, int64_t n_pad,
-                                                                      int64_t n_items, float* __restrict__ pv,
+                                                                      int64_t n_items, int32_t* __restrict__ pk,
                                                                       int32_t* __restrict__ pi) {
-  __shared__ float sv[MA_THREADS / 64];
+  __shared__ int sv[MA_THREADS / 64];
   __shared__ int si[MA_THREADS / 64];
   const int64_t q = blockIdx.x / n_items, item = blockIdx.x % n_items;
   uint16_t* row = logits + q * ld;
-  float best = -__builtin_inff();
+  int best = EXL3_KEY_NONE;
   int besti = 0x7FFFFFFF;
   u32x4 v[2];
   int64_t c[2];
@@ -62,14 +53,14 @@ __global__ __launch_bounds__(MA_THREADS) void head_mask_argmax_kernel(uint16_t* 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint16_t e = (uint16_t)(v[h][j >> 1] >> (16 * (j & 1)));
-      head_argmax_combine(best, besti, (float)__builtin_bit_cast(f16, e), (int)(c[h] + j));
+      argmax_combine(best, besti, argmax_key(e), (int)(c[h] + j));
     }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    const float ov = __shfl_xor(best, off);
+    const int ov = __shfl_xor(best, off);
     const int oi = __shfl_xor(besti, off);
-    head_argmax_combine(best, besti, ov, oi);
+    argmax_combine(best, besti, ov, oi);
   }
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
@@ -78,8 +69,8 @@ __global__ __launch_bounds__(MA_THREADS) void head_mask_argmax_kernel(uint16_t* 
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < MA_THREADS / 64; ++w) head_argmax_combine(best, besti, sv[w], si[w]);
-    pv[q * n_items + item] = best;
+    for (int w = 1; w < MA_THREADS / 64; ++w) argmax_combine(best, besti, sv[w], si[w]);
+    pk[q * n_items + item] = best;
     pi[q * n_items + item] = besti;
   }
 }
@@ -87,17 +78,17 @@ __global__ __launch_bounds__(MA_THREADS) void head_mask_argmax_kernel(uint16_t* 
 int64_t head_argmax_items(int64_t n_pad) { return (n_pad + MA_COLS - 1) / MA_COLS; }
 
 hipError_t launch_head_mask_argmax(uint16_t* logits, int64_t ld, int64_t M, int64_t n_valid, int64_t n_pad,
-                                   int64_t* argmax, float* pv, int32_t* pi, hipStream_t stream) {
+                                   int64_t* argmax, int32_t* pk, int32_t* pi, hipStream_t stream) {
   const int64_t n_items = head_argmax_items(n_pad);
   // rows per launch keep every grid well below 2^32 work-items
   const int64_t rows = std::max<int64_t>(1, ((int64_t)1 << 22) / n_items);
   for (int64_t m0 = 0; m0 < M; m0 += rows) {
     const int64_t mr = std::min(rows, M - m0);
     head_mask_argmax_kernel<<<(unsigned)(mr * n_items), MA_THREADS, 0, stream>>>(
-        logits + m0 * ld, ld, n_valid, n_pad, n_items, pv + m0 * n_items, pi + m0 * n_items);
+        logits + m0 * ld, ld, n_valid, n_pad, n_items, pk + m0 * n_items, pi + m0 * n_items);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_argmax_final(pv + m0 * n_items, pi + m0 * n_items, n_items, mr, argmax + m0, stream);
+    e = launch_argmax_final(pk + m0 * n_items, pi + m0 * n_items, n_items, mr, argmax + m0, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -27,13 +27,6 @@ namespace exl3 {
 #define LG_KC 64                // k per chunk
 #define LG_STEPS (LG_KC / 32)
 
-__device__ __forceinline__ void argmax_combine(float& bv, int& bi, float v, int i) {
-  if (v > bv || (v == bv && i < bi)) {
-    bv = v;
-    bi = i;
-  }
-}
-
 // x (M x K) -> xp[mg][j][g][q][0..8) = x[16 mg + q][32 j + 8 g + 0..8], zero
 // for rows past M: the B fragment of lane (g, q) at k-step j, for row group
 // mg, is 16 contiguous bytes and a wave's 64 fragments are 1 KiB.
@@ -75,7 +68,7 @@ __device__ __forceinline__ void logits_mfma_chunk(const u32x4 (&av)[LG_TILES][LG
 __global__ __launch_bounds__(64 * LG_WAVES) void logits_kernel(const uint16_t* __restrict__ xp, int32_t M, int32_t K,
                                                                const uint16_t* __restrict__ w, int64_t n_valid,
                                                                int64_t n_pad, uint16_t* __restrict__ logits,
-                                                               int64_t ld, bool vec_store, float* __restrict__ pv,
+                                                               int64_t ld, bool vec_store, int32_t* __restrict__ pk,
                                                                int32_t* __restrict__ pi, int64_t n_items, int32_t m0) {
   const int64_t item = (int64_t)blockIdx.x * LG_WAVES + (threadIdx.x >> 6);
   if (item >= n_items) return;  // whole wave; no workgroup barriers below
@@ -112,9 +105,9 @@ __global__ __launch_bounds__(64 * LG_WAVES) void logits_kernel(const uint16_t* _
   }
 
   // Epilogue: lane holds D[p = p0 + 16t + 4g + r][q]; round to fp16, mask the
-  // pad columns, store, and keep the first maximum.
+  // pad columns, store, and keep the first maximum (argmax_key order).
   const bool qok = q < M;
-  float best = -__builtin_inff();
+  int best = EXL3_KEY_NONE;
   int besti = 0x7FFFFFFF;
 #pragma unroll
   for (int t = 0; t < LG_TILES; ++t) {
@@ -125,7 +118,7 @@ __global__ __launch_bounds__(64 * LG_WAVES) void logits_kernel(const uint16_t* _
       const int64_t p = pb + r;
       const f16 v = (f16)acc[t][r];
       h[r] = (p < n_valid) ? __builtin_bit_cast(uint16_t, v) : (uint16_t)0xFC00;
-      if (p < n_pad) argmax_combine(best, besti, (float)__builtin_bit_cast(f16, h[r]), (int)p);
+      if (p < n_pad) argmax_combine(best, besti, argmax_key(h[r]), (int)p);
     }
     if (qok) {
       uint16_t* dst = logits + (int64_t)q * ld + pb;
@@ -142,26 +135,26 @@ __global__ __launch_bounds__(64 * LG_WAVES) void logits_kernel(const uint16_t* _
   // lanes pl, pl+16, pl+32, pl+48 hold the same output row q
 #pragma unroll
   for (int o = 16; o <= 32; o <<= 1) {
-    const float v2 = __shfl_xor(best, o);
+    const int v2 = __shfl_xor(best, o);
     const int i2 = __shfl_xor(besti, o);
     argmax_combine(best, besti, v2, i2);
   }
   if (g == 0 && qok) {  // pairs stored [q][item]: the final pass reads each row contiguously
-    pv[(int64_t)q * n_items + item] = best;
+    pk[(int64_t)q * n_items + item] = best;
     pi[(int64_t)q * n_items + item] = besti;
   }
 }
 
-// argmax[q] over the per-wave (max, first index) pairs; any combination order
-// gives the same (largest value, smallest index) pair.
-__global__ __launch_bounds__(256) void argmax_final_kernel(const float* __restrict__ pv, const int32_t* __restrict__ pi,
+// argmax[q] over the per-wave (key, first index) pairs; any combination order
+// gives the same (largest key, smallest index) pair.
+__global__ __launch_bounds__(256) void argmax_final_kernel(const int32_t* __restrict__ pk, const int32_t* __restrict__ pi,
                                                            int64_t n_items, int32_t M, int64_t* __restrict__ out) {
-  __shared__ float sv[256];
+  __shared__ int sv[256];
   __shared__ int si[256];
   const int q = blockIdx.x;
-  float best = -__builtin_inff();
+  int best = EXL3_KEY_NONE;
   int besti = 0x7FFFFFFF;
-  const float* rv = pv + (int64_t)q * n_items;
+  const int32_t* rv = pk + (int64_t)q * n_items;
   const int32_t* ri = pi + (int64_t)q * n_items;
   for (int64_t it = threadIdx.x; it < n_items; it += 256) argmax_combine(best, besti, rv[it], ri[it]);
   sv[threadIdx.x] = best;
@@ -169,7 +162,7 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const float* __restri
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
     if ((int)threadIdx.x < s) {
-      float b = sv[threadIdx.x];
+      int b = sv[threadIdx.x];
       int bi = si[threadIdx.x];
       argmax_combine(b, bi, sv[threadIdx.x + s], si[threadIdx.x + s]);
       sv[threadIdx.x] = b;
@@ -186,7 +179,7 @@ int64_t logits_items(int64_t n_pad) { return (n_pad + LG_ROWS - 1) / LG_ROWS; }
 size_t logits_xperm_bytes(int64_t M, int32_t K) { return (size_t)((M + 15) / 16) * 16 * K * 2; }
 
 hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int64_t n_valid, int64_t n_pad,
-                         uint16_t* logits, int64_t ld, int64_t* argmax, float* pv, int32_t* pi, uint16_t* xp,
+                         uint16_t* logits, int64_t ld, int64_t* argmax, int32_t* pk, int32_t* pi, uint16_t* xp,
                          hipStream_t stream, Marks* marks) {
   const int64_t n_items = logits_items(n_pad);
   const bool vec = (ld % 4) == 0 && ((uintptr_t)logits % 8) == 0;
@@ -198,22 +191,22 @@ hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t
   for (int32_t m0 = 0; m0 < M; m0 += 16) {
     hipError_t e = mark_begin(marks, kMarkLogits, stream);
     if (e != hipSuccess) return e;
-    logits_kernel<<<grid, 64 * LG_WAVES, 0, stream>>>(xp, M, K, w, n_valid, n_pad, logits, ld, vec, pv, pi, n_items,
+    logits_kernel<<<grid, 64 * LG_WAVES, 0, stream>>>(xp, M, K, w, n_valid, n_pad, logits, ld, vec, pk, pi, n_items,
                                                       m0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = mark_end(marks, kMarkLogits, stream);
     if (e != hipSuccess) return e;
   }
-  argmax_final_kernel<<<M, 256, 0, stream>>>(pv, pi, n_items, M, argmax);
+  argmax_final_kernel<<<M, 256, 0, stream>>>(pk, pi, n_items, M, argmax);
   return hipGetLastError();
 }
 
 // The second argmax stage on its own, for callers with their own first stage
 // (the quantized head's pad mask pass).
-hipError_t launch_argmax_final(const float* pv, const int32_t* pi, int64_t n_items, int64_t M, int64_t* out,
+hipError_t launch_argmax_final(const int32_t* pk, const int32_t* pi, int64_t n_items, int64_t M, int64_t* out,
                                hipStream_t stream) {
-  argmax_final_kernel<<<(unsigned)M, 256, 0, stream>>>(pv, pi, n_items, (int32_t)M, out);
+  argmax_final_kernel<<<(unsigned)M, 256, 0, stream>>>(pk, pi, n_items, (int32_t)M, out);
   return hipGetLastError();
 }
 
