@@ -89,17 +89,45 @@ __device__ __forceinline__ void load_rows_lds(const uint16_t* __restrict__ g, in
 // issued through inline assembly so that the compiler does not track it: its
 // waits cannot count register loads and the direct-to-LDS loads of A in one
 // sequence and would fall back to waiting for all of them (vmcnt(0)) at the
-// top of every k step. The kernel waits for these loads itself, and every
-// wait also guards the registers: the compiler takes the destination as
-// written at issue, so a slot's previous load must have landed before the
-// slot is read or its registers are reused (for the refill's address), and
-// all of them before the registers outlive the k loop. The counts rely on
-// vector memory loads returning in issue order, direct-to-LDS loads
+// top of every k step. The kernel waits for these loads itself (wait_slot),
+// with counts derived below from the loads each k step issues; the counts
+// rely on vector memory loads returning in issue order, direct-to-LDS loads
 // included.
 __device__ __forceinline__ f16x8 load_frag(const uint16_t* p) {
   f16x8 v;
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
   return v;
+}
+
+// Vector-memory loads one wave issues per k step, in issue order: B slots 0,
+// 1 and 2 (G_QT fragments each), the 4 direct-to-LDS loads of the next A
+// stage (32 rows per wave, 8 rows per instruction), B slot 3.
+constexpr int kBLoads = G_QT;
+constexpr int kALoads = 4;
+constexpr int kLoadsPerStep = 4 * kBLoads + kALoads;
+// Before the MFMAs of sub-step s (s = 0, 1, 2) slot s must have landed. Issued
+// after it: slots s+1..2 of this k step, the A stage, slot 3, and the refills
+// of slots 0..s-1 issued in this k step -- the same count for every s.
+constexpr int wait_slot_count(int s) { return (2 - s) * kBLoads + kALoads + kBLoads + s * kBLoads; }
+constexpr int kWaitSlot = wait_slot_count(0);
+static_assert(wait_slot_count(1) == kWaitSlot && wait_slot_count(2) == kWaitSlot, "slot waits differ");
+// Before the barrier: slot 3 and the A stage (issued before it) have landed
+// once only the three refills issued since are outstanding.
+constexpr int kWaitStage = 3 * kBLoads;
+// Prologue, issued in steady-state order (A stage 0, slots 0..2, A stage 1,
+// slot 3): A stage 0 has landed once the loads after it are outstanding.
+constexpr int kWaitPrologue = kLoadsPerStep;
+static_assert(kWaitPrologue < 64 && kWaitSlot < kLoadsPerStep && kWaitStage < kWaitSlot,
+              "vmcnt counts out of range (6 bits)");
+
+// Waits until at most N vector-memory loads are outstanding. The slot's
+// registers are named as read and written by the wait, so the compiler can
+// neither move the MFMAs that read them above it nor reuse them while their
+// load may still be in flight.
+template <int N>
+__device__ __forceinline__ void wait_slot(f16x8 (&slot)[G_QT]) {
+  static_assert(G_QT == 2, "one operand per fragment of the slot");
+  asm volatile("s_waitcnt vmcnt(%2)" : "+v"(slot[0]), "+v"(slot[1]) : "n"(N) : "memory");
 }
 
 // Output rotation + signs + fp16 store of one 128 (p) x 32 (q) block of a
@@ -326,38 +354,38 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
     for (int sub = 0; sub < 3; ++sub) load_b(kb0, sub);
     issue_loads(1, (kb0 + min(1, nk - 1)) * G_BK);
     load_b(kb0, 3);
-    // stage 0 landed (the 12 loads after it may not have)
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    // stage 0 landed (the loads after it may not have)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitPrologue) : "memory");
     __syncthreads();
     read_frags(0, 0, 0);
     for (int kk = 0; kk < nk; ++kk) {
       const int b = kk & 1;
       const int kn = kb0 + min(kk + 1, nk - 1);  // the k step the B slots are refilled with
-      // Slot s of this k step has landed once at most 10 loads are
-      // outstanding: issued after it are the later slots, the 4 A loads of
-      // stage kk+1 and this k step's refills, 10 in all, for s = 0, 1, 2; the
-      // A loads themselves get the whole k step to land.
-      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      // Slot s of this k step has landed once kWaitSlot loads are
+      // outstanding (the later slots, the A loads of stage kk+1 and this k
+      // step's refills), for s = 0, 1, 2; the A loads themselves get the
+      // whole k step to land.
+      wait_slot<kWaitSlot>(bq[0]);
       read_frags(b, 1, 1);
       mfmas(0, 0);
       load_b(kn, 0);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      wait_slot<kWaitSlot>(bq[1]);
       read_frags(b, 2, 0);
       mfmas(1, 1);
       load_b(kn, 1);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      wait_slot<kWaitSlot>(bq[2]);
       read_frags(b, 3, 1);
       mfmas(0, 2);
       load_b(kn, 2);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
-      // at most the 6 B loads just issued outstanding: slot 3 and this
-      // wave's A loads of stage kk+1 (issued before it) have landed
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      // only the refills just issued outstanding: slot 3 and this wave's A
+      // loads of stage kk+1 (issued before it) have landed
+      wait_slot<kWaitStage>(bq[3]);
       __syncthreads();
       issue_loads(b, (kb0 + min(kk + 2, nk - 1)) * G_BK);
       if (kk + 1 < nk) read_frags(b ^ 1, 0, 0);
@@ -367,7 +395,10 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
     }
     // the last B loads (of the last k step again) must land before their
     // registers are reused: the compiler does not know they are in flight
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_slot<0>(bq[0]);
+    wait_slot<0>(bq[1]);
+    wait_slot<0>(bq[2]);
+    wait_slot<0>(bq[3]);
   };
 
   if (MODE == 0) {
