@@ -18,7 +18,7 @@
  *   [P1046] pegainfer PR #1046, "perf(qwen35): align the logits GEMM width":
  *          Summary (round the decodable width up to a multiple of 128, clamp
  *          by the weight rows), the review follow-ups (pad columns forced to
- *          -inf after every logits GEMM, a no-op when no padding is needed;
+ *          -inf after every logits GEMM, with nothing to do at an aligned width;
  *          GEMM and mask owned by one call so the GEMM is unreachable without
  *          the mask), Testing (248077 -> 248192 inside 248320 rows).
  *

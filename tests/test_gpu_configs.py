@@ -29,11 +29,20 @@ def cb():
     return WL.codebook()
 
 
-def sample_rows(M, k=12):
-    if M <= k:
+def sample_rows(M):
+    """The first and last three rows plus one row in every 64-row block (so
+    every 64-row quarter of every 256-row GEMM tile is compared), at a
+    different offset in each block."""
+    if M <= 12:
         return np.arange(M, dtype=np.int64)
-    mid = np.linspace(3, M - 4, k - 6).astype(np.int64)
-    return np.unique(np.concatenate([[0, 1, 2], mid, [M - 3, M - 2, M - 1]])).astype(np.int64)
+    blocks = [min(64 * b + (37 * b + 11) % 64, M - 1) for b in range((M + 63) // 64)]
+    return np.unique(np.concatenate([[0, 1, 2], blocks, [M - 3, M - 2, M - 1]])).astype(np.int64)
+
+
+def test_sample_rows_cover_every_tile_quarter():
+    for M in (128, 256, 1024, 2048, 4096):
+        r = sample_rows(M)
+        assert set(r // 64) == set(range((M + 63) // 64)) and set(r // 256) == set(range((M + 255) // 256))
 
 
 def gpu_linear(X, lay, x, pm):

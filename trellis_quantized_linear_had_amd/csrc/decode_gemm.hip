@@ -1,6 +1,7 @@
 // Fused trellis decode-GEMM for decode-shaped calls (vLLM PR #316, summary and
-// "Problem": the fused kernel decodes the trellis once per output tile, so its
-// cost grows with the row count; it serves every call below the threshold).
+// "Problem"): each trellis tile is decoded again for every tile of output rows,
+// so this path pays more decode work as M rises and serves the calls below the
+// row threshold.
 //
 // Yr = Xr . W with W decoded on the fly. One workgroup per CU (the 128 KiB
 // codebook fills most of the 160 KiB LDS); the K x N weight grid is cut into
