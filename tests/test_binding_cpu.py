@@ -57,6 +57,7 @@ def test_head_rejects_bad_arguments(layer):
     raises("logits must be", B.head_logits_argmax, x16(2, 256), layer, 300, logits=x16(2, 128))
     raises("argmax has dtype", B.head_logits_argmax, x16(2, 256), layer, 300,
            argmax=torch.zeros(2, dtype=torch.int32))
+    raises("argmax holds", B.head_logits_argmax, x16(2, 256), layer, 300, argmax=torch.zeros(1, dtype=torch.int64))
     raises("must be on a GPU", B.head_logits_argmax, x16(2, 256), layer, 300)
 
 
@@ -65,8 +66,8 @@ def test_logits_rejects_bad_arguments():
     raises("w must be a 2-D", B.logits_pad_mask_argmax, x16(2, 256), torch.zeros(10, dtype=torch.int16), 5)
     raises("columns; the layer takes K = 256", B.logits_pad_mask_argmax, x16(2, 128), w, 257)
     raises("logits has", B.logits_pad_mask_argmax, x16(2, 256), w, 257, logits=x16(2, 257))
-    raises("argmax has shape", B.logits_pad_mask_argmax, x16(2, 256), w, 257,
-           argmax=torch.zeros(3, dtype=torch.int64))
+    raises("argmax holds", B.logits_pad_mask_argmax, x16(2, 256), w, 257,
+           argmax=torch.zeros(1, dtype=torch.int64))
     raises("must be on a GPU", B.logits_pad_mask_argmax, x16(2, 256), w, 257)
 
 

@@ -246,11 +246,11 @@ def head_logits_argmax(x: torch.Tensor, layer: Layer, n_valid: int, prefill_min_
     _require(1 <= n_valid <= layer.N, "n_valid = %d must be in [1, N = %d]" % (n_valid, layer.N))
     n_pad = logits_padded_width(n_valid, layer.N)
     if logits is not None:
-        _require(logits.dim() == 2 and logits.shape[0] == M and logits.shape[1] >= n_pad and logits.stride(1) == 1,
-                 "logits must be M x (>= %d) with unit column stride" % n_pad)
+        _require(logits.dim() == 2 and logits.shape[0] >= M and logits.shape[1] >= n_pad and logits.stride(1) == 1,
+                 "logits must be (>= M) x (>= %d) with unit column stride" % n_pad)
         _require(logits.dtype in _F16, "logits has dtype %s" % logits.dtype)
     if argmax is not None:
-        _tensor(argmax, "argmax", (torch.int64,), shape=(M,))
+        _tensor(argmax, "argmax", (torch.int64,), min_numel=M)
     if scratch is not None:
         _tensor(scratch, "scratch", (torch.uint8, torch.int8))
     _on(layer.device, ("x", x), ("logits", logits), ("argmax", argmax), ("scratch", scratch))
@@ -326,15 +326,15 @@ def logits_pad_mask_argmax(x: torch.Tensor, w: torch.Tensor, n_valid: int, scrat
     n_pad = logits_padded_width(n_valid, w_rows)
     _require(n_pad > 0, "n_valid = %d must be in [1, w_rows = %d]" % (n_valid, w_rows))
     if logits is not None:
-        _require(logits.dim() == 2 and logits.shape[0] == M and logits.stride(1) == 1 and logits.dtype in _F16,
-                 "logits must be an M x (>= n_pad) fp16 or int16 tensor with unit column stride")
+        _require(logits.dim() == 2 and logits.shape[0] >= M and logits.stride(1) == 1 and logits.dtype in _F16,
+                 "logits must be an (>= M) x (>= n_pad) fp16 or int16 tensor with unit column stride")
         if ld_logits is None:
             ld_logits = logits.stride(0)
         _require(ld_logits == logits.stride(0) and logits.shape[1] >= n_pad,
                  "logits has %d columns and row stride %d; ld_logits %s and n_pad %d"
                  % (logits.shape[1], logits.stride(0), ld_logits, n_pad))
     if argmax is not None:
-        _tensor(argmax, "argmax", (torch.int64,), shape=(M,))
+        _tensor(argmax, "argmax", (torch.int64,), min_numel=M)
     if scratch is not None:
         _tensor(scratch, "scratch", (torch.uint8, torch.int8))
     _on(x.device, ("x", x), ("w", w), ("logits", logits), ("argmax", argmax), ("scratch", scratch))
