@@ -82,7 +82,7 @@ def nan_logits_case():
     """Inputs whose logits hold NaNs: a NaN weight row makes its column NaN in
     every row of x, a NaN row of x makes every logit of that row NaN, and a
     huge weight row overflows one logit to +inf (a NaN must still beat it)."""
-    x, w = _case(4, 4, 64, 400, 300)   # n_pad = 384
+    x, w = _case(4, 4, 128, 400, 300)  # n_pad = 384
     x, w = x.copy(), w.copy()
     w[137] = 0x7E00                    # column 137: NaN everywhere
     w[50] = f16(np.sign(val(x[0])) * 60000.0)  # row 0, column 50: +inf
