@@ -132,6 +132,25 @@ typedef struct exl3_layer {
 int exl3_linear(const exl3_layer *layer, const uint16_t *x, int64_t M, uint16_t *y, void *scratch,
                 size_t scratch_bytes, int32_t prefill_min_m, void *stream);
 
+/* exl3_linear for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same dispatch, kernels and results (bit-identical to exl3_linear), with the
+ * scratch held by the library instead of passed in -- a device array of
+ * EXL3_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, kept until the process ends.
+ * It covers every fused-path call below the default threshold at the MLP and
+ * wide geometries (K5120 x N17408, K17408 x N5120, K5120 x N32768: at most
+ * 26.5 MiB at M = 127); a call whose exl3_linear_scratch_bytes exceeds it
+ * returns EXL3_ESCRATCH before any launch. The first call on a device looks
+ * up the array's device address (hipGetSymbolAddress); no call allocates or
+ * frees memory. Every call on one GPU uses that GPU's one array, and the
+ * array keeps what the last call left (no kernel reads scratch it did not
+ * write in the same call): calls that overlap on one GPU -- on different
+ * streams, or from several threads -- race and must be ordered by the
+ * caller. Other arguments, limits and statuses as exl3_linear. */
+#define EXL3_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+int exl3_linear_noalloc(const exl3_layer *layer, const uint16_t *x, int64_t M, uint16_t *y, int32_t prefill_min_m,
+                        void *stream);
+
 /* Scratch needed by exl3_linear for this geometry, row count and threshold
  * (the path is chosen the same way), enough for a layer of any width 1..8.
  * Pure host function. Returns 0 for invalid shapes. */

@@ -6,12 +6,14 @@ from ._lib import (  # noqa: F401
     LAYOUT_KN,
     LAYOUT_NK,
     MAX_CHUNK_COLS,
+    NOALLOC_SCRATCH_BYTES,
     Layer,
     decode_states,
     had_r_128,
     head_logits_argmax,
     head_scratch_bytes,
     linear,
+    linear_noalloc,
     linear_scratch_bytes,
     logits_pad_mask_argmax,
     logits_padded_width,

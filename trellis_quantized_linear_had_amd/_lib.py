@@ -19,11 +19,13 @@ LIB_PATH = os.path.join(_PKG, "libexl3.so")
 EXL3_OK, EXL3_EINVAL, EXL3_ESHAPE, EXL3_ESCRATCH, EXL3_EWIDTH, EXL3_EHIP, EXL3_EARCH = range(7)
 LAYOUT_KN, LAYOUT_NK = 0, 1
 MAX_CHUNK_COLS = 32768
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 DEFAULT_PREFILL_MIN_M = 128
 
 EXPORTS = (
     "exl3_linear",
     "exl3_linear_scratch_bytes",
+    "exl3_linear_noalloc",
     "exl3_head_logits_argmax",
     "exl3_head_scratch_bytes",
     "exl3_reconstruct",
@@ -61,6 +63,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.exl3_linear.argtypes = [ctypes.POINTER(Exl3Layer), vp, i64, vp, vp, sz, i32, vp]
         L.exl3_linear.restype = ctypes.c_int
+        L.exl3_linear_noalloc.argtypes = [ctypes.POINTER(Exl3Layer), vp, i64, vp, i32, vp]
+        L.exl3_linear_noalloc.restype = ctypes.c_int
         L.exl3_linear_scratch_bytes.argtypes = [i32, i32, i64, i32]
         L.exl3_linear_scratch_bytes.restype = sz
         L.exl3_head_logits_argmax.argtypes = [ctypes.POINTER(Exl3Layer), vp, i64, i64, vp, i64, vp, vp, sz, i32, vp]
@@ -232,6 +236,21 @@ def linear(x: torch.Tensor, layer: Layer, prefill_min_m: int = DEFAULT_PREFILL_M
     scratch = _scratch(scratch, linear_scratch_bytes(layer.K, layer.N, M, prefill_min_m), x.device, stream)
     check(lib().exl3_linear(layer.c, _ptr(x), M, _ptr(out), _ptr(scratch), scratch.numel(), prefill_min_m,
                             _stream(stream)))
+    return out
+
+
+def linear_noalloc(x: torch.Tensor, layer: Layer, prefill_min_m: int = DEFAULT_PREFILL_MIN_M, out=None,
+                   stream=None) -> torch.Tensor:
+    """layer(x) through the allocation-free entry point (the library's own
+    per-GPU scratch of NOALLOC_SCRATCH_BYTES; calls on one GPU must not
+    overlap). `out` must be given where nothing may be allocated."""
+    M = _rows_of(x, layer.K)
+    if out is not None:
+        _tensor(out, "out", _F16, shape=(M, layer.N))
+    _on(layer.device, ("x", x), ("out", out))
+    if out is None:
+        out = _empty((M, layer.N), x.dtype, x.device, stream)
+    check(lib().exl3_linear_noalloc(layer.c, _ptr(x), M, _ptr(out), prefill_min_m, _stream(stream)))
     return out
 
 

@@ -340,8 +340,10 @@ int linear_cols(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
 }
 
 // Common call checks of exl3_linear and exl3_head_logits_argmax.
+// own_scratch: the library supplies the scratch (the allocation-free entry
+// point), so the caller's scratch argument is not checked.
 int validate_call(const exl3_layer* L, const uint16_t* x, int64_t M, const void* y, const void* scratch,
-                  int32_t prefill_min_m) {
+                  int32_t prefill_min_m, bool own_scratch = false) {
   int st = validate_layer(L);
   if (st) return st;
   if (M < 0) return fail(EXL3_EINVAL, "M = %lld is negative", (long long)M);
@@ -349,8 +351,8 @@ int validate_call(const exl3_layer* L, const uint16_t* x, int64_t M, const void*
   if (M > 0x7FFFFFFF) return fail(EXL3_EINVAL, "M = %lld is too large", (long long)M);
   if (M == 0) return EXL3_OK;
   if (!x || !y) return fail(EXL3_EINVAL, "x or the output is NULL");
-  if (!scratch) return fail(EXL3_EINVAL, "scratch is NULL");
-  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)scratch & 255u))
+  if (!own_scratch && !scratch) return fail(EXL3_EINVAL, "scratch is NULL");
+  if (!aligned16(x) || !aligned16(y) || (!own_scratch && ((uintptr_t)scratch & 255u)))
     return fail(EXL3_EINVAL, "x and the output must be 16-byte aligned and scratch 256-byte aligned");
   // the prefill GEMM addresses the rotated input (M x K fp16) with 32-bit
   // byte offsets
@@ -378,6 +380,33 @@ HeadLayout head_layout(int32_t K, int32_t N, int64_t M, int64_t n_valid, int32_t
   h.pi_off = h.pk_off + align256(pairs * sizeof(int32_t));
   h.total = h.pi_off + align256(pairs * sizeof(int32_t));
   return h;
+}
+
+// Scratch of exl3_linear_noalloc: a file-scope device array, one copy on each
+// GPU the library runs on, held until the process ends. Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol): the device address comes from hipGetSymbolAddress, once per
+// device with that device current, and is kept per device.
+__device__ __align__(256) unsigned char scratch[EXL3_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[64];  // device address of `scratch` per device index, once resolved
+
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(EXL3_EARCH, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p & 255u)) return fail(EXL3_EHIP, "scratch symbol address %p is not 256-byte aligned", p);
+    g_noalloc_ptr[dev] = p;
+  }
+  *out = g_noalloc_ptr[dev];
+  return EXL3_OK;
 }
 
 }  // namespace
@@ -471,6 +500,23 @@ size_t exl3_linear_scratch_bytes(int32_t K, int32_t N, int64_t M, int32_t prefil
 int exl3_linear(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* scratch, size_t scratch_bytes,
                 int32_t prefill_min_m, void* stream_) {
   return exl3::linear_entry(L, x, M, y, scratch, scratch_bytes, prefill_min_m, (hipStream_t)stream_, nullptr);
+}
+
+int exl3_linear_noalloc(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, int32_t prefill_min_m,
+                        void* stream_) {
+  g_msg[0] = 0;
+  int st = validate_call(L, x, M, y, nullptr, prefill_min_m, true);
+  if (st || M == 0) return st;
+  const size_t need = exl3_linear_scratch_bytes(L->K, L->N, M, prefill_min_m);
+  if (need > (size_t)EXL3_NOALLOC_SCRATCH_BYTES)
+    return fail(EXL3_ESCRATCH, "this call needs %zu bytes of scratch; exl3_linear_noalloc holds %d (use exl3_linear "
+                "with a caller-owned buffer)", need, EXL3_NOALLOC_SCRATCH_BYTES);
+  st = check_device();
+  if (st) return st;
+  void* sb = nullptr;
+  st = noalloc_scratch(&sb);
+  if (st) return st;
+  return linear_cols(L, x, M, y, L->N, L->N, (char*)sb, prefill_min_m, (hipStream_t)stream_, nullptr);
 }
 
 size_t exl3_head_scratch_bytes(int32_t K, int32_t N, int64_t M, int64_t n_valid, int32_t prefill_min_m) {
