@@ -36,12 +36,16 @@ PREFILL_FLOP = 2 * PREFILL_M * K * N    # 365,072,220,160
 RECON_BYTES = K * N // 2 + K * N * 2 + N * 2
 HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
-# Secondary roof of the decode kernels: one random 16-bit codebook read from
-# LDS per weight; a probe measured 8.5 such reads per CU per clock, so 256 CUs
-# at the 2.4 GHz peak clock decode 5.22e12 weights/s = 2611 GB/s of packed
-# 4-bit codes.
-LDS_GATHERS_PER_CU_CLK = 8.5
-LDS_GATHER_ROOF_GBPS = LDS_GATHERS_PER_CU_CLK * 256 * 2.4e9 * 0.5 / 1e9
+# Secondary roof of the trellis kernels: one random 16-bit codebook read from
+# LDS per weight. The gather probe's rate per CU per clock (measured in every
+# run; 11.66 on the last boxes) times 256 CUs at the 2.4 GHz peak clock gives
+# the weights per second, and 0.5 byte of packed 4-bit codes per weight the
+# GB/s (3.58 TB/s at 11.66).
+PEAK_CLOCK_HZ = 2.4e9
+
+
+def lds_gather_roof_gbps(per_cu_clk: float, bits: int = 4) -> float:
+    return per_cu_clk * 256 * PEAK_CLOCK_HZ * bits / 8 / 1e9
 
 
 def parse():
@@ -243,6 +247,8 @@ def main():
     tiles = (N // 256) * (PREFILL_M // 256)       # 544 output tiles of 256 x 256
     full_tiles = tiles // 256 * 256                 # 512 run at full K; the rest are split along K
     gemm_full_flop = 2 * 256 * 256 * K * full_tiles
+    ceil = ceilings(log)
+    gather_roof = lds_gather_roof_gbps(ceil["lds_gather_lookups_per_cu_clk"])
     kernels = {}
     for M in DEC_M:
         us = kern_us["decode_gemm_kernel M=%d" % M]
@@ -250,7 +256,7 @@ def main():
         kernels["decode_gemm_kernel M=%d" % M] = {
             "bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "us": us, "per_launch": "%d B packed codes (K5120 x N17408 x 0.5 B)" % CODE_BYTES,
-            "lds_gather_roof_GBps": LDS_GATHER_ROOF_GBPS, "lds_gather_frac": gbps / LDS_GATHER_ROOF_GBPS}
+            "lds_gather_roof_GBps": gather_roof, "lds_gather_frac": gbps / gather_roof}
     us = kern_us["gemm_had_kernel<0> M=2048"]
     kernels["gemm_had_kernel<0> M=2048"] = {
         "bound": "mfma", "achieved": gemm_full_flop / (us * 1e-6) / 1e12, "peak": MFMA_F16_PEAK_TFLOPS,
@@ -264,7 +270,6 @@ def main():
         kernels["logits_kernel M=16"] = {
             "bound": "hbm", "achieved": logits_bytes / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "us": us, "per_launch": "%d B fp16 weight rows read (248192 x 5120 x 2)" % logits_bytes}
-    ceil = ceilings(log)
     for k, r in kernels.items():
         r["frac"] = r["achieved"] / r["peak"]
         r["traffic"] = stored_traffic(k)
@@ -292,6 +297,38 @@ def main():
     roof["us"] = kernels[dom_key]["us"]
     roof["per_launch"] = kernels[dom_key]["per_launch"]
 
+    # The metric's own paths beside the dominant kernel: the decode call and
+    # its decode-GEMM kernel (packed 4-bit codes against HBM and against the
+    # LDS-gather ceiling), the prefill call (2MKN over the whole call) and its
+    # full-tile GEMM launch.
+    dec_call_gbps = {M: CODE_BYTES / (dec_ms[M] * 1e-3) / 1e9 for M in DEC_M}
+    gk = kernels["gemm_had_kernel<0> M=2048"]
+    metric_roofs = {
+        "decode_call": {
+            "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+            "achieved": {str(M): round(v, 1) for M, v in dec_call_gbps.items()},
+            "frac": {str(M): round(v / HBM_PEAK_GBPS, 4) for M, v in dec_call_gbps.items()},
+            "frac_of_lds_gather_probe": {str(M): round(v / ceil["lds_gather_GBps_4bit_codes"], 4)
+                                         for M, v in dec_call_gbps.items()},
+            "per_call": "%d B packed codes" % CODE_BYTES},
+        "decode_kernel": {
+            "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+            "achieved": {str(M): round(kernels["decode_gemm_kernel M=%d" % M]["achieved"], 1) for M in DEC_M},
+            "frac": {str(M): round(kernels["decode_gemm_kernel M=%d" % M]["achieved"] / HBM_PEAK_GBPS, 4)
+                     for M in DEC_M},
+            "frac_of_lds_gather_probe": {str(M): round(kernels["decode_gemm_kernel M=%d" % M]["achieved"]
+                                                       / ceil["lds_gather_GBps_4bit_codes"], 4) for M in DEC_M}},
+        "prefill_call": {
+            "bound": "mfma", "unit": "TFLOP/s", "peak": MFMA_F16_PEAK_TFLOPS, "achieved": round(pre_tflops, 1),
+            "frac": round(pre_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "frac_of_mfma_probe": round(pre_tflops / ceil["mfma_f16_TFLOPs"], 4),
+            "per_call": "%d FLOP (2 x 2048 x 5120 x 17408), whole call" % PREFILL_FLOP},
+        "prefill_gemm_full_tiles": {
+            "bound": "mfma", "unit": "TFLOP/s", "peak": MFMA_F16_PEAK_TFLOPS, "achieved": round(gk["achieved"], 1),
+            "frac": round(gk["frac"], 4), "frac_of_mfma_probe": round(gk["frac_of_measured_ceiling"], 4),
+            "us": round(gk["us"], 2), "per_launch": gk["per_launch"]},
+    }
+
     result = {
         "metric": "decode GB/s + us/call at M=1..16; prefill TFLOP/s at M=2048, K5120xN17408",
         "value": round(value, 2),
@@ -316,6 +353,7 @@ def main():
         "prefill_tflops": round(pre_tflops, 1),
         "logits_us_per_call": None if log_ms is None else round(log_ms * 1e3, 2),
         "roofline": roof,
+        "metric_rooflines": metric_roofs,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "ceilings": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in ceil.items()},
@@ -653,6 +691,7 @@ def bits_sweep() -> str:
     dev = torch.device("cuda:0")
     sh = torch.cuda.current_stream().cuda_stream
     cb = W.codebook()
+    gather_clk = ceilings()["lds_gather_lookups_per_cu_clk"]
 
     def time_calls(layers, x, M, y, scr, reps):
         def one(i):
@@ -694,7 +733,7 @@ def bits_sweep() -> str:
             scr = torch.empty(X.linear_scratch_bytes(K, N, M), dtype=torch.uint8, device=dev)
             row[M] = time_calls(layers, x, M, y, scr, 24 if M < 128 else 6)
             del x, y, scr
-        roof = LDS_GATHER_ROOF_GBPS * bits / 4  # one gather per weight: bits / 8 bytes of codes
+        roof = lds_gather_roof_gbps(gather_clk, bits)  # one gather per weight: bits / 8 bytes of codes
         dk = row[1][1][_measure.DECODE]
         rk = row[PREFILL_M][1][_measure.RECONSTRUCT]
         rbytes = K * N * bits // 8 + K * N * 2 + N * 2
@@ -726,6 +765,7 @@ def head_sweep() -> str:
     dev = torch.device("cuda:0")
     sh = torch.cuda.current_stream().cuda_stream
     cb = W.codebook()
+    gather_clk = ceilings()["lds_gather_lookups_per_cu_clk"]
     lc = W.LOGITS
     n_valid, rows = lc["n_valid"], lc["w_rows"]
     n_pad = X.logits_padded_width(n_valid, rows)
@@ -749,7 +789,7 @@ def head_sweep() -> str:
     for bits in (4, 6):
         lay = X.Layer.from_numpy(W.layer(lc["seed"], K, rows, 0, bits), cb)
         code_bytes = K * n_pad * bits // 8
-        roof = LDS_GATHER_ROOF_GBPS * bits / 4
+        roof = lds_gather_roof_gbps(gather_clk, bits)
         for M in (1, 4, 16, 64):
             x = _lib.to_device_u16(W.activations(lc["seed"], M, K))
             lg = torch.empty((M, n_pad), dtype=torch.int16, device=dev)
@@ -794,30 +834,84 @@ def head_sweep() -> str:
     return "\n".join(out)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(target_s: float, log):
-    """The plain fp64 oracle timed on the host cores on a bounded sample of
-    the same workload: whole decode calls at M = 16 on the K5120 x N17408
-    layer (every weight decoded once per call), repeated until the target
-    time is reached."""
+    """The plain fp64 oracle, as it stands, timed on the host cores. The
+    headline value: whole decode calls at M = 16 on the K5120 x N17408 layer
+    (every weight decoded once per call), repeated for about target_s
+    seconds. Beside it, one timing per configuration of the workload (decode
+    at each M; both prefill geometries and the wide projection on a labelled
+    subset of 16 of the 2048 rows -- the oracle decodes the whole weight once
+    per call and then computes each listed row; the padded logits at M = 1
+    in full and at M = 16 on 2 of its rows), with the rate on the work
+    actually done."""
     from oracle import oracle as O
 
     cb = W.codebook()
-    L = W.layer(W.SEED_DECODE, K, N, 0)
-    x = W.activations(W.SEED_DECODE, 16, K)
     O.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    per_config = []
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    L = W.layer(W.SEED_DECODE, K, N, 0)
+    x16 = W.activations(W.SEED_DECODE, 16, K)
     calls, t0 = 0, time.perf_counter()
     while True:
-        O.exl3_linear(x, L, cb)
+        O.exl3_linear(x16, L, cb)
         calls += 1
         el = time.perf_counter() - t0
         if el >= target_s or calls >= 50:
             break
     gbps = calls * CODE_BYTES / el / 1e9
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     log("oracle: %d decode calls in %.2f s" % (calls, el))
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+    per_config.append({"config": "decode K5120xN17408 M=16", "rows": "all 16", "seconds": round(el / calls, 3),
+                       "rate": round(gbps, 4), "unit": "GB/s of packed codes"})
+    for M in (1, 4, 8):
+        x = W.activations(W.SEED_DECODE, M, K)
+        sec = timed(lambda: O.exl3_linear(x, L, cb))
+        per_config.append({"config": "decode K5120xN17408 M=%d" % M, "rows": "all %d" % M, "seconds": round(sec, 3),
+                           "rate": round(CODE_BYTES / sec / 1e9, 4), "unit": "GB/s of packed codes"})
+    rows = np.arange(0, 2048, 128, dtype=np.int64)  # 16 of the 2048 rows, one per 128-row block
+    cases = [("prefill K5120xN17408 M=2048", W.PREFILL["seed"], 5120, 17408, (0,)),
+             ("prefill K17408xN5120 M=2048", W.PREFILL["seed"], 17408, 5120, (1,)),
+             ("wide K5120xN32768 M=2048", W.WIDE["seed"], 5120, 32768, ())]
+    for name, seed, k, n, extra in cases:
+        Lc = W.layer(seed, k, n, *extra)
+        x = W.activations(seed, 2048, k, *extra)
+        sec = timed(lambda: O.exl3_linear(x, Lc, cb, rows))
+        per_config.append({"config": name, "rows": "16 of 2048 (every 128th)", "seconds": round(sec, 3),
+                           "rate": round(2 * len(rows) * k * n / sec / 1e9, 4),
+                           "unit": "GFLOP/s on the rows computed (the weight decode included)"})
+    lc = W.LOGITS
+    wl = W.logits_weights(lc["seed"], lc["w_rows"], lc["K"], threads=threads)
+    for M, rws in ((1, None), (16, np.array([0, 15], np.int64))):
+        x = W.activations(lc["seed"], M, lc["K"])
+        sec = timed(lambda: O.logits(x, wl, lc["n_valid"], rws))
+        nr = M if rws is None else len(rws)
+        per_config.append({"config": "padded logits K5120 n_valid=248077 M=%d" % M,
+                           "rows": "all 1" if rws is None else "2 of 16 (first, last)", "seconds": round(sec, 3),
+                           "rate": round(nr * 248192 * lc["K"] * 2 / sec / 1e9, 4),
+                           "unit": "GB/s of fp16 weight rows per computed row"})
+    del wl
+    log("oracle: per-configuration timings done")
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
             "sample": "%d oracle decode call(s), M=16, K5120xN17408 (89.1M weights decoded per call), %.1f s"
-                      % (calls, el)}
+                      % (calls, el),
+            "per_config": per_config}
 
 
 if __name__ == "__main__":
