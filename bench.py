@@ -76,6 +76,10 @@ def parse():
                     help="instead of the bench line: time the trellis-quantized output head (the padded-logits "
                          "geometry, 4 and 6 bits per weight) at M = 1, 4, 16, 64 beside the dense fp16 logits "
                          "projection, and print a markdown summary")
+    ap.add_argument("--dq-sweep", action="store_true",
+                    help="instead of the bench line: time the three kernel sequences of exl3_linear (fused "
+                         "decode-GEMM, reconstruct + GEMM, dequant-in-GEMM) over M on both MLP geometries, with the "
+                         "main kernel alone, and print a markdown summary")
     ap.add_argument("--pmc-workload", choices=("logits", "gemm", "decode", "reconstruct", "gemm_tail"), default=None,
                     help="run only a counter-collection workload: two 1 GiB device copies (calibration) then "
                          "three calls of the named path; prints nothing else")
@@ -108,6 +112,9 @@ def main():
         return
     if args.head:
         print(head_sweep())
+        return
+    if args.dq_sweep:
+        print(dq_sweep())
         return
     if args.ceilings:
         c = ceilings()
@@ -672,6 +679,63 @@ def ceilings(log=None) -> dict:
     if log:
         log("ceilings measured")
     return out
+
+
+def dq_sweep() -> str:
+    """exl3_linear's three kernel sequences forced at the same shapes: the
+    fused decode-GEMM, reconstruct + GEMM, and the dequant-in-GEMM, over M
+    on both MLP geometries (6 rotating 4-bit weight sets, 267 MB of codes);
+    whole calls back to back between one event pair, and the dequant-GEMM
+    kernel alone (event pairs around its launch)."""
+    import torch
+
+    import trellis_quantized_linear_had_amd as X
+    from trellis_quantized_linear_had_amd import _lib, _measure
+
+    dev = torch.device("cuda:0")
+    sh = torch.cuda.current_stream().cuda_stream
+    cb = W.codebook()
+    out = ["| geometry | M | fused µs | reconstruct+GEMM µs | dequant-GEMM µs | same, whole units µs | its kernels µs | "
+           "call TFLOP/s | kernels GB/s of codes |", "|---|---|---|---|---|---|---|---|---|"]
+    kt = _measure.KernelTimer(pairs=512, per_call=4)
+    for g, (k, n) in enumerate(((5120, 17408), (17408, 5120))):
+        layers = [X.Layer.from_numpy(W.layer(W.SEED_PREFILL, k, n, 2 * s), cb) for s in range(6)]
+        for M in (16, 32, 64, 128, 256, 512, 1024, 2048):
+            x = _lib.to_device_u16(W.activations(W.SEED_PREFILL, M, k, g))
+            y = torch.empty((M, n), dtype=torch.int16, device=dev)
+            scr = torch.empty(max(_measure.linear_scratch_bytes(k, n, M, v) for v in (1, 2, 3, 4)), dtype=torch.uint8,
+                              device=dev)
+            row = {}
+            for var in (_measure.VARIANT_FUSED, _measure.VARIANT_RECON_GEMM, _measure.VARIANT_DEQUANT_GEMM,
+                        _measure.VARIANT_DEQUANT_WHOLE):
+                reps = 12 if M <= 256 else 6
+                if var == _measure.VARIANT_FUSED and M > 256:
+                    row[var] = None
+                    continue
+                for i in range(2):
+                    kt.linear_variant(layers[i % 6], x, M, y, scr, sh, var)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(reps):
+                    kt.linear_variant(layers[i % 6], x, M, y, scr, sh, var)
+                e1.record()
+                torch.cuda.synchronize()
+                row[var] = e0.elapsed_time(e1) / reps * 1e3
+            for i in range(6):
+                kt.linear(layers[i % 6], x, M, y, scr, 128, sh, _measure.DECODE, _measure.VARIANT_DEQUANT_GEMM)
+            ms, cnt = kt.read(_measure.DECODE)
+            kus = ms / cnt * 1e3
+            out.append("| K%dxN%d | %d | %s | %.1f | %.1f | %.1f | %.1f | %.0f | %.0f |" % (
+                k, n, M, "—" if row[_measure.VARIANT_FUSED] is None else "%.1f" % row[_measure.VARIANT_FUSED],
+                row[_measure.VARIANT_RECON_GEMM], row[_measure.VARIANT_DEQUANT_GEMM],
+                row[_measure.VARIANT_DEQUANT_WHOLE], kus, 2 * M * k * n / row[_measure.VARIANT_DEQUANT_GEMM] / 1e6,
+                k * n / 2 / kus / 1e3))
+            print("[bench] dq-sweep K%d N%d M=%d done" % (k, n, M), file=sys.stderr, flush=True)
+            del x, y, scr
+        del layers
+        torch.cuda.empty_cache()
+    kt.close()
+    return "\n".join(out)
 
 
 def bits_sweep() -> str:

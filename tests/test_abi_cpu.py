@@ -239,12 +239,14 @@ def test_measure_library_exports_and_validation_without_gpu():
     vpp = ctypes.POINTER(ctypes.c_void_p)
     # an unknown mark kind, and event arrays missing: refused before the library call
     assert L.exl3m_linear_marked(None, None, 1, None, None, 0, 128, None, 7, 0, None, None,
-                                 ctypes.byref(used)) == X.EXL3_EINVAL
+                                 ctypes.byref(used), 0) == X.EXL3_EINVAL
     assert L.exl3m_linear_marked(None, None, 1, None, None, 0, 128, None, 0, 4, None, None,
-                                 ctypes.byref(used)) == X.EXL3_EINVAL
+                                 ctypes.byref(used), 0) == X.EXL3_EINVAL
+    assert L.exl3m_linear_marked(None, None, 1, None, None, 0, 128, None, 0, 0, vpp(), vpp(),
+                                 ctypes.byref(used), 9) == X.EXL3_EINVAL   # unknown variant
     # valid marks, then the library's own validation (NULL layer) speaks
     assert L.exl3m_linear_marked(None, None, 1, None, None, 0, 128, None, 0, 0, vpp(), vpp(),
-                                 ctypes.byref(used)) == X.EXL3_EINVAL
+                                 ctypes.byref(used), 0) == X.EXL3_EINVAL
     assert used.value == 0
     assert "layer is NULL" in L.exl3m_strerror(X.EXL3_EINVAL).decode()
 

@@ -10,6 +10,7 @@ from . import _lib
 
 MEASURE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libexl3_measure.so")
 DECODE, GEMM, LOGITS, RECONSTRUCT = 0, 1, 2, 3
+VARIANT_AUTO, VARIANT_FUSED, VARIANT_RECON_GEMM, VARIANT_DEQUANT_GEMM, VARIANT_DEQUANT_WHOLE = 0, 1, 2, 3, 4
 PROBE_WORKGROUPS = 256
 PROBE_SINK_BYTES = 256 * 32 * 256 * 4
 EXPORTS = (
@@ -17,6 +18,7 @@ EXPORTS = (
     "exl3m_events_destroy",
     "exl3m_elapsed_ms",
     "exl3m_linear_marked",
+    "exl3m_linear_scratch_bytes",
     "exl3m_head_marked",
     "exl3m_logits_marked",
     "exl3m_probe_lds_gather",
@@ -40,7 +42,7 @@ def mlib() -> ctypes.CDLL:
         L.exl3m_events_destroy.argtypes = [ip, vpp]
         L.exl3m_elapsed_ms.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_float)]
         L.exl3m_linear_marked.argtypes = [ctypes.POINTER(_lib.Exl3Layer), vp, i64, vp, vp, sz, i32, vp, ip, ip, vpp,
-                                          vpp, ctypes.POINTER(ip)]
+                                          vpp, ctypes.POINTER(ip), ip]
         L.exl3m_head_marked.argtypes = [ctypes.POINTER(_lib.Exl3Layer), vp, i64, i64, vp, i64, vp, vp, sz, i32, vp,
                                         ip, ip, vpp, vpp, ctypes.POINTER(ip)]
         L.exl3m_logits_marked.argtypes = [vp, i64, i32, vp, i64, i64, vp, i64, vp, vp, sz, vp, ip, ip, vpp, vpp,
@@ -48,12 +50,18 @@ def mlib() -> ctypes.CDLL:
         L.exl3m_probe_lds_gather.argtypes = [i64, vp, vp, vp]
         L.exl3m_probe_mfma.argtypes = [i64, vp, vp, vp]
         L.exl3m_probe_stream.argtypes = [i32, vp, vp, i64, vp, vp]
+        L.exl3m_linear_scratch_bytes.argtypes = [i32, i32, i64, i32, ip]
         L.exl3m_strerror.argtypes = [ip]
         L.exl3m_strerror.restype = ctypes.c_char_p
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = ip
+        L.exl3m_linear_scratch_bytes.restype = sz
         _m = L
     return _m
+
+
+def linear_scratch_bytes(K: int, N: int, M: int, variant: int, prefill_min_m: int = 128) -> int:
+    return int(mlib().exl3m_linear_scratch_bytes(K, N, M, prefill_min_m, variant))
 
 
 def check(status: int) -> None:
@@ -90,12 +98,19 @@ class KernelTimer:
         e = ctypes.cast(ctypes.byref(self.stop, off * ctypes.sizeof(ctypes.c_void_p)), vpp)
         return off, s, e
 
-    def linear(self, layer, x, M, y, scratch, prefill_min_m, stream, kind):
+    def linear(self, layer, x, M, y, scratch, prefill_min_m, stream, kind, variant=VARIANT_AUTO):
         off, s, e = self._slot()
         used = ctypes.c_int(0)
         check(mlib().exl3m_linear_marked(layer.c, x.data_ptr(), M, y.data_ptr(), scratch.data_ptr(), scratch.numel(),
-                                         prefill_min_m, stream, kind, self.per_call, s, e, ctypes.byref(used)))
+                                         prefill_min_m, stream, kind, self.per_call, s, e, ctypes.byref(used),
+                                         variant))
         self._record(kind, off, used.value)
+
+    def linear_variant(self, layer, x, M, y, scratch, stream, variant):
+        """One exl3_linear call with the kernel sequence forced, unmarked."""
+        used = ctypes.c_int(0)
+        check(mlib().exl3m_linear_marked(layer.c, x.data_ptr(), M, y.data_ptr(), scratch.data_ptr(), scratch.numel(),
+                                         128, stream, DECODE, 0, None, None, ctypes.byref(used), variant))
 
     def head(self, layer, x, M, n_valid, lg, ld, am, scratch, prefill_min_m, stream, kind):
         off, s, e = self._slot()

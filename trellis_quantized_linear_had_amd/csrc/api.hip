@@ -18,6 +18,7 @@
 
 #include "exl3.h"
 #include "decode_plan.h"
+#include "dq_plan.h"
 #include "internal.h"
 #include "marks.h"
 
@@ -45,6 +46,10 @@ hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, in
                            int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream,
                            Marks* marks);
 size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K);
+hipError_t launch_dqgemm(const uint16_t* xf, const uint32_t* codes, const uint16_t* cb, const uint16_t* scale,
+                         const uint16_t* sign_n, uint16_t* y, int64_t ldy, float* partials, int32_t K, int32_t N,
+                         int32_t ldt, int32_t M, const DqPlan& plan, hipStream_t stream);
+size_t dq_partial_bytes(const DqPlan& plan);
 hipError_t launch_logits(const uint16_t* x, int32_t M, int32_t K, const uint16_t* w, int64_t n_valid, int64_t n_pad,
                          uint16_t* logits, int64_t ld, int64_t* argmax, int32_t* pk, int32_t* pi, uint16_t* xp,
                          hipStream_t stream, Marks* marks);
@@ -271,6 +276,67 @@ DecodeLayout decode_layout(int32_t K, int32_t N, int64_t M, int32_t bits) {
   return l;
 }
 
+// Dequant-in-GEMM plan: row fragments per pass (the fewest 32-row fragments
+// that hold M, at most 8), 256-column units, and the split between whole
+// units and K-split tail units that minimises the modelled time: rounds of
+// 256 CUs, each as long as its workgroups' 16-k steps (the larger of the
+// LDS-gather time of four waves and the MFMA time per step, measured
+// 0.24 and 0.06 nqb us) plus a fixed cost for the codebook load and the
+// output stage, plus the tail's fp32 partials written and read back.
+DqPlan plan_dq(int32_t K, int32_t N, int64_t M, bool whole = false) {
+  DqPlan p;
+  p.nqb = M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8;
+  const int R = 32 * p.nqb;
+  p.passes = (int32_t)((M + R - 1) / R);
+  p.pblocks = (N + 255) / 256;
+  const int ksub = K / 16;
+  const int64_t units = (int64_t)p.passes * p.pblocks;
+  const double step_us = std::max(0.24, 0.06 * p.nqb), wg_us = 3.0;
+  auto rounds = [](int64_t wgs) { return (double)((wgs + 255) / 256); };
+  double best = 1e300;
+  p.full = (int32_t)units;
+  p.tail = 0;
+  p.tail_ks = 1;
+  p.ksub_per_piece = ksub;
+  const int64_t fr = units / 256;
+  for (int64_t nf = std::max<int64_t>(0, fr - 1); nf <= fr; ++nf) {
+    const int64_t full = nf * 256, tail = units - full;
+    for (int ks = 1; ks <= (whole ? 1 : std::min(ksub / 4, 16)); ++ks) {
+      if (tail == 0 && ks > 1) break;
+      const int per = ((ksub + ks - 1) / ks + 3) / 4 * 4;  // whole 4-step blocks (ksub is a multiple of 8)
+      const int ks_eff = (ksub + per - 1) / per;
+      double t = rounds(full) * (ksub * step_us + wg_us);
+      if (ks_eff == 1) {
+        t = rounds(full + tail) * (ksub * step_us + wg_us);
+      } else {
+        t += rounds(tail * ks_eff) * (per * step_us + wg_us) + (double)tail * ks_eff * R * 256 * 8.0 / 4e6;
+      }
+      if (t < best - 1e-9) {
+        best = t;
+        p.full = (int32_t)(ks_eff == 1 ? units : full);
+        p.tail = (int32_t)(ks_eff == 1 ? 0 : tail);
+        p.tail_ks = ks_eff;
+        p.ksub_per_piece = ks_eff == 1 ? ksub : per;
+      }
+    }
+  }
+  return p;
+}
+
+struct DqLayout {
+  size_t xf_off, part_off, total;
+  DqPlan plan;
+};
+
+DqLayout dq_layout(int32_t K, int32_t N, int64_t M, bool whole = false) {
+  DqLayout l;
+  l.plan = plan_dq(K, N, M, whole);
+  l.xf_off = 0;
+  l.part_off = align256((size_t)((M + 31) / 32 * 32) * K * 2);
+  l.total = l.part_off + align256(dq_partial_bytes(l.plan));
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,8 +364,12 @@ namespace {
 // The layer over its leading ncols columns (ncols a multiple of 128, at most
 // N), written to y with leading dimension ldy. Arguments are validated by the
 // callers; scratch holds linear_cols_scratch_bytes(K, ncols, M, pm).
-size_t linear_cols_scratch_bytes(int32_t K, int32_t ncols, int64_t M, int32_t prefill_min_m) {
-  if (use_prefill(M, prefill_min_m)) return prefill_layout(K, ncols, M).total;
+size_t linear_cols_scratch_bytes(int32_t K, int32_t ncols, int64_t M, int32_t prefill_min_m,
+                                 int variant = kVariantAuto) {
+  if (variant == kVariantDequantGemm || variant == kVariantDequantGemmWhole)
+    return dq_layout(K, ncols, M, variant == kVariantDequantGemmWhole).total;
+  if (variant == kVariantReconstructGemm || (variant == kVariantAuto && use_prefill(M, prefill_min_m)))
+    return prefill_layout(K, ncols, M).total;
   // the decode path's partial slices depend on the plan, which differs
   // between 4 bits and the other widths: enough for either
   return std::max(decode_layout(K, ncols, M, 4).total, decode_layout(K, ncols, M, 3).total);
@@ -308,7 +378,22 @@ size_t linear_cols_scratch_bytes(int32_t K, int32_t ncols, int64_t M, int32_t pr
 int linear_cols(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, int64_t ldy, int32_t ncols,
                 char* sb, int32_t prefill_min_m, hipStream_t stream, Marks* marks) {
   const int32_t K = L->K, N = L->N;
-  if (use_prefill(M, prefill_min_m)) {
+  const int variant = marks ? marks->variant : kVariantAuto;
+  if (variant == kVariantDequantGemm || variant == kVariantDequantGemmWhole) {
+    if (L->bits != 4) return fail(EXL3_ESHAPE, "the dequant-GEMM takes 4-bit codes only");
+    const DqLayout l = dq_layout(K, ncols, M, variant == kVariantDequantGemmWhole);
+    uint16_t* xf = (uint16_t*)(sb + l.xf_off);
+    float* part = (float*)(sb + l.part_off);
+    EXL3_TRY(launch_had128_frag(x, xf, M, K, L->sign_k, stream), "input rotation");
+    EXL3_TRY(mark_begin(marks, kMarkDecode, stream), "event record");
+    EXL3_TRY(launch_dqgemm(xf, L->codes, L->codebook, L->scale, L->sign_n, y, ldy, part, K, ncols, N / 16,
+                           (int32_t)M, l.plan, stream),
+             "dequant gemm");
+    EXL3_TRY(mark_end(marks, kMarkDecode, stream), "event record");
+    return EXL3_OK;
+  }
+  const bool prefill = variant == kVariantReconstructGemm || (variant == kVariantAuto && use_prefill(M, prefill_min_m));
+  if (prefill) {
     const PrefillLayout l = prefill_layout(K, ncols, M);
     uint16_t* xr = (uint16_t*)(sb + l.xr_off);
     uint16_t* wt = (uint16_t*)(sb + l.w_off);
@@ -418,12 +503,18 @@ int linear_entry(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y,
   g_msg[0] = 0;
   int st = validate_call(L, x, M, y, scratch, prefill_min_m);
   if (st || M == 0) return st;
-  const size_t need = exl3_linear_scratch_bytes(L->K, L->N, M, prefill_min_m);
+  const size_t need =
+      linear_cols_scratch_bytes(L->K, L->N, M, prefill_min_m, marks ? marks->variant : (int)kVariantAuto);
   if (scratch_bytes < need)
     return fail(EXL3_ESCRATCH, "scratch has %zu bytes; this call needs %zu", scratch_bytes, need);
   st = check_device();
   if (st) return st;
   return linear_cols(L, x, M, y, L->N, L->N, (char*)scratch, prefill_min_m, stream, marks);
+}
+
+size_t linear_variant_scratch_bytes(int32_t K, int32_t N, int64_t M, int32_t prefill_min_m, int variant) {
+  if (K <= 0 || N <= 0 || K % 128 || N % 128 || M <= 0) return 0;
+  return linear_cols_scratch_bytes(K, N, M, prefill_min_m, variant);
 }
 
 int logits_entry(const uint16_t* x, int64_t M, int32_t K, const uint16_t* w, int64_t w_rows, int64_t n_valid,

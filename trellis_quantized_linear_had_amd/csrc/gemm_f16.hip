@@ -42,6 +42,7 @@
 // share one 256-row strip of W^T run together on one XCD and read it through
 // that XCD's L2.
 #include "common.h"
+#include "epilogue.h"
 #include "marks.h"
 
 namespace exl3 {
@@ -128,76 +129,6 @@ template <int N>
 __device__ __forceinline__ void wait_slot(f16x8 (&slot)[G_QT]) {
   static_assert(G_QT == 2, "one operand per fragment of the slot");
   asm volatile("s_waitcnt vmcnt(%2)" : "+v"(slot[0]), "+v"(slot[1]) : "n"(N) : "memory");
-}
-
-// Output rotation + signs + fp16 store of one 128 (p) x 32 (q) block of a
-// wave. a[i][r] holds D[p][q] with (inside the 128-row rotation block)
-// p = 32 i + 8 (r >> 2) + 4 lhalf + (r & 3), q = q0 + lrow. Index bits of p:
-// 0,1 <- r&3; 2 <- lhalf; 3,4 <- r>>2; 5,6 <- i. Six stages in registers, one
-// across lanes 32 apart.
-__device__ __forceinline__ void rotate_store_block(f32x16 (&a)[4], int lane, int pw, int q0, int P, int Q,
-                                                   uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
-                                                   const uint16_t* __restrict__ sign_n) {
-  const int lrow = lane & 31, lhalf = lane >> 5;
-  // The 16 sign words go out before the butterflies and are used after them:
-  // one memory round trip, under the arithmetic, and no wait between the
-  // stores. Without signs, row 0 of y (in bounds, then masked off) is read.
-  u32x2 sg[4][4];
-  const uint32_t smask = sign_n ? 0x80008000u : 0u;
-  if (pw < P) {  // uniform over the wave
-    const uint16_t* sp = (sign_n ? sign_n : y) + n0 + pw;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) sg[i][g] = *reinterpret_cast<const u32x2*>(sp + 32 * i + 8 * g + 4 * lhalf);
-  }
-#pragma unroll
-  for (int h = 1; h <= 8; h <<= 1) {  // register bits r&1, r&2, r&4, r&8
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if ((r & h) == 0) {
-          const float u = a[i][r], v = a[i][r + h];
-          a[i][r] = u + v;
-          a[i][r + h] = u - v;
-        }
-  }
-#pragma unroll
-  for (int h = 1; h <= 2; h <<= 1) {  // register bits of i
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if ((i & h) == 0)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float u = a[i][r], v = a[i + h][r];
-          a[i][r] = u + v;
-          a[i + h][r] = u - v;
-        }
-  }
-  const float s = lhalf ? -1.f : 1.f;  // lane bit: partner 32 lanes away
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float partner = __shfl_xor(a[i][r], 32);
-      a[i][r] = __builtin_fmaf(s, a[i][r], partner);
-    }
-  if (pw >= P) return;
-  const int q = q0 + lrow;
-  if (q >= Q) return;
-  uint16_t* yrow = y + (int64_t)q * ldy + n0 + pw;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int p = 32 * i + 8 * g + 4 * lhalf;
-      u32x2 o;
-      o[0] = pack_f16x2(a[i][4 * g] * EXL3_INV_SQRT128, a[i][4 * g + 1] * EXL3_INV_SQRT128);
-      o[1] = pack_f16x2(a[i][4 * g + 2] * EXL3_INV_SQRT128, a[i][4 * g + 3] * EXL3_INV_SQRT128);
-      o ^= sg[i][g] & smask;
-      *reinterpret_cast<u32x2*>(yrow + p) = o;
-    }
 }
 
 // Epilogue of one wave's 128 x 64 block: two 32-wide q blocks.

@@ -17,6 +17,9 @@ struct Marks;
 int linear_entry(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* scratch, size_t scratch_bytes,
                  int32_t prefill_min_m, hipStream_t stream, Marks* marks);
 
+// Scratch of exl3_linear with its kernel sequence forced (marks.h variants).
+size_t linear_variant_scratch_bytes(int32_t K, int32_t N, int64_t M, int32_t prefill_min_m, int variant);
+
 // exl3_head_logits_argmax with optional marks (kMarkDecode, kMarkReconstruct,
 // kMarkGemm).
 int head_entry(const exl3_layer* L, const uint16_t* x, int64_t M, int64_t n_valid, uint16_t* logits,

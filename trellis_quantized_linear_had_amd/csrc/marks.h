@@ -17,6 +17,18 @@ struct Marks {
   int used;           // event pairs recorded so far
   hipEvent_t* start;  // capacity events each, created by the caller
   hipEvent_t* stop;
+  int variant;        // kernel choice of exl3_linear: 0 = the library's own, else a KernelVariant
+};
+
+// Kernel sequences of exl3_linear a measurement caller may force, to time
+// them against each other at the same shape.
+enum KernelVariant {
+  kVariantAuto = 0,
+  kVariantFused = 1,
+  kVariantReconstructGemm = 2,
+  kVariantDequantGemm = 3,
+  kVariantDequantGemmWhole = 4,  // the dequant-GEMM with every unit over all of K (no split tail)
+  kVariantLast = 4
 };
 
 inline hipError_t mark_begin(Marks* m, int kind, hipStream_t s) {

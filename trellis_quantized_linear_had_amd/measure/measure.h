@@ -33,12 +33,25 @@ int exl3m_events_destroy(int n, void **events);
 /* Waits for event b, then *ms = time from a to b in milliseconds. */
 int exl3m_elapsed_ms(void *a, void *b, float *ms);
 
+/* Kernel sequences of exl3_linear that a measurement may force. */
+#define EXL3M_VARIANT_AUTO 0         /* the library's own choice */
+#define EXL3M_VARIANT_FUSED 1        /* decode-GEMM + output stage */
+#define EXL3M_VARIANT_RECON_GEMM 2   /* reconstruct + MFMA GEMM */
+#define EXL3M_VARIANT_DEQUANT_GEMM 3 /* dequant-in-GEMM (its own output stage; a K-split tail and fixup) */
+#define EXL3M_VARIANT_DEQUANT_WHOLE 4 /* the same with every unit over all of K */
+
 /* exl3_linear, with one event pair recorded on `stream` around every launch
  * of `kind` (start[i] before, stop[i] after), at most `capacity` pairs;
- * *used = the pairs recorded. */
+ * *used = the pairs recorded. `variant` forces a kernel sequence (the
+ * dequant-GEMM marks as EXL3M_DECODE); EXL3M_VARIANT_AUTO is exl3_linear's
+ * own dispatch. */
 int exl3m_linear_marked(const exl3_layer *layer, const uint16_t *x, int64_t M, uint16_t *y, void *scratch,
                         size_t scratch_bytes, int32_t prefill_min_m, void *stream, int kind, int capacity,
-                        void **start, void **stop, int *used);
+                        void **start, void **stop, int *used, int variant);
+
+/* Scratch bytes exl3m_linear_marked needs with this variant (0 for invalid
+ * shapes); EXL3M_VARIANT_AUTO gives exl3_linear_scratch_bytes. */
+size_t exl3m_linear_scratch_bytes(int32_t K, int32_t N, int64_t M, int32_t prefill_min_m, int variant);
 
 /* exl3_head_logits_argmax with marks, as exl3m_linear_marked. */
 int exl3m_head_marked(const exl3_layer *layer, const uint16_t *x, int64_t M, int64_t n_valid, uint16_t *logits,

@@ -38,11 +38,13 @@ int mhip(hipError_t e, const char* where) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int make_marks(exl3::Marks& m, int kind, int capacity, void** start, void** stop, int* used) {
+int make_marks(exl3::Marks& m, int kind, int capacity, void** start, void** stop, int* used, int variant = 0) {
   if (kind < 0 || kind >= exl3::kMarkKinds) return mfail(EXL3_EINVAL, "mark kind %d is not 0..3", kind);
+  if (variant < 0 || variant > exl3::kVariantLast) return mfail(EXL3_EINVAL, "variant %d is not 0..4", variant);
   if (capacity < 0 || (capacity > 0 && (!start || !stop)) || !used)
     return mfail(EXL3_EINVAL, "bad event arrays (capacity %d)", capacity);
-  m = exl3::Marks{kind, capacity, 0, reinterpret_cast<hipEvent_t*>(start), reinterpret_cast<hipEvent_t*>(stop)};
+  m = exl3::Marks{kind, capacity, 0, reinterpret_cast<hipEvent_t*>(start), reinterpret_cast<hipEvent_t*>(stop),
+                  variant};
   return EXL3_OK;
 }
 
@@ -87,14 +89,19 @@ int exl3m_elapsed_ms(void* a, void* b, float* ms) {
 
 int exl3m_linear_marked(const exl3_layer* layer, const uint16_t* x, int64_t M, uint16_t* y, void* scratch,
                         size_t scratch_bytes, int32_t prefill_min_m, void* stream, int kind, int capacity,
-                        void** start, void** stop, int* used) {
+                        void** start, void** stop, int* used, int variant) {
   m_own = false;
   exl3::Marks m;
-  int st = make_marks(m, kind, capacity, start, stop, used);
+  int st = make_marks(m, kind, capacity, start, stop, used, variant);
   if (st) return st;
   st = exl3::linear_entry(layer, x, M, y, scratch, scratch_bytes, prefill_min_m, (hipStream_t)stream, &m);
   *used = m.used;
   return st;
+}
+
+size_t exl3m_linear_scratch_bytes(int32_t K, int32_t N, int64_t M, int32_t prefill_min_m, int variant) {
+  if (variant < 0 || variant > exl3::kVariantLast) return 0;
+  return exl3::linear_variant_scratch_bytes(K, N, M, prefill_min_m, variant);
 }
 
 int exl3m_head_marked(const exl3_layer* layer, const uint16_t* x, int64_t M, int64_t n_valid, uint16_t* logits,
