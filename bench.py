@@ -496,61 +496,94 @@ def pmc_workload(kind: str):
     print("[bench] pmc workload %s done" % kind, file=sys.stderr, flush=True)
 
 
+def interleaved_us(calls, reps, rounds=3):
+    """Microseconds per call of each entry of `calls` (name -> one(i) that
+    enqueues call i): every callable warmed up, then `rounds` rounds that
+    time `reps` back-to-back calls of each in turn between one event pair;
+    the least of a callable's rounds is its figure, so a clock still ramping
+    up (or a neighbour's leftovers in the caches) does not bias whichever
+    callable happens to run first."""
+    import torch
+
+    for one in calls.values():
+        for i in range(2):
+            one(i)
+    torch.cuda.synchronize()
+    best = {}
+    for _ in range(rounds):
+        for name, one in calls.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                one(i)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            best[name] = min(best.get(name, us), us)
+    return best
+
+
 def sweep(bits: int = 4) -> str:
-    """Fused (decode-GEMM) and prefill (reconstruct + GEMM) paths over M,
-    forced through prefill_min_m (0: fused at every M; 1: prefill at every M),
-    6 rotating weight sets per geometry (267 MB of 4-bit codes at the MLP
-    geometries, above the 256 MB MALL), back-to-back calls between one event
-    pair per cell. At 4 bits: both MLP geometries, then the wide projection
-    K5120 x N32768 at M = 2048 (one 32768-column slice) with its scratch
-    bytes. At another width: the MLP geometries and a square K5120 x N5120
-    projection (attention-sized), M up to 1024, to locate that width's
-    crossover."""
+    """exl3_linear's kernel sequences over M, each forced through the
+    measurement library (decode-GEMM, reconstruct + GEMM and, at 4 bits, the
+    dequant-GEMM), beside the default dispatch (threshold 128), 6 rotating
+    weight sets per geometry (267 MB of 4-bit codes at the MLP geometries,
+    above the 256 MB MALL), back-to-back calls between one event pair per
+    cell. At 4 bits: both MLP geometries, then the wide projection K5120 x
+    N32768 at M = 2048 (one 32768-column slice) with its scratch bytes. At
+    another width: the MLP geometries and a square K5120 x N5120 projection
+    (attention-sized), M up to 1024, to locate that width's crossover."""
     import torch
 
     import trellis_quantized_linear_had_amd as X
-    from trellis_quantized_linear_had_amd import _lib
+    from trellis_quantized_linear_had_amd import _lib, _measure
 
     lib = _lib.lib()
     dev = torch.device("cuda:0")
     sh = torch.cuda.current_stream().cuda_stream
     cb = W.codebook()
 
-    def time_calls(layers, x, M, y, scr, pm, reps):
+    def caller(layers, x, M, y, scr, variant=None):
         def one(i):
-            _lib.check(lib.exl3_linear(layers[i % len(layers)].c, x.data_ptr(), M, y.data_ptr(), scr.data_ptr(),
-                                       scr.numel(), pm, sh))
-        for i in range(2):
-            one(i)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(reps):
-            one(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e3
+            lay = layers[i % len(layers)]
+            if variant is None:
+                _lib.check(lib.exl3_linear(lay.c, x.data_ptr(), M, y.data_ptr(), scr.data_ptr(), scr.numel(), 128,
+                                           sh))
+            else:
+                _measure.linear_forced(lay, x, M, y, scr, sh, variant)
+        return one
 
-    out = ["| geometry | bits | M | fused µs | prefill µs | faster | prefill TFLOP/s |",
-           "|---|---|---|---|---|---|---|"]
+    names = {_measure.VARIANT_FUSED: "decode-GEMM", _measure.VARIANT_RECON_GEMM: "reconstruct+GEMM",
+             _measure.VARIANT_DEQUANT_GEMM: "dequant-GEMM"}
+    variants = [_measure.VARIANT_FUSED, _measure.VARIANT_RECON_GEMM] + (
+        [_measure.VARIANT_DEQUANT_GEMM] if bits == 4 else [])
+    out = ["| geometry | bits | M | " + " | ".join("%s µs" % names[v] for v in variants) +
+           " | default dispatch µs | fastest | default TFLOP/s |",
+           "|---|---|---|" + "---|" * len(variants) + "---|---|---|"]
     cross = {}
     geoms = ((5120, 17408), (17408, 5120)) if bits == 4 else ((5120, 17408), (17408, 5120), (5120, 5120))
-    Ms = (16, 32, 64, 96, 128, 192, 256, 512, 1024, 2048, 4096) if bits == 4 else (16, 32, 64, 96, 128, 192, 256,
-                                                                                    512, 1024)
+    Ms = (16, 32, 48, 64, 96, 128, 192, 256, 384, 512, 1024, 2048, 4096) if bits == 4 else (
+        16, 32, 64, 96, 128, 192, 256, 512, 1024)
     for gi, (Kg, Ng) in enumerate(geoms):
         layers = [X.Layer.from_numpy(W.layer(W.SEED_PREFILL, Kg, Ng, 2 * s + gi, bits), cb) for s in range(6)]
         for M in Ms:
             x = _lib.to_device_u16(W.activations(W.SEED_PREFILL, M, Kg, gi))
             y = torch.empty((M, Ng), dtype=torch.int16, device=dev)
-            scr = torch.empty(max(X.linear_scratch_bytes(Kg, Ng, M, 0), X.linear_scratch_bytes(Kg, Ng, M, 1)),
-                              dtype=torch.uint8, device=dev)
-            fused = time_calls(layers, x, M, y, scr, 0, 6) if M <= 1024 else None
-            pre = time_calls(layers, x, M, y, scr, 1, 6)
-            if fused is not None and pre < fused and (Kg, Ng) not in cross:
+            need = max([X.linear_scratch_bytes(Kg, Ng, M, 128)] +
+                       [_measure.linear_scratch_bytes(Kg, Ng, M, v) for v in variants])
+            scr = torch.empty(need, dtype=torch.uint8, device=dev)
+            calls = {v: caller(layers, x, M, y, scr, v) for v in variants
+                     if not (v == _measure.VARIANT_FUSED and M > 1024)}
+            calls["default"] = caller(layers, x, M, y, scr)
+            t = interleaved_us(calls, 6)
+            dflt = t.pop("default")
+            fastest = min(t, key=t.get)
+            if (_measure.VARIANT_FUSED in t and t[_measure.VARIANT_RECON_GEMM] < t[_measure.VARIANT_FUSED]
+                    and (Kg, Ng) not in cross):
                 cross[(Kg, Ng)] = M
             out.append("| K%d×N%d | %d | %d | %s | %.1f | %s | %.1f |" % (
-                Kg, Ng, bits, M, "%.1f" % fused if fused is not None else "—", pre,
-                "—" if fused is None else ("prefill" if pre < fused else "fused"), 2 * M * Kg * Ng / pre / 1e6))
+                Kg, Ng, bits, M, " | ".join("%.1f" % t[v] if v in t else "—" for v in variants), dflt,
+                names[fastest], 2 * M * Kg * Ng / dflt / 1e6))
             print("[bench] sweep K%d N%d M%d done" % (Kg, Ng, M), file=sys.stderr, flush=True)
             del x, y, scr
         del layers
@@ -581,8 +614,8 @@ def sweep(bits: int = 4) -> str:
             del wt
         lines.append("")
     for (Kg, Ng), M in cross.items():
-        lines.append("Crossover K%d×N%d, %d bits: prefill is faster from M = %d on (among the M measured)." % (
-            Kg, Ng, bits, M))
+        lines.append("Crossover K%d×N%d, %d bits: reconstruct + GEMM is faster than the decode-GEMM from M = %d on "
+                     "(among the M measured)." % (Kg, Ng, bits, M))
     if bits != 4:
         return "\n".join(lines)
     Kw, Nw, Mw = 5120, 32768, 2048
@@ -591,7 +624,7 @@ def sweep(bits: int = 4) -> str:
     y = torch.empty((Mw, Nw), dtype=torch.int16, device=dev)
     need = X.linear_scratch_bytes(Kw, Nw, Mw)
     scr = torch.empty(need, dtype=torch.uint8, device=dev)
-    us = time_calls(layers, x, Mw, y, scr, 128, 6)
+    us = interleaved_us({"default": caller(layers, x, Mw, y, scr)}, 6)["default"]
     lines.append("")
     lines.append("Wide projection K%d×N%d, M = %d (one 32768-column slice): %.1f µs per call, %.1f TFLOP/s; "
                  "scratch %d B (x̃ %d B + fp16 W slice %d B + GEMM-tail partials %d B)" % (
@@ -705,22 +738,12 @@ def dq_sweep() -> str:
             y = torch.empty((M, n), dtype=torch.int16, device=dev)
             scr = torch.empty(max(_measure.linear_scratch_bytes(k, n, M, v) for v in (1, 2, 3, 4)), dtype=torch.uint8,
                               device=dev)
-            row = {}
-            for var in (_measure.VARIANT_FUSED, _measure.VARIANT_RECON_GEMM, _measure.VARIANT_DEQUANT_GEMM,
-                        _measure.VARIANT_DEQUANT_WHOLE):
-                reps = 12 if M <= 256 else 6
-                if var == _measure.VARIANT_FUSED and M > 256:
-                    row[var] = None
-                    continue
-                for i in range(2):
-                    kt.linear_variant(layers[i % 6], x, M, y, scr, sh, var)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for i in range(reps):
-                    kt.linear_variant(layers[i % 6], x, M, y, scr, sh, var)
-                e1.record()
-                torch.cuda.synchronize()
-                row[var] = e0.elapsed_time(e1) / reps * 1e3
+            def forced(var):
+                return lambda i: kt.linear_variant(layers[i % 6], x, M, y, scr, sh, var)
+            vs = [v for v in (_measure.VARIANT_FUSED, _measure.VARIANT_RECON_GEMM, _measure.VARIANT_DEQUANT_GEMM,
+                              _measure.VARIANT_DEQUANT_WHOLE) if not (v == _measure.VARIANT_FUSED and M > 256)]
+            row = interleaved_us({v: forced(v) for v in vs}, 12 if M <= 256 else 6)
+            row.setdefault(_measure.VARIANT_FUSED, None)
             for i in range(6):
                 kt.linear(layers[i % 6], x, M, y, scr, 128, sh, _measure.DECODE, _measure.VARIANT_DEQUANT_GEMM)
             ms, cnt = kt.read(_measure.DECODE)

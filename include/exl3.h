@@ -112,19 +112,30 @@ typedef struct exl3_layer {
 /* y = layer(x) for x (M x K, row-major fp16) into y (M x N, row-major fp16).
  * Dispatch happens here, on the host, at call time [P316 "Change": the branch
  * must sit inside the op]: if prefill_min_m > 0 and M >= prefill_min_m the
- * prefill path runs (input rotation into scratch; then, per slice of at most
- * EXL3_MAX_CHUNK_COLS columns, reconstruct the slice to fp16 into scratch and
- * run the MFMA GEMM whose epilogue applies the output rotation and sign_n);
- * otherwise the fused decode path runs (a decode-GEMM that decodes every
- * trellis tile once per pass of up to 64 rows and multiplies it with those
- * rows -- for M <= 16 it also applies the input rotation itself, otherwise a
- * rotation pass writes it to scratch first -- then an output-stage kernel that
- * sums the split-K partials in a fixed order and applies the output rotation
- * and sign_n). prefill_min_m = 0 means the fused path for every M. M = 0 is a
- * no-op returning EXL3_OK.
+ * prefill side runs, otherwise the fused side (prefill_min_m = 0: the fused
+ * side for every M). Each side picks its kernels by width and row count:
+ *   - prefill, reconstruct + GEMM (every width; 4 bits above 1024 rows): input
+ *     rotation into scratch; then, per slice of at most EXL3_MAX_CHUNK_COLS
+ *     columns, reconstruct the slice to fp16 into scratch and run the MFMA
+ *     GEMM whose epilogue applies the output rotation and sign_n;
+ *   - fused, decode-GEMM (widths other than 4; 4 bits below 48 rows): a
+ *     kernel that decodes every trellis tile once per pass of up to 64 rows
+ *     and multiplies it with those rows -- for M <= 16 it also applies the
+ *     input rotation itself, otherwise a rotation pass writes it to scratch
+ *     first -- then an output-stage kernel that sums the split-K partials in
+ *     a fixed order and applies the output rotation and sign_n;
+ *   - dequant-GEMM (4 bits: 48 rows and up on the fused side, up to 1024 rows
+ *     on the prefill side) [P316 follow-up item 4: dequantisation fused into
+ *     the GEMM]: input rotation into scratch, then an MFMA GEMM that decodes
+ *     each trellis tile into its operand registers once per pass of up to
+ *     256 rows and applies scales, output rotation and sign_n in its
+ *     epilogue; a K-split remainder of the work leaves fp32 partials that a
+ *     fixup kernel sums in a fixed order before the same epilogue.
+ * All three give y within the fp16 rounding of the same sums, not
+ * bit-identical to each other. M = 0 is a no-op returning EXL3_OK.
  * Limits (EXL3_ESHAPE otherwise): K, N positive multiples of 128, K < 65536,
- * K * N / 2 (the packed codes) below 4 GiB, and on the prefill path
- * M * K * 2 below 4 GiB.
+ * K * N / 2 (the packed codes) below 4 GiB, and on the reconstruct + GEMM
+ * route M * K * 2 below 4 GiB; M at most 2^31 - 32 (EXL3_EINVAL otherwise).
  * scratch: device memory of at least
  *   exl3_linear_scratch_bytes(K, N, M, prefill_min_m) bytes, owned by the
  * caller and reusable across layers of the same geometry; its contents are
@@ -136,10 +147,10 @@ int exl3_linear(const exl3_layer *layer, const uint16_t *x, int64_t M, uint16_t 
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same dispatch, kernels and results (bit-identical to exl3_linear), with the
  * scratch held by the library instead of passed in -- a device array of
- * EXL3_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, kept until the process ends.
+ * EXL3_NOALLOC_SCRATCH_BYTES (48 MiB) per GPU, kept until the process ends.
  * It covers every fused-path call below the default threshold at the MLP and
  * wide geometries (K5120 x N17408, K17408 x N5120, K5120 x N32768: at most
- * 26.5 MiB at M = 127); a call whose exl3_linear_scratch_bytes exceeds it
+ * 34.3 MiB at M = 127); a call whose exl3_linear_scratch_bytes exceeds it
  * returns EXL3_ESCRATCH before any launch. The first call on a device looks
  * up the array's device address (hipGetSymbolAddress); no call allocates or
  * frees memory. Every call on one GPU uses that GPU's one array, and the
@@ -147,7 +158,7 @@ int exl3_linear(const exl3_layer *layer, const uint16_t *x, int64_t M, uint16_t 
  * write in the same call): calls that overlap on one GPU -- on different
  * streams, or from several threads -- race and must be ordered by the
  * caller. Other arguments, limits and statuses as exl3_linear. */
-#define EXL3_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+#define EXL3_NOALLOC_SCRATCH_BYTES (48 * 1024 * 1024)
 int exl3_linear_noalloc(const exl3_layer *layer, const uint16_t *x, int64_t M, uint16_t *y, int32_t prefill_min_m,
                         void *stream);
 

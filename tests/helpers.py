@@ -68,5 +68,43 @@ def require_gpu():
     return torch
 
 
+# exl3_linear's kernel sequences: the decode-GEMM ("fused"), reconstruct +
+# GEMM ("recon") and the dequant-GEMM ("dq", 4 bits only). At 4 bits the
+# dispatch takes the dequant-GEMM from 48 rows on the fused side and up to
+# 1024 rows on the prefill side.
+DQ_FUSED_MIN_ROWS, DQ_PREFILL_MAX_ROWS = 48, 1024
+
+
+def route(bits: int, M: int, pm: int) -> str:
+    prefill = pm > 0 and M >= pm
+    if bits == 4 and (M <= DQ_PREFILL_MAX_ROWS if prefill else M >= DQ_FUSED_MIN_ROWS):
+        return "dq"
+    return "recon" if prefill else "fused"
+
+
+def linear_forced(lay, x, route_name: str, out=None, scratch=None, sync: bool = True):
+    """exl3_linear with its kernel sequence forced (through the measurement
+    library); x is a host uint16 array or a device tensor. Returns the host
+    output if sync, else the device output."""
+    import torch
+
+    from trellis_quantized_linear_had_amd import _lib, _measure
+
+    variant = {"fused": _measure.VARIANT_FUSED, "recon": _measure.VARIANT_RECON_GEMM,
+               "dq": _measure.VARIANT_DEQUANT_GEMM, "dq_whole": _measure.VARIANT_DEQUANT_WHOLE}[route_name]
+    xd = x if isinstance(x, torch.Tensor) else _lib.to_device_u16(x)
+    M = xd.shape[0]
+    if out is None:
+        out = torch.full((M, lay.N), 0x7E7E, dtype=torch.int16, device="cuda")
+    if scratch is None:
+        scratch = torch.empty(max(1, _measure.linear_scratch_bytes(lay.K, lay.N, M, variant)), dtype=torch.uint8,
+                              device="cuda")
+    _measure.linear_forced(lay, xd, M, out, scratch, torch.cuda.current_stream().cuda_stream, variant)
+    if not sync:
+        return out
+    torch.cuda.synchronize()
+    return _lib.to_host_u16(out)
+
+
 def announce(name: str):
     print("[gpu-case] %s" % name, file=sys.__stderr__, flush=True)

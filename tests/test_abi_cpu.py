@@ -189,16 +189,16 @@ def test_head_validation_and_scratch():
 
 def test_noalloc_refuses_oversize_before_any_device_work():
     """The size check of the allocation-free entry point comes before the
-    device is touched: a prefill call far beyond its 32 MiB array is refused
+    device is touched: a prefill call far beyond its 48 MiB array is refused
     here, with no GPU."""
     L = X.lib()
     layer = X.Exl3Layer(0x1000, 0x1000, 0x1000, None, None, 5120, 17408, 4)
     st = L.exl3_linear_noalloc(ctypes.byref(layer), 0x1000, 2048, 0x2000, 128, None)
     assert st == X.EXL3_ESCRATCH
-    assert "exl3_linear_noalloc holds 33554432" in L.exl3_strerror(st).decode()
+    assert "exl3_linear_noalloc holds 50331648" in L.exl3_strerror(st).decode()
     assert L.exl3_linear_noalloc(ctypes.byref(layer), None, 16, 0x2000, 128, None) == X.EXL3_EINVAL
     assert L.exl3_linear_noalloc(ctypes.byref(layer), 0x1000, 0, 0x2000, 128, None) == X.EXL3_OK
-    assert X.NOALLOC_SCRATCH_BYTES == 32 * 1024 * 1024
+    assert X.NOALLOC_SCRATCH_BYTES == 48 * 1024 * 1024
 
 
 def measure_declared_functions():

@@ -88,10 +88,11 @@ def test_linear_both_paths(T, X, cb, bits, M):
     x = WL.activations(34, M, K)
     ref = O.exl3_linear(x, L, cb)
     lay = X.Layer.from_numpy(L, cb)
-    fused = host16(X.linear(dev16(x), lay, prefill_min_m=0))
-    prefill = host16(X.linear(dev16(x), lay, prefill_min_m=1))
-    H.assert_rows_close(fused, ref, what="fused")
-    H.assert_rows_close(prefill, ref, what="prefill")
+    for r in ("fused", "recon") + (("dq",) if bits == 4 else ()):
+        H.assert_rows_close(H.linear_forced(lay, x, r), ref, what=r)
+    for pm in (0, 1):  # the dispatch at this width
+        want = H.linear_forced(lay, x, H.route(bits, M, pm))
+        assert np.array_equal(host16(X.linear(dev16(x), lay, prefill_min_m=pm)), want), pm
 
 
 @pytest.mark.parametrize("bits,M,pm", [(6, 1, 128), (6, 16, 128), (6, 2048, 128), (2, 16, 128), (8, 64, 128)])

@@ -88,8 +88,10 @@ def test_prefill_config(T, X, cb, geom):
         ref = O.exl3_linear(x, L, cb, rows)
         y = gpu_linear(X, lay, x, 128)
         H.assert_rows_close(y[rows], ref, what="prefill M=%d" % M)
-        if M == 128:  # at the threshold the fused path must agree too
-            H.assert_rows_close(gpu_linear(X, lay, x, 0)[rows], ref, what="fused M=128")
+        if H.route(4, M, 128) != "recon":  # the dequant-GEMM's rows: reconstruct + GEMM forced too
+            H.assert_rows_close(H.linear_forced(lay, x, "recon")[rows], ref, what="recon M=%d" % M)
+        if M == 128:  # at the threshold the decode-GEMM must agree too
+            H.assert_rows_close(H.linear_forced(lay, x, "fused")[rows], ref, what="fused M=128")
 
 
 def test_wide_config(T, X, cb):

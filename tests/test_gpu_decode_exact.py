@@ -32,8 +32,12 @@ def X(T):
 
 
 def run(X, lay, x, pm):
+    """pm: a threshold for exl3_linear's dispatch, or the name of a kernel
+    sequence to force."""
     from trellis_quantized_linear_had_amd import _lib
 
+    if isinstance(pm, str):
+        return H.linear_forced(lay, x, pm)
     return _lib.to_host_u16(X.linear(_lib.to_device_u16(x), lay, prefill_min_m=pm))
 
 
@@ -53,7 +57,7 @@ def check_all_k(X, L, K, N, bits, M, pms, what):
                 if not np.array_equal(got, want):
                     bad = np.argwhere(got != want)
                     m, n = bad[0]
-                    raise AssertionError("%s %s pm=%d: %d outputs differ; first at row %d (k=%d), column %d"
+                    raise AssertionError("%s %s pm=%s: %d outputs differ; first at row %d (k=%d), column %d"
                                          % (what, kind, pm, len(bad), m, ks[m], n))
 
 
@@ -61,12 +65,16 @@ def check_all_k(X, L, K, N, bits, M, pms, what):
 @pytest.mark.parametrize("N", [128, 1152, 2560])
 @pytest.mark.parametrize("M", [16, 40, 100])
 def test_fused_decode_states_bit_exact(T, X, bits, N, M):
-    """Fused path forced (prefill_min_m = 0); at M = 40 also the prefill path
-    (forced, prefill_min_m = 1) on the same rows."""
+    """The fused side (prefill_min_m = 0), the decode-GEMM forced where that
+    side takes the dequant-GEMM (4 bits, M = 100), and at M = 40 also the
+    prefill side (prefill_min_m = 1) on the same rows."""
     K = 256
     H.announce("exact decode bits=%d K%d N%d M=%d" % (bits, K, N, M))
     L = E.unit_layer(60 + bits, K, N, bits)
-    check_all_k(X, L, K, N, bits, M, (0, 1) if M == 40 else (0,), "K%d N%d bits=%d M=%d" % (K, N, bits, M))
+    pms = (0, 1) if M == 40 else (0,)
+    if H.route(bits, M, 0) != "fused":
+        pms += ("fused",)
+    check_all_k(X, L, K, N, bits, M, pms, "K%d N%d bits=%d M=%d" % (K, N, bits, M))
 
 
 def test_fused_decode_states_bit_exact_full_geometry(T, X):

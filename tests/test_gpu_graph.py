@@ -59,7 +59,8 @@ def _replays_match_eager(torch, call, inputs, outputs, fresh_inputs, other_work)
             assert torch.equal(o, e), "replay %d differs from the eager result" % rep
 
 
-@pytest.mark.parametrize("M,pm", [(1, 128), (2, 128), (4, 128), (8, 128), (16, 128), (256, 128)])
+@pytest.mark.parametrize("M,pm", [(1, 128), (2, 128), (4, 128), (8, 128), (16, 128), (64, 128), (256, 128),
+                                  (1100, 128)])
 def test_linear_graph_replay_bit_identical(T, M, pm):
     import torch
 

@@ -78,7 +78,7 @@ def run_head(T, X, x, lay, n_valid, M, ld, pm):
 
 @pytest.mark.parametrize("bits", [4, 6])
 @pytest.mark.parametrize("n_valid", [777, 1024, 1, 129])
-@pytest.mark.parametrize("M", [1, 5, 16, 130])
+@pytest.mark.parametrize("M", [1, 5, 16, 64, 130])
 def test_head_small(T, X, cb, bits, n_valid, M):
     H.announce("head bits=%d K256 N1024 n_valid=%d M=%d" % (bits, n_valid, M))
     K, N = 256, 1024

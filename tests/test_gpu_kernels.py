@@ -136,20 +136,23 @@ def run_linear(X, L, cb, x, pm):
     return host16(X.linear(dev16(x), lay, prefill_min_m=pm))
 
 
-@pytest.mark.parametrize("M", [1, 5, 16, 17, 128, 130, 300])
-def test_linear_tiny_both_paths(T, X, cb, M):
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 47, 48, 64, 127, 128, 130, 300, 1024, 1025])
+def test_linear_tiny_every_route(T, X, cb, M):
+    """Each kernel sequence (forced) against the oracle, and the dispatch:
+    the default threshold, 0 (fused side only) and 1 (prefill side only)
+    each give the forced output of the sequence the rule names, bit for bit."""
     H.announce("linear tiny K256 N256 M=%d" % M)
     K = N = 256
     L = WL.layer(WL.SEED_TINY, K, N)
+    lay = X.Layer.from_numpy(L, cb)
     x = WL.activations(WL.SEED_TINY, M, K)
     ref = O.exl3_linear(x, L, cb)
-    fused = run_linear(X, L, cb, x, 0)
-    prefill = run_linear(X, L, cb, x, 1)
-    default = run_linear(X, L, cb, x, 128)
-    H.assert_rows_close(fused, ref, what="fused")
-    H.assert_rows_close(prefill, ref, what="prefill")
-    H.assert_rows_close(fused, prefill, what="fused vs prefill")
-    assert np.array_equal(default, prefill if M >= 128 else fused)
+    out = {r: H.linear_forced(lay, x, r) for r in ("fused", "recon", "dq")}
+    for r, y in out.items():
+        H.assert_rows_close(y, ref, what=r)
+    H.assert_rows_close(out["fused"], out["recon"], what="fused vs recon")
+    for pm in (128, 0, 1):
+        assert np.array_equal(run_linear(X, L, cb, x, pm), out[H.route(4, M, pm)]), pm
 
 
 def test_linear_deterministic(T, X, cb):
@@ -172,13 +175,16 @@ def test_prefill_gemm_repeatable(T, X, cb, K, N, M):
     H.announce("prefill repeatable K%d N%d M%d" % (K, N, M))
     import torch
 
+    from trellis_quantized_linear_had_amd import _measure
+
     L = WL.layer(26, K, N)
     lay = X.Layer.from_numpy(L, cb)
     x = dev16(WL.activations(26, M, K))
-    scr = torch.empty(X.linear_scratch_bytes(K, N, M), dtype=torch.uint8, device="cuda")
+    scr = torch.empty(_measure.linear_scratch_bytes(K, N, M, _measure.VARIANT_RECON_GEMM), dtype=torch.uint8,
+                      device="cuda")
     outs = [torch.empty((M, N), dtype=torch.int16, device="cuda") for _ in range(8)]
-    for o in outs:
-        X.linear(x, lay, scratch=scr, out=o)
+    for o in outs:  # reconstruct + GEMM forced (at M = 200 the dispatch picks the dequant-GEMM)
+        H.linear_forced(lay, x, "recon", out=o, scratch=scr, sync=False)
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
@@ -191,7 +197,7 @@ def test_linear_two_slices(T, X, cb):
     x = WL.activations(26, M, K)
     rows = np.array([0, 1, 64, 128, 129], np.int64)
     ref = O.exl3_linear(x, L, cb, rows)
-    got = run_linear(X, L, cb, x, 128)
+    got = H.linear_forced(X.Layer.from_numpy(L, cb), x, "recon")
     H.assert_rows_close(got[rows], ref)
 
 
@@ -206,9 +212,10 @@ def test_linear_prefill_gemm_tail(T, X, cb, K, N, M):
     x = WL.activations(28, M, K)
     rows = np.unique(np.array([0, 1, 31, 32, 127, 128, 255, 256, 257, M // 2, M - 2, M - 1], np.int64) % M)
     ref = O.exl3_linear(x, L, cb, rows)
-    got = run_linear(X, L, cb, x, 1)
+    lay = X.Layer.from_numpy(L, cb)
+    got = H.linear_forced(lay, x, "recon")
     H.assert_rows_close(got[rows], ref)
-    again = run_linear(X, L, cb, x, 1)
+    again = H.linear_forced(lay, x, "recon")
     assert np.array_equal(got, again)  # the piece order is fixed: bit-identical reruns
 
 
@@ -245,11 +252,12 @@ def test_linear_zero_codes_rank_one(T, X, cb):
     K, N = 512, 640
     L = WL.layer(33, K, N)
     L["codes"] = np.zeros_like(L["codes"])
+    lay = X.Layer.from_numpy(L, cb)
     for M in (3, 130):
         x = WL.activations(33, M, K)
         ref = O.exl3_linear(x, L, cb)
-        H.assert_rows_close(run_linear(X, L, cb, x, 0), ref, what="fused M=%d" % M)
-        H.assert_rows_close(run_linear(X, L, cb, x, 1), ref, what="prefill M=%d" % M)
+        for r in ("fused", "recon", "dq"):
+            H.assert_rows_close(H.linear_forced(lay, x, r), ref, what="%s M=%d" % (r, M))
 
 
 def test_linear_without_signs(T, X, cb):
@@ -349,14 +357,15 @@ def test_logits_aligned_width_mask_is_noop(T, X):
     assert np.array_equal(am, ref_am)
 
 
-@pytest.mark.parametrize("M,pm", [(1, 128), (16, 128), (130, 128)])
-def test_linear_largest_k(T, X, cb, M, pm):
+@pytest.mark.parametrize("M,route", [(1, None), (16, None), (130, None), (130, "recon"), (64, "fused")])
+def test_linear_largest_k(T, X, cb, M, route):
     """K = 65408, the largest K the library takes (an fp16 weight slice of
-    K x 32768 columns stays within 32-bit byte offsets), on both paths."""
-    H.announce("linear K65408 N256 M=%d pm=%d" % (M, pm))
+    K x 32768 columns stays within 32-bit byte offsets), on every route
+    (the dispatch's at M = 1, 16 and 130, the others forced)."""
+    H.announce("linear K65408 N256 M=%d route=%s" % (M, route))
     K, N = 65408, 256
     L = WL.layer(27, K, N)
     x = WL.activations(27, M, K)
-    y = run_linear(X, L, cb, x, pm)
+    y = run_linear(X, L, cb, x, 128) if route is None else H.linear_forced(X.Layer.from_numpy(L, cb), x, route)
     rows = np.unique(np.array([0, M // 2, M - 1], np.int64))
     H.assert_rows_close(y[rows], O.exl3_linear(x, L, cb, rows))

@@ -37,8 +37,10 @@ def both(T, X, lay, x, pm):
 
 @pytest.mark.parametrize("K,N,Ms,pm", [
     (5120, 17408, (16, 4), 128),     # the decode configuration: prologue-rotation fused path
-    (5120, 17408, (100, 33), 0),     # fused path with row groups, forced
-    (256, 256, (200, 130), 128),     # prefill path (reconstruct + GEMM)
+    (5120, 17408, (33, 20), 0),      # decode-GEMM with row groups, forced fused side
+    (17408, 5120, (127, 64), 128),   # dequant-GEMM with its split-K tail, the largest fused-side scratch
+    (256, 256, (200, 130), 128),     # dequant-GEMM on the prefill side
+    (256, 256, (1100, 1030), 128),   # prefill path (reconstruct + GEMM)
 ])
 def test_noalloc_matches_linear_two_calls(T, X, K, N, Ms, pm):
     lay = X.Layer.from_numpy(WL.layer(81, K, N), WL.codebook())

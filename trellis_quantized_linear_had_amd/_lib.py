@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libexl3.so")
 EXL3_OK, EXL3_EINVAL, EXL3_ESHAPE, EXL3_ESCRATCH, EXL3_EWIDTH, EXL3_EHIP, EXL3_EARCH = range(7)
 LAYOUT_KN, LAYOUT_NK = 0, 1
 MAX_CHUNK_COLS = 32768
-NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
+NOALLOC_SCRATCH_BYTES = 48 * 1024 * 1024
 DEFAULT_PREFILL_MIN_M = 128
 
 EXPORTS = (

@@ -73,6 +73,15 @@ def check(status: int) -> None:
     raise RuntimeError("exl3 status %d: %s" % (status, msg))
 
 
+def linear_forced(layer, x, M, y, scratch, stream, variant):
+    """One exl3_linear call (device tensors x, y, scratch) with the kernel
+    sequence forced to `variant` instead of the row-count dispatch; scratch
+    holds linear_scratch_bytes(K, N, M, variant). Nothing is timed."""
+    used = ctypes.c_int(0)
+    check(mlib().exl3m_linear_marked(layer.c, x.data_ptr(), M, y.data_ptr(), scratch.data_ptr(), scratch.numel(),
+                                     128, stream, DECODE, 0, None, None, ctypes.byref(used), variant))
+
+
 class KernelTimer:
     """Event pairs around every launch of one kind inside library calls.
 
@@ -108,9 +117,7 @@ class KernelTimer:
 
     def linear_variant(self, layer, x, M, y, scratch, stream, variant):
         """One exl3_linear call with the kernel sequence forced, unmarked."""
-        used = ctypes.c_int(0)
-        check(mlib().exl3m_linear_marked(layer.c, x.data_ptr(), M, y.data_ptr(), scratch.data_ptr(), scratch.numel(),
-                                         128, stream, DECODE, 0, None, None, ctypes.byref(used), variant))
+        linear_forced(layer, x, M, y, scratch, stream, variant)
 
     def head(self, layer, x, M, n_valid, lg, ld, am, scratch, prefill_min_m, stream, kind):
         off, s, e = self._slot()

@@ -276,24 +276,27 @@ DecodeLayout decode_layout(int32_t K, int32_t N, int64_t M, int32_t bits) {
   return l;
 }
 
-// Dequant-in-GEMM plan: row fragments per pass (the fewest 32-row fragments
-// that hold M, at most 8), 256-column units, and the split between whole
-// units and K-split tail units that minimises the modelled time: rounds of
-// 256 CUs, each as long as its workgroups' 16-k steps (the larger of the
-// LDS-gather time of four waves and the MFMA time per step, measured
-// 0.24 and 0.06 nqb us) plus a fixed cost for the codebook load and the
-// output stage, plus the tail's fp32 partials written and read back.
-DqPlan plan_dq(int32_t K, int32_t N, int64_t M, bool whole = false) {
+// Dequant-in-GEMM plan: row fragments per pass (1, 2, 4 or 8 fragments of
+// 32 rows), 256-column units, and the split between whole units and K-split
+// tail units, the combination that minimises the modelled time: rounds of
+// 256 CUs, each as long as its workgroups' 16-k steps plus a fixed cost for
+// the codebook load and the output stage, plus the tail's fp32 partials
+// written and read back. The step costs (0.27, 0.32, 0.40 and 0.52 us for 1,
+// 2, 4 and 8 fragments) are the slopes of whole-unit runs over K at the MLP
+// geometries: the four waves' LDS gathers bound one fragment, the MFMAs and
+// the shared operand loads the larger passes.
+DqPlan plan_dq_rows(int32_t K, int32_t N, int64_t M, int nqb, bool whole, double& best) {
+  static constexpr double kStepUs[9] = {0, 0.27, 0.32, 0, 0.40, 0, 0, 0, 0.52};
   DqPlan p;
-  p.nqb = M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8;
-  const int R = 32 * p.nqb;
+  p.nqb = nqb;
+  const int R = 32 * nqb;
   p.passes = (int32_t)((M + R - 1) / R);
   p.pblocks = (N + 255) / 256;
   const int ksub = K / 16;
   const int64_t units = (int64_t)p.passes * p.pblocks;
-  const double step_us = std::max(0.24, 0.06 * p.nqb), wg_us = 3.0;
+  const double step_us = kStepUs[nqb], wg_us = 3.0;
   auto rounds = [](int64_t wgs) { return (double)((wgs + 255) / 256); };
-  double best = 1e300;
+  best = 1e300;
   p.full = (int32_t)units;
   p.tail = 0;
   p.tail_ks = 1;
@@ -321,6 +324,23 @@ DqPlan plan_dq(int32_t K, int32_t N, int64_t M, bool whole = false) {
     }
   }
   return p;
+}
+
+// The least modelled time over the row-fragment counts that leave no whole
+// fragment of a pass empty (a pass of R rows serves M in ceil(M / R) passes).
+DqPlan plan_dq(int32_t K, int32_t N, int64_t M, bool whole = false) {
+  DqPlan best_plan{};
+  double best = 1e300;
+  for (int nqb : {1, 2, 4, 8}) {
+    if (nqb > 1 && 32 * (nqb / 2) >= M) break;
+    double t;
+    const DqPlan p = plan_dq_rows(K, N, M, nqb, whole, t);
+    if (t < best - 1e-9) {
+      best = t;
+      best_plan = p;
+    }
+  }
+  return best_plan;
 }
 
 struct DqLayout {
@@ -361,27 +381,61 @@ const char* exl3_strerror(int status) {
 
 namespace {
 
+// The kernel sequence of one call. At 4 bits the dequant-GEMM takes the row
+// counts where it measured fastest on both MLP geometries: from 48 rows on
+// the fused side (the decode-GEMM below) and up to 1024 rows on the prefill
+// side (reconstruct + GEMM above). A forced variant overrides the choice.
+enum Route { kRouteDecode, kRouteReconstructGemm, kRouteDequantGemm, kRouteDequantGemmWhole };
+constexpr int64_t kDqFusedMinRows = 48, kDqPrefillMaxRows = 1024;
+
+Route route_of(int32_t bits, int64_t M, int32_t prefill_min_m, int variant) {
+  switch (variant) {
+    case kVariantFused:
+      return kRouteDecode;
+    case kVariantReconstructGemm:
+      return kRouteReconstructGemm;
+    case kVariantDequantGemm:
+      return kRouteDequantGemm;
+    case kVariantDequantGemmWhole:
+      return kRouteDequantGemmWhole;
+    default:
+      break;
+  }
+  const bool dq_ok = bits == 4;
+  if (use_prefill(M, prefill_min_m)) return dq_ok && M <= kDqPrefillMaxRows ? kRouteDequantGemm : kRouteReconstructGemm;
+  return dq_ok && M >= kDqFusedMinRows ? kRouteDequantGemm : kRouteDecode;
+}
+
+size_t route_scratch_bytes(Route r, int32_t K, int32_t ncols, int64_t M, int32_t bits) {
+  switch (r) {
+    case kRouteReconstructGemm:
+      return prefill_layout(K, ncols, M).total;
+    case kRouteDequantGemm:
+    case kRouteDequantGemmWhole:
+      return dq_layout(K, ncols, M, r == kRouteDequantGemmWhole).total;
+    default:
+      return decode_layout(K, ncols, M, bits).total;
+  }
+}
+
 // The layer over its leading ncols columns (ncols a multiple of 128, at most
 // N), written to y with leading dimension ldy. Arguments are validated by the
-// callers; scratch holds linear_cols_scratch_bytes(K, ncols, M, pm).
+// callers; scratch holds linear_cols_scratch_bytes(K, ncols, M, pm). The
+// size does not depend on the width, so it covers the route taken at 4 bits
+// and the one taken at the other widths (whose decode plans also differ).
 size_t linear_cols_scratch_bytes(int32_t K, int32_t ncols, int64_t M, int32_t prefill_min_m,
                                  int variant = kVariantAuto) {
-  if (variant == kVariantDequantGemm || variant == kVariantDequantGemmWhole)
-    return dq_layout(K, ncols, M, variant == kVariantDequantGemmWhole).total;
-  if (variant == kVariantReconstructGemm || (variant == kVariantAuto && use_prefill(M, prefill_min_m)))
-    return prefill_layout(K, ncols, M).total;
-  // the decode path's partial slices depend on the plan, which differs
-  // between 4 bits and the other widths: enough for either
-  return std::max(decode_layout(K, ncols, M, 4).total, decode_layout(K, ncols, M, 3).total);
+  return std::max(route_scratch_bytes(route_of(4, M, prefill_min_m, variant), K, ncols, M, 4),
+                  route_scratch_bytes(route_of(3, M, prefill_min_m, variant), K, ncols, M, 3));
 }
 
 int linear_cols(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, int64_t ldy, int32_t ncols,
                 char* sb, int32_t prefill_min_m, hipStream_t stream, Marks* marks) {
   const int32_t K = L->K, N = L->N;
-  const int variant = marks ? marks->variant : kVariantAuto;
-  if (variant == kVariantDequantGemm || variant == kVariantDequantGemmWhole) {
+  const Route route = route_of(L->bits, M, prefill_min_m, marks ? marks->variant : kVariantAuto);
+  if (route == kRouteDequantGemm || route == kRouteDequantGemmWhole) {
     if (L->bits != 4) return fail(EXL3_ESHAPE, "the dequant-GEMM takes 4-bit codes only");
-    const DqLayout l = dq_layout(K, ncols, M, variant == kVariantDequantGemmWhole);
+    const DqLayout l = dq_layout(K, ncols, M, route == kRouteDequantGemmWhole);
     uint16_t* xf = (uint16_t*)(sb + l.xf_off);
     float* part = (float*)(sb + l.part_off);
     EXL3_TRY(launch_had128_frag(x, xf, M, K, L->sign_k, stream), "input rotation");
@@ -390,10 +444,7 @@ int linear_cols(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
                            (int32_t)M, l.plan, stream),
              "dequant gemm");
     EXL3_TRY(mark_end(marks, kMarkDecode, stream), "event record");
-    return EXL3_OK;
-  }
-  const bool prefill = variant == kVariantReconstructGemm || (variant == kVariantAuto && use_prefill(M, prefill_min_m));
-  if (prefill) {
+  } else if (route == kRouteReconstructGemm) {
     const PrefillLayout l = prefill_layout(K, ncols, M);
     uint16_t* xr = (uint16_t*)(sb + l.xr_off);
     uint16_t* wt = (uint16_t*)(sb + l.w_off);
@@ -428,12 +479,13 @@ int linear_cols(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
 // own_scratch: the library supplies the scratch (the allocation-free entry
 // point), so the caller's scratch argument is not checked.
 int validate_call(const exl3_layer* L, const uint16_t* x, int64_t M, const void* y, const void* scratch,
-                  int32_t prefill_min_m, bool own_scratch = false) {
+                  int32_t prefill_min_m, bool own_scratch = false, int variant = kVariantAuto) {
   int st = validate_layer(L);
   if (st) return st;
   if (M < 0) return fail(EXL3_EINVAL, "M = %lld is negative", (long long)M);
   if (prefill_min_m < 0) return fail(EXL3_EINVAL, "prefill_min_m = %d is negative", prefill_min_m);
-  if (M > 0x7FFFFFFF) return fail(EXL3_EINVAL, "M = %lld is too large", (long long)M);
+  // rows are padded to multiples of 32 in int32
+  if (M > 0x7FFFFFE0) return fail(EXL3_EINVAL, "M = %lld is too large", (long long)M);
   if (M == 0) return EXL3_OK;
   if (!x || !y) return fail(EXL3_EINVAL, "x or the output is NULL");
   if (!own_scratch && !scratch) return fail(EXL3_EINVAL, "scratch is NULL");
@@ -441,7 +493,7 @@ int validate_call(const exl3_layer* L, const uint16_t* x, int64_t M, const void*
     return fail(EXL3_EINVAL, "x and the output must be 16-byte aligned and scratch 256-byte aligned");
   // the prefill GEMM addresses the rotated input (M x K fp16) with 32-bit
   // byte offsets
-  if (use_prefill(M, prefill_min_m) && M * L->K * 2 > (int64_t)UINT32_MAX)
+  if (route_of(L->bits, M, prefill_min_m, variant) == kRouteReconstructGemm && M * L->K * 2 > (int64_t)UINT32_MAX)
     return fail(EXL3_ESHAPE, "M = %lld, K = %d: the prefill path needs M * K * 2 below 4 GiB", (long long)M, L->K);
   return EXL3_OK;
 }
@@ -501,10 +553,10 @@ namespace exl3 {
 int linear_entry(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* scratch, size_t scratch_bytes,
                  int32_t prefill_min_m, hipStream_t stream, Marks* marks) {
   g_msg[0] = 0;
-  int st = validate_call(L, x, M, y, scratch, prefill_min_m);
+  const int variant = marks ? marks->variant : (int)kVariantAuto;
+  int st = validate_call(L, x, M, y, scratch, prefill_min_m, false, variant);
   if (st || M == 0) return st;
-  const size_t need =
-      linear_cols_scratch_bytes(L->K, L->N, M, prefill_min_m, marks ? marks->variant : (int)kVariantAuto);
+  const size_t need = linear_cols_scratch_bytes(L->K, L->N, M, prefill_min_m, variant);
   if (scratch_bytes < need)
     return fail(EXL3_ESCRATCH, "scratch has %zu bytes; this call needs %zu", scratch_bytes, need);
   st = check_device();
