@@ -106,6 +106,21 @@ def test_linear_full_size_sampled_rows(T, X, cb, bits, M, pm):
     H.assert_rows_close(y[rows], O.exl3_linear(x, L, cb, rows))
 
 
+@pytest.mark.parametrize("M", [512, 300])
+def test_linear_fused_many_passes_other_width(T, X, cb, M):
+    """The fused decode path forced (prefill_min_m = 0) at 6 bits on the MLP
+    geometry with many passes of four row groups (the reduction of every pass
+    but the last goes through the LDS left beside the codebook); sampled rows
+    in every 64-row block against the oracle."""
+    H.announce("linear bits=6 K5120 N17408 M=%d fused (sampled rows)" % M)
+    K, N = 5120, 17408
+    L = WL.layer(39, K, N, 0, 6)
+    x = WL.activations(39, M, K)
+    rows = np.unique(np.concatenate([[0, M - 1], np.arange(5, M, 64)])).astype(np.int64)
+    y = host16(X.linear(dev16(x), X.Layer.from_numpy(L, cb), prefill_min_m=0))
+    H.assert_rows_close(y[rows], O.exl3_linear(x, L, cb, rows))
+
+
 def test_linear_deterministic_other_width(T, X, cb):
     H.announce("linear determinism bits=5")
     K, N = 1024, 2048

@@ -136,8 +136,8 @@ bool use_prefill(int64_t M, int32_t prefill_min_m) { return prefill_min_m > 0 &&
 // gets the same work, the grid fills at most whole rounds of 256 CUs, and the
 // modelled cost (per round: the workgroup's tile-steps and the padded
 // per-wave share, once per pass of G row groups, plus a round cost of about
-// 4 us for the codebook load, prologue and reduction; plus
-// the fp32 partial traffic) is least. The LDS gathers are the bound, so a pass
+// 4 us for the codebook load, prologue and reduction; plus the fp32 partial
+// traffic and the rows of Xr that every column slice reads again) is least. The LDS gathers are the bound, so a pass
 // of G groups costs about one gather pass (the extra MFMAs and A fragments add
 // a few per cent per group). With x_in_lds (one group) the workgroup's k range
 // is a whole number of 128-element blocks and its rotated slice of the M rows
@@ -192,7 +192,10 @@ static bool plan_decode_search(int32_t K, int32_t N, int64_t M, bool x_in_lds, i
             (double)rounds *
             (30.0 * passes * gfac * ((double)ntpw_real * kpw + 16.0 * kpw_wave * nt_inst) + 10000.0);
         const double partial = (double)ks * M * N * 8.0 / 2083.0;
-        const double cost = decode + partial;
+        // every column slice reads all M rows of Xr over its k range again
+        // (ns M K fp16 through the L2s, about 10 TB/s)
+        const double xread = (double)ns * M * K * 2.2e-4;
+        const double cost = decode + partial + xread;
         if (cost < best_cost - 1e-9) {
           best_cost = cost;
           best = DecodePlan{ks, ns, kpw, ntpw_real, wn, wk, nt_inst, x_in_lds ? 1 : 0, G};

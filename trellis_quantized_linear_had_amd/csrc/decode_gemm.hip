@@ -237,7 +237,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
   // 4*(lane>>4) + r, column lane & 15. `dead`: no gather follows, so the whole
   // LDS block holds one slot per (wave, tile) and all waves store at once, in
   // passes of `chunk` tiles; otherwise (the codebook is still needed) the
-  // waves accumulate through the small reduction buffer one at a time.
+  // slots go to the 32 KiB beside the codebook: all at once when the wk slots
+  // of every tile fit there, else the waves accumulate one at a time.
   const int eoff = 4 * (lane >> 4) * 16 + c;
   const int wt_off = wt_begin - t_begin;
   auto reduce_store = [&](const f32x4 (&accg)[NT], int m0g, bool dead) {
@@ -263,6 +264,23 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_gemm_kernel(const uint16_t
         }
         __syncthreads();
       }
+    } else if (plan.wk * tw * 256 <= 8192) {
+      // The wk slots of every tile fit beside the codebook: all waves store
+      // at once and every thread sums the slots in wave order (the same sums
+      // as the one-wave-at-a-time loop below, without its wk barriers).
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (t < nt_w)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[(wk_idx * tw + wt_off + t) * 256 + eoff + r * 16] = accg[t][r];
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < tw * 256; idx += DEC_THREADS) {
+        float sum = red[idx];
+        for (int j = 1; j < plan.wk; ++j) sum += red[j * tw * 256 + idx];
+        const int t = idx >> 8, e = idx & 255, m = m0g + (e >> 4), n = (t_begin + t) * 16 + (e & 15);
+        if (m < M) partials[((int64_t)ks * M + m) * N + n] = sum;
+      }
+      __syncthreads();
     } else {
       const int rbase = wt_off * 256 + eoff;
       for (int j = 0; j < plan.wk; ++j) {
