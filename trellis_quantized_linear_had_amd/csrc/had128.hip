@@ -46,50 +46,58 @@ __global__ __launch_bounds__(256) void had128_kernel(const uint16_t* in, uint16_
 // MFMA fragment order for Mpad = ceil(M / 32) * 32 rows, rows past M zero.
 // Block (qb, t) of 32 rows x 16 k is 1 KiB at halves (qb * K/16 + t) * 512;
 // lane l = row % 32 + 32 * ((k % 16) / 8) of it holds k .. k + 7 of its row.
-// Items (128-column block b, row) run row-fastest, so the four 16-lane groups
-// of a wave are four consecutive rows of one block and every store
-// instruction writes 64 contiguous bytes per fragment position.
+// One workgroup per (32-row block qb, 128-column block b): 16 lanes per row
+// rotate as in had128_kernel, each lane two rows 16 apart (both loads in
+// flight together), the results meet in LDS in fragment order, and each of
+// the 4 waves then stores two whole 1 KiB fragment blocks, one contiguous
+// store instruction each.
 template <bool PRE>
 __global__ __launch_bounds__(256) void had128_frag_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
-                                                          int32_t M, int32_t Mpad, int32_t K,
-                                                          const uint16_t* __restrict__ sign_pre) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int q = (int)(gid & 15);
-  const int64_t nitems = (int64_t)Mpad * (K / 128);
-  const int64_t item_raw = gid >> 4;
-  // groups past the end compute a valid item and do not store
-  const int64_t item = item_raw < nitems ? item_raw : nitems - 1;
-  const int row = (int)(item % Mpad), b = (int)(item / Mpad);
+                                                          int32_t M, int32_t K, const uint16_t* __restrict__ sign_pre) {
+  __shared__ u32x4 frag[8 * 64];
+  const int nb = K / 128;
+  const int qb = (int)(blockIdx.x / nb), b = (int)(blockIdx.x % nb);
+  const int q = threadIdx.x & 15, r0 = threadIdx.x >> 4;
   const int64_t col0 = (int64_t)b * 128 + 8 * q;
-  // rows past M read row M - 1 and store zeros
-  u32x4 d = *reinterpret_cast<const u32x4*>(in + (int64_t)min(row, M - 1) * K + col0);
-  if (PRE) d ^= (*reinterpret_cast<const u32x4*>(sign_pre + col0) & 0x80008000u);
-  float v[8];
+  u32x4 d[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v[2 * j] = bits_lo_f16(d[j]);
-    v[2 * j + 1] = bits_hi_f16(d[j]);
+  for (int h = 0; h < 2; ++h)  // rows past M read row M - 1 and store zeros
+    d[h] = *reinterpret_cast<const u32x4*>(in + (int64_t)min(32 * qb + r0 + 16 * h, M - 1) * K + col0);
+  const u32x4 sg = PRE ? (*reinterpret_cast<const u32x4*>(sign_pre + col0) & 0x80008000u) : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = r0 + 16 * h;
+    const u32x4 x = d[h] ^ sg;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bits_lo_f16(x[j]);
+      v[2 * j + 1] = bits_hi_f16(x[j]);
+    }
+    wht128_16(v, q);
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * EXL3_INV_SQRT128, v[2 * j + 1] * EXL3_INV_SQRT128);
+    if (32 * qb + r >= M) o = (u32x4){0u, 0u, 0u, 0u};
+    frag[(q >> 1) * 64 + r + 32 * (q & 1)] = o;  // block t = 8 b + q / 2, lane r + 32 (q & 1)
   }
-  wht128_16(v, q);
-  u32x4 o;
+  __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * EXL3_INV_SQRT128, v[2 * j + 1] * EXL3_INV_SQRT128);
-  if (row >= M) o = (u32x4){0u, 0u, 0u, 0u};
-  const int64_t t = col0 / 16;
-  const int lf = row % 32 + 32 * (q & 1);
-  if (item_raw < nitems) *reinterpret_cast<u32x4*>(out + (((int64_t)(row / 32) * (K / 16) + t) * 64 + lf) * 8) = o;
+  for (int h = 0; h < 2; ++h) {
+    const int t = 2 * w + h;
+    *reinterpret_cast<u32x4*>(out + (((int64_t)qb * (K / 16) + 8 * b + t) * 64 + lane) * 8) = frag[t * 64 + lane];
+  }
 }
 
 hipError_t launch_had128_frag(const uint16_t* in, uint16_t* out, int64_t M, int32_t K, const uint16_t* sign_pre,
                               hipStream_t stream) {
-  const int64_t Mpad = (M + 31) / 32 * 32;
-  const int64_t threads = Mpad * (K / 128) * 16;
-  if (threads == 0) return hipSuccess;
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  const int64_t blocks = (M + 31) / 32 * (K / 128);
+  if (blocks == 0) return hipSuccess;
   if (sign_pre)
-    had128_frag_kernel<true><<<grid, 256, 0, stream>>>(in, out, (int32_t)M, (int32_t)Mpad, K, sign_pre);
+    had128_frag_kernel<true><<<(unsigned)blocks, 256, 0, stream>>>(in, out, (int32_t)M, K, sign_pre);
   else
-    had128_frag_kernel<false><<<grid, 256, 0, stream>>>(in, out, (int32_t)M, (int32_t)Mpad, K, sign_pre);
+    had128_frag_kernel<false><<<(unsigned)blocks, 256, 0, stream>>>(in, out, (int32_t)M, K, sign_pre);
   return hipGetLastError();
 }
 
