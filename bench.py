@@ -80,7 +80,8 @@ def parse():
                     help="instead of the bench line: time the three kernel sequences of exl3_linear (fused "
                          "decode-GEMM, reconstruct + GEMM, dequant-in-GEMM) over M on both MLP geometries, with the "
                          "main kernel alone, and print a markdown summary")
-    ap.add_argument("--pmc-workload", choices=("logits", "gemm", "decode", "reconstruct", "gemm_tail"), default=None,
+    ap.add_argument("--pmc-workload", choices=("logits", "gemm", "decode", "reconstruct", "gemm_tail", "dq"),
+                    default=None,
                     help="run only a counter-collection workload: two 1 GiB device copies (calibration) then "
                          "three calls of the named path; prints nothing else")
     return ap.parse_args()
@@ -373,6 +374,7 @@ def main():
 
 
 COPY_BYTES = 1 << 30
+DQ_PMC_M = 256
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "trellis_quantized_linear_had_amd", "csrc")
 # kernel name in the counter files, the key used in the bench line, and the
@@ -386,6 +388,10 @@ PMC_KERNELS = {
                     ("reconstruct.hip", "trellis.h", "common.h")),
     # the down-projection geometry, where all 160 tiles run as stream-K pieces
     "gemm_tail": ("exl3::gemm_had_kernel<1>", "gemm_had_kernel<1> K17408xN5120 M=2048", ("gemm_f16.hip", "common.h")),
+    # the dequant-GEMM at M = 256 (the dispatch's choice there): 68 units of 256 rows x 256 columns, each
+    # split in three k pieces
+    "dq": ("exl3::dqgemm_kernel<8, true>", "dqgemm_kernel<8,true> K5120xN17408 M=256",
+           ("dqgemm.hip", "dq_plan.h", "epilogue.h", "trellis.h", "common.h")),
 }
 
 
@@ -483,8 +489,8 @@ def pmc_workload(kind: str):
             _lib.check(lib.logits_pad_mask_argmax(xl.data_ptr(), LOGITS_M, K, wl.data_ptr(), w_rows, n_valid,
                                                   lg.data_ptr(), n_pad, am.data_ptr(), scr.data_ptr(), scr.numel(), sh))
     else:
-        pre = kind in ("gemm", "reconstruct", "gemm_tail")  # these run inside the prefill call
-        M = PREFILL_M if pre else max(DEC_M)
+        pre = kind in ("gemm", "reconstruct", "gemm_tail", "dq")  # these run inside the prefill call
+        M = DQ_PMC_M if kind == "dq" else PREFILL_M if pre else max(DEC_M)
         Kw, Nw = (N, K) if kind == "gemm_tail" else (K, N)
         layer = X.Layer.from_numpy(W.layer(W.SEED_PREFILL if pre else W.SEED_DECODE, Kw, Nw, 0), cb)
         x = _lib.to_device_u16(W.activations(W.SEED_PREFILL if pre else W.SEED_DECODE, M, Kw, 0))
