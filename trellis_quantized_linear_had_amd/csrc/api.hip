@@ -24,7 +24,7 @@
 
 namespace exl3 {
 hipError_t launch_had128_frag(const uint16_t* in, uint16_t* out, int64_t M, int32_t K, const uint16_t* sign_pre,
-                              hipStream_t stream);
+                              bool rows16, hipStream_t stream);
 hipError_t launch_had128(const uint16_t* in, uint16_t* out, int64_t rows, int64_t cols, const uint16_t* sign_pre,
                          const uint16_t* sign_post, hipStream_t stream);
 hipError_t launch_reconstruct_nk(const uint32_t* codes, const uint16_t* cb, const uint16_t* scale, int32_t K,
@@ -441,7 +441,7 @@ int linear_cols(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
     const DqLayout l = dq_layout(K, ncols, M, route == kRouteDequantGemmWhole);
     uint16_t* xf = (uint16_t*)(sb + l.xf_off);
     float* part = (float*)(sb + l.part_off);
-    EXL3_TRY(launch_had128_frag(x, xf, M, K, L->sign_k, stream), "input rotation");
+    EXL3_TRY(launch_had128_frag(x, xf, M, K, L->sign_k, false, stream), "input rotation");
     EXL3_TRY(mark_begin(marks, kMarkDecode, stream), "event record");
     EXL3_TRY(launch_dqgemm(xf, L->codes, L->codebook, L->scale, L->sign_n, y, ldy, part, K, ncols, N / 16,
                            (int32_t)M, l.plan, stream),
@@ -451,7 +451,7 @@ int linear_cols(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
     const PrefillLayout l = prefill_layout(K, ncols, M);
     uint16_t* xr = (uint16_t*)(sb + l.xr_off);
     uint16_t* wt = (uint16_t*)(sb + l.w_off);
-    EXL3_TRY(launch_had128_frag(x, xr, M, K, L->sign_k, stream), "input rotation");
+    EXL3_TRY(launch_had128_frag(x, xr, M, K, L->sign_k, true, stream), "input rotation");
     for (int32_t n0 = 0; n0 < ncols; n0 += l.chunk) {
       const int32_t nc = std::min(l.chunk, ncols - n0);
       EXL3_TRY(mark_begin(marks, kMarkReconstruct, stream), "event record");

@@ -78,6 +78,71 @@ __device__ __forceinline__ void rotate_store_block(f32x16 (&a)[4], int lane, int
     }
 }
 
+// The same output stage for a wave holding v_mfma_f32_16x16x32_f16
+// accumulators of one 128 (p) x 16 (q) block: a[i][r] = D[p][q] with (inside
+// the 128-row rotation block) p = 16 i + 4 (lane >> 4) + r, q = q0 + (lane & 15).
+// Index bits of p: 0,1 <- r; 2,3 <- lane bits 4,5; 4,5,6 <- i. Five stages in
+// registers, two across lanes 16 and 32 apart.
+__device__ __forceinline__ void rotate_store_block16(f32x4 (&a)[8], int lane, int pw, int q0, int P, int Q,
+                                                     uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
+                                                     const uint16_t* __restrict__ sign_n) {
+  const int lq = lane & 15, lg = lane >> 4;
+  // the 8 sign words go out before the butterflies (one memory round trip);
+  // without signs, row 0 of y (in bounds, then masked off) is read
+  u32x2 sg[8];
+  const uint32_t smask = sign_n ? 0x80008000u : 0u;
+  if (pw < P) {  // uniform over the wave
+    const uint16_t* sp = (sign_n ? sign_n : y) + n0 + pw;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sg[i] = *reinterpret_cast<const u32x2*>(sp + 16 * i + 4 * lg);
+  }
+#pragma unroll
+  for (int h = 1; h <= 2; h <<= 1)  // register bits r&1, r&2
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if ((r & h) == 0) {
+          const float u = a[i][r], v = a[i][r + h];
+          a[i][r] = u + v;
+          a[i][r + h] = u - v;
+        }
+#pragma unroll
+  for (int h = 1; h <= 4; h <<= 1)  // register bits of i
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & h) == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float u = a[i][r], v = a[i + h][r];
+          a[i][r] = u + v;
+          a[i + h][r] = u - v;
+        }
+#pragma unroll
+  for (int m = 16; m <= 32; m <<= 1) {  // lane bits 4, 5: the partner m lanes away
+    const float s = (lane & m) ? -1.f : 1.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float partner = __shfl_xor(a[i][r], m);
+        a[i][r] = __builtin_fmaf(s, a[i][r], partner);
+      }
+  }
+  if (pw >= P) return;
+  const int q = q0 + lq;
+  if (q >= Q) return;
+  uint16_t* yrow = y + (int64_t)q * ldy + n0 + pw;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    u32x2 o;
+    o[0] = pack_f16x2(a[i][0] * EXL3_INV_SQRT128, a[i][1] * EXL3_INV_SQRT128);
+    o[1] = pack_f16x2(a[i][2] * EXL3_INV_SQRT128, a[i][3] * EXL3_INV_SQRT128);
+    o ^= sg[i] & smask;
+    *reinterpret_cast<u32x2*>(yrow + 16 * i + 4 * lg) = o;
+  }
+}
+
 // The same output stage split for a block whose two 64-row halves sit in two
 // waves (the dequant-GEMM): each wave runs the six stages inside its half on
 // its tiles t[0], t[1] (p = 32 f + 8 (r >> 2) + 4 lhalf + (r & 3): register

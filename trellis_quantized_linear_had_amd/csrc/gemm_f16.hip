@@ -8,26 +8,29 @@
 //
 // Computing the transpose (p = output column n, q = input row m) puts the
 // 128-column rotation along the MFMA's row dimension, which a lane holds in
-// registers: six of its seven butterfly stages run in registers and one
-// crosses lanes 32 apart.
+// registers: five of its seven butterfly stages run in registers and two
+// cross lanes (16 and 32 apart).
 //
 // Tiling: 256 (p) x 256 (q) per workgroup, 64-wide k steps. 8 waves form
-// 2 (p) x 4 (q); each owns 128 p-rows (one rotation block, 4
-// v_mfma_f32_32x32x16_f16 row tiles) and 2 32-wide q tiles; two waves per
-// SIMD. A (W^T, shared by the 4 waves of a p half) goes from global memory
-// straight into LDS (global_load_lds_dwordx4, no register staging), two
-// stages, one barrier per k step. Inside a stage each 128-byte row is cut in
-// 16-byte chunks XOR-swizzled by ((row >> 1) & 7): the LDS serves a 16-byte
-// read 16 lanes at a time over 64 banks, and this key makes every group of 16
-// consecutive rows hit 16 distinct bank groups (zero bank-conflict cycles).
-// The swizzle is applied on the global side, because a direct-to-LDS load
-// writes lane i's 16 bytes at base + 16 i. B (the rotated x, shared by only
-// the 2 waves of a q quarter) does not pass through the LDS: the input
-// rotation stores it in MFMA fragment order (had128_frag_kernel: 32 rows x 16 k
-// per 1 KiB block, lane l holding row l % 32, k 8 (l / 32) .. + 8), so each
-// wave loads its B fragments straight into registers, one contiguous 1 KiB per
-// load instruction, one k step ahead. With both operands in LDS its reads and
-// writes matched the MFMA time per k step; without B they take 5/8 of it.
+// 2 (p) x 4 (q); each owns 128 p-rows (one rotation block, 8
+// v_mfma_f32_16x16x32_f16 row tiles) and 4 16-wide q tiles; two waves per
+// SIMD. The 16x16x32 shape does the work of the 32x32x16 one with the same
+// operand bytes per k, and under the chip's power limit it runs at a higher
+// clock (measured: an MFMA loop on random data 1.86 vs 1.65 PFLOP/s). A k step
+// is four half-steps h: k32 sub-step h / 2 on the p-tiles 4 (h % 2) .. + 3.
+// A (W^T, shared by the 4 waves of a p half) goes from global memory straight
+// into LDS (global_load_lds_dwordx4, no register staging), two stages, one
+// barrier per k step. Inside a stage each 128-byte row is cut in 16-byte
+// chunks XOR-swizzled by ((row >> 1) & 7): the LDS serves a 16-byte read 16
+// lanes at a time over 64 banks, and the 16 lanes of a fragment read (16
+// consecutive rows, one chunk) then hit 16 distinct bank groups. The swizzle
+// is applied on the global side, because a direct-to-LDS load writes lane i's
+// 16 bytes at base + 16 i. B (the rotated x, shared by only the 2 waves of a q
+// quarter) does not pass through the LDS: the input rotation stores it in
+// 16-row fragment order (had128_frag_kernel: 16 rows x 32 k per 1 KiB block,
+// lane l holding row l % 16, k 8 (l / 16) .. + 8), so each wave loads its B
+// fragments straight into registers, one contiguous 1 KiB per load
+// instruction, one k step ahead.
 //
 // Tail balance: tiles are dealt to the 256 CUs in rounds. The largest
 // multiple of 256 tiles runs whole; the k-steps of the remaining tiles are
@@ -50,11 +53,11 @@ namespace exl3 {
 #define G_BP 256
 #define G_BQ 256
 #define G_BK 64
-#define G_WQ 4
-#define G_QT 2
+#define G_PT 8   // 16-row p tiles per wave (128 rows)
+#define G_QT 4   // 16-wide q tiles per wave (64 columns)
 #define G_THREADS 512
 #define G_STAGE (G_BP * G_BK)  // halves per stage (A only)
-#define G_FRAG 512             // halves per 32 x 16 B fragment block (1 KiB)
+#define G_FRAG 512             // halves per 16 x 32 fragment block (1 KiB)
 #define G_CUS 256
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -100,26 +103,28 @@ __device__ __forceinline__ f16x8 load_frag(const uint16_t* p) {
   return v;
 }
 
-// Vector-memory loads one wave issues per k step, in issue order: B slots 0,
-// 1 and 2 (G_QT fragments each), the 4 direct-to-LDS loads of the next A
-// stage (32 rows per wave, 8 rows per instruction), B slot 3.
+// Vector-memory loads one wave issues per k step, in issue order: B slot 0
+// (the next k step's first k32 sub-step, G_QT fragments), the 4 direct-to-LDS
+// loads of the A stage after next (32 rows per wave, 8 rows per instruction),
+// B slot 1 (its second k32 sub-step).
 constexpr int kBLoads = G_QT;
 constexpr int kALoads = 4;
-constexpr int kLoadsPerStep = 4 * kBLoads + kALoads;
-// Before the MFMAs of sub-step s (s = 0, 1, 2) slot s must have landed. Issued
-// after it: slots s+1..2 of this k step, the A stage, slot 3, and the refills
-// of slots 0..s-1 issued in this k step -- the same count for every s.
-constexpr int wait_slot_count(int s) { return (2 - s) * kBLoads + kALoads + kBLoads + s * kBLoads; }
-constexpr int kWaitSlot = wait_slot_count(0);
-static_assert(wait_slot_count(1) == kWaitSlot && wait_slot_count(2) == kWaitSlot, "slot waits differ");
-// Before the barrier: slot 3 and the A stage (issued before it) have landed
-// once only the three refills issued since are outstanding.
-constexpr int kWaitStage = 3 * kBLoads;
-// Prologue, issued in steady-state order (A stage 0, slots 0..2, A stage 1,
-// slot 3): A stage 0 has landed once the loads after it are outstanding.
-constexpr int kWaitPrologue = kLoadsPerStep;
-static_assert(kWaitPrologue < 64 && kWaitSlot < kLoadsPerStep && kWaitStage < kWaitSlot,
+constexpr int kLoadsPerStep = 2 * kBLoads + kALoads;
+// Before half-step 0 slot 0 must have landed: issued after it, the A stage and
+// slot 1. Before half-step 2 slot 1 must have landed: issued after it, this
+// k step's refill of slot 0.
+constexpr int kWaitSlot0 = kALoads + kBLoads;
+constexpr int kWaitSlot1 = kBLoads;
+// Before the barrier the A stage (issued before slot 1's refill of the
+// previous k step) must have landed: issued after it, that refill and this
+// k step's refill of slot 0.
+constexpr int kWaitStage = 2 * kBLoads;
+// Prologue, issued in steady-state order (A stage 0, slot 0, A stage 1,
+// slot 1): A stage 0 has landed once the loads after it are outstanding.
+constexpr int kWaitPrologue = kBLoads + kALoads + kBLoads;
+static_assert(kWaitPrologue < 64 && kWaitSlot0 < kLoadsPerStep && kWaitSlot1 < kWaitSlot0 && kWaitStage < kLoadsPerStep,
               "vmcnt counts out of range (6 bits)");
+static_assert(kWaitPrologue == kLoadsPerStep, "the prologue issues one k step's loads after A stage 0");
 
 // Waits until at most N vector-memory loads are outstanding. The slot's
 // registers are named as read and written by the wait, so the compiler can
@@ -127,35 +132,30 @@ static_assert(kWaitPrologue < 64 && kWaitSlot < kLoadsPerStep && kWaitStage < kW
 // load may still be in flight.
 template <int N>
 __device__ __forceinline__ void wait_slot(f16x8 (&slot)[G_QT]) {
-  static_assert(G_QT == 2, "one operand per fragment of the slot");
-  asm volatile("s_waitcnt vmcnt(%2)" : "+v"(slot[0]), "+v"(slot[1]) : "n"(N) : "memory");
+  static_assert(G_QT == 4, "one operand per fragment of the slot");
+  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(slot[0]), "+v"(slot[1]), "+v"(slot[2]), "+v"(slot[3]) : "n"(N) : "memory");
 }
 
-// Epilogue of one wave's 128 x 64 block: two 32-wide q blocks.
-__device__ __forceinline__ void rotate_store(f32x16 (&acc)[4][G_QT], int lane, int pw, int qw, int P, int Q,
+// Epilogue of one wave's 128 x 64 block: four 16-wide q blocks.
+__device__ __forceinline__ void rotate_store(f32x4 (&acc)[G_PT][G_QT], int lane, int pw, int qw, int P, int Q,
                                              uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
                                              const uint16_t* __restrict__ sign_n) {
 #pragma unroll
   for (int j = 0; j < G_QT; ++j) {
-    f32x16 blk[4];
+    f32x4 blk[G_PT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) blk[i] = acc[i][j];
-    rotate_store_block(blk, lane, pw, qw + 32 * j, P, Q, y, ldy, n0, sign_n);
+    for (int i = 0; i < G_PT; ++i) blk[i] = acc[i][j];
+    rotate_store_block16(blk, lane, pw, qw + 16 * j, P, Q, y, ldy, n0, sign_n);
   }
 }
 
 // One accumulator tile in scratch: 512 threads x 128 floats, stored as 32
 // float4 columns of 512 (coalesced in both the writer and the fixup).
-__device__ __forceinline__ void store_partial(const f32x16 (&acc)[4][G_QT], f32x4* __restrict__ dst) {
+__device__ __forceinline__ void store_partial(const f32x4 (&acc)[G_PT][G_QT], f32x4* __restrict__ dst) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < G_PT; ++i)
 #pragma unroll
-    for (int j = 0; j < G_QT; ++j)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4 v = {acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
-        dst[((i * G_QT + j) * 4 + c) * G_THREADS + threadIdx.x] = v;
-      }
+    for (int j = 0; j < G_QT; ++j) dst[(i * G_QT + j) * G_THREADS + threadIdx.x] = acc[i][j];
 }
 
 // Slot of the partial of piece v for tail tile t: the (piece, tile) pairs in
@@ -202,30 +202,44 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wp = wave & 1, wq = wave >> 1;
-  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int lrow = lane & 15, lchunk = lane >> 4;
 
-  f32x16 acc[4][G_QT];
-  // A fragments of one k16 sub-step, two register sets; B fragments of the 4
-  // sub-steps of one k step: slot s is refilled with the next k step's
-  // sub-step s as soon as this k step's MFMAs of sub-step s are issued
-  f16x8 af[2][4], bq[4][G_QT];
-  auto read_frags = [&](int stage, int s, int buf) {
+  f32x4 acc[G_PT][G_QT];
+  // A fragments of one half-step (4 p tiles), two register sets; B fragments
+  // of the two k32 sub-steps of one k step: slot t is refilled with the next
+  // k step's sub-step t once this k step's last MFMAs reading it are issued
+  f16x8 af[2][4], bq[2][G_QT];
+  // A fragments of half-step h of stage `stage`: p tiles 4 (h % 2) .. + 3,
+  // k32 sub-step h / 2 (chunks 4 (h / 2) .. + 3, one per 16-lane group)
+  auto read_frags = [&](int stage, int h, int set) {
     const uint16_t* As = smem + stage * G_STAGE;
-    const int ch = 2 * s + lhalf;
+    const int ch = 4 * (h >> 1) + lchunk;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[buf][i] = *reinterpret_cast<const f16x8*>(&As[swz(128 * wp + 32 * i + lrow, ch)]);
+    for (int i = 0; i < 4; ++i)
+      af[set][i] = *reinterpret_cast<const f16x8*>(&As[swz(128 * wp + 16 * (4 * (h & 1) + i) + lrow, ch)]);
   };
-  auto mfmas = [&](int buf, int s) {
+  auto mfmas = [&](int set, int h) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < G_QT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[buf][i], bq[s][j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < G_QT; ++j) {
+        f32x4& d = acc[4 * (h & 1) + i][j];
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[set][i], bq[h >> 1][j], d, 0, 0, 0);
+      }
   };
-  // Pins the order inside one sub-step: the 4 A-fragment reads of the next
-  // sub-step and the 2 B-fragment loads of the next k step go out between
-  // the first MFMAs, so they land under the remaining ones.
+  // Pins the order inside one half-step: the 4 A-fragment reads of the next
+  // half-step go out between the first MFMAs, so they land under the rest.
   auto interleave = [&]() {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * G_QT - 4, 0);
+  };
+  // ... and with a slot refill in the half-step: its G_QT B loads go out
+  // between the next MFMAs.
+  auto interleave_loads = [&]() {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
@@ -236,42 +250,40 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8 - 4 - G_QT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * G_QT - 4 - G_QT, 0);
   };
 
   // acc = sum over k-steps [kb0, kb1) of one tile. Schedule per k step kb
-  // (stage buffer b = (kb - kb0) & 1):
-  //   sub-steps 0..2: read the next sub-step's A fragments, MFMAs, then load
-  //   B(kb + 1, s) into slot s;
-  //   sub-step 3: its A fragments are in registers; wait for this wave's A
-  //   loads of stage kb+1, barrier (every wave is done reading buffer b and
-  //   stage kb+1 has landed), issue the A loads of stage kb+2 into buffer b,
-  //   read sub-step 0 of stage kb+1, and only then run sub-step 3's MFMAs,
-  //   which cover the barrier and the fragment-read latency.
+  // (stage buffer b = (kb - kb0) & 1), half-steps h = 0..3:
+  //   h = 0: wait for slot 0; read h = 1's A fragments; MFMAs;
+  //   h = 1: read h = 2's A fragments; MFMAs; refill slot 0 (B(kb + 1, 0));
+  //   h = 2: wait for slot 1; read h = 3's A fragments; MFMAs;
+  //   h = 3: its A fragments are in registers; wait for this wave's A loads
+  //   of stage kb+1, barrier (every wave is done reading buffer b and stage
+  //   kb+1 has landed), issue the A loads of stage kb+2 into buffer b, read
+  //   h = 0 of stage kb+1, then run h = 3's MFMAs, which cover the barrier and
+  //   the fragment-read latency; refill slot 1 (B(kb + 1, 1)).
   // B loads past the range re-read the last k step (never used). Ends with a
   // barrier, so the stage buffers may be refilled at once.
   auto run_tile = [&](int p_base, int q_base, int kb0, int kb1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < G_PT; ++i)
 #pragma unroll
-      for (int j = 0; j < G_QT; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int j = 0; j < G_QT; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
     uint32_t offa[4];
     lane_offsets(K, p_base, P, 32 * wave, lane, offa);
-    // this wave's B blocks: q rows q_base + 64 wq + 32 j (clamped to the last
+    // this wave's B blocks: q rows q_base + 64 wq + 16 j (clamped to the last
     // block; rows past Q are never stored)
-    const int nqb = (Q + 31) / 32, ksub = K / 16;
+    const int nqb = (Q + 15) / 16, kt32 = K / 32;
     const uint16_t* bsrc[G_QT];
 #pragma unroll
     for (int j = 0; j < G_QT; ++j) {
-      const int qb = min((q_base + 32 * G_QT * wq + 32 * j) / 32, nqb - 1);
-      bsrc[j] = B + ((int64_t)qb * ksub * 64 + lane) * 8;
+      const int qb = min((q_base + 16 * G_QT * wq + 16 * j) / 16, nqb - 1);
+      bsrc[j] = B + ((int64_t)qb * kt32 * 64 + lane) * 8;
     }
-    auto load_b = [&](int kb, int sub) {
+    auto load_b = [&](int kb, int t) {
 #pragma unroll
-      for (int j = 0; j < G_QT; ++j)
-        bq[sub][j] = load_frag(bsrc[j] + (int64_t)(4 * kb + sub) * G_FRAG);
+      for (int j = 0; j < G_QT; ++j) bq[t][j] = load_frag(bsrc[j] + (int64_t)(2 * kb + t) * G_FRAG);
     };
     auto issue_loads = [&](int stage, int k0) { load_rows_lds(A, k0, offa, smem + stage * G_STAGE, 32 * wave); };
     const int nk = kb1 - kb0;
@@ -279,12 +291,11 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
     // Every k step issues the same loads in the same order, so the waits are
     // fixed counts: A loads of a stage past the range re-load the last k step
     // into a buffer no later k step reads. The prologue issues its loads in
-    // the steady state's order: B slots 0..2, A stage 1, B slot 3.
+    // the steady state's order: A stage 0, slot 0, A stage 1, slot 1.
     issue_loads(0, kb0 * G_BK);
-#pragma unroll
-    for (int sub = 0; sub < 3; ++sub) load_b(kb0, sub);
+    load_b(kb0, 0);
     issue_loads(1, (kb0 + min(1, nk - 1)) * G_BK);
-    load_b(kb0, 3);
+    load_b(kb0, 1);
     // stage 0 landed (the loads after it may not have)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitPrologue) : "memory");
     __syncthreads();
@@ -292,44 +303,36 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
     for (int kk = 0; kk < nk; ++kk) {
       const int b = kk & 1;
       const int kn = kb0 + min(kk + 1, nk - 1);  // the k step the B slots are refilled with
-      // Slot s of this k step has landed once kWaitSlot loads are
-      // outstanding (the later slots, the A loads of stage kk+1 and this k
-      // step's refills), for s = 0, 1, 2; the A loads themselves get the
-      // whole k step to land.
-      wait_slot<kWaitSlot>(bq[0]);
+      wait_slot<kWaitSlot0>(bq[0]);
       read_frags(b, 1, 1);
       mfmas(0, 0);
-      load_b(kn, 0);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
-      wait_slot<kWaitSlot>(bq[1]);
       read_frags(b, 2, 0);
       mfmas(1, 1);
-      load_b(kn, 1);
-      interleave();
+      load_b(kn, 0);
+      interleave_loads();
       __builtin_amdgcn_sched_barrier(0);
-      wait_slot<kWaitSlot>(bq[2]);
+      wait_slot<kWaitSlot1>(bq[1]);
       read_frags(b, 3, 1);
       mfmas(0, 2);
-      load_b(kn, 2);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
-      // only the refills just issued outstanding: slot 3 and this wave's A
-      // loads of stage kk+1 (issued before it) have landed
-      wait_slot<kWaitStage>(bq[3]);
+      // only slot 1's refill of the previous k step and slot 0's refill of
+      // this one may be outstanding: this wave's A loads of stage kk+1 (issued
+      // before them) have landed
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitStage) : "memory");
       __syncthreads();
       issue_loads(b, (kb0 + min(kk + 2, nk - 1)) * G_BK);
       if (kk + 1 < nk) read_frags(b ^ 1, 0, 0);
       mfmas(1, 3);
-      load_b(kn, 3);
+      load_b(kn, 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     // the last B loads (of the last k step again) must land before their
     // registers are reused: the compiler does not know they are in flight
     wait_slot<0>(bq[0]);
     wait_slot<0>(bq[1]);
-    wait_slot<0>(bq[2]);
-    wait_slot<0>(bq[3]);
   };
 
   if (MODE == 0) {
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
     const int tile = tile_base + t;
     const int p_base = (tile / tiles_q) * G_BP, q_base = (tile % tiles_q) * G_BQ;
     run_tile(p_base, q_base, 0, nk_all);
-    rotate_store(acc, lane, p_base + 128 * wp, q_base + 32 * G_QT * wq, P, Q, y, ldy, n0, sign_n);
+    rotate_store(acc, lane, p_base + 128 * wp, q_base + 16 * G_QT * wq, P, Q, y, ldy, n0, sign_n);
   } else {
     const int total = count * nk_all;
     const int pieces = (total + units - 1) / units;
@@ -357,9 +360,9 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
   }
 }
 
-// Sums the k-pieces of one 128 (p) x 32 (q) block of a tail tile in piece
+// Sums the k-pieces of one 128 (p) x 16 (q) block of a tail tile in piece
 // order and runs the rotation epilogue. One single-wave workgroup per (tail
-// tile, wave, 32-wide q block) spreads the partial reads over the CUs; the
+// tile, wave, 16-wide q block) spreads the partial reads over the CUs; the
 // loads of two pieces are in flight together.
 __global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict__ partial, int32_t units,
                                                         int32_t sdiv, int32_t grp, int32_t tile_base, int32_t P,
@@ -379,45 +382,29 @@ __global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict_
   const int nk = K / G_BK;
   const int w_lo = item * nk / units, w_hi = ((item + 1) * nk - 1) / units;
   auto piece = [&](int w) { return partial + (int64_t)partial_slot(w, item, sdiv) * (G_BP * G_BQ / 4) + tid; };
-  f32x16 a[4];
+  f32x4 a[G_PT];
   {
     const f32x4* src = piece(w_lo);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4 v = src[((i * G_QT + j) * 4 + c) * G_THREADS];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[i][4 * c + e] = v[e];
-      }
+    for (int i = 0; i < G_PT; ++i) a[i] = src[(i * G_QT + j) * G_THREADS];
   }
   for (int w = w_lo + 1; w <= w_hi; w += 2) {
     const f32x4* s0 = piece(w);
     const f32x4* s1 = piece(min(w + 1, w_hi));
-    f32x4 v0[16], v1[16];
+    f32x4 v0[G_PT], v1[G_PT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < G_PT; ++i) {
+      v0[i] = s0[(i * G_QT + j) * G_THREADS];
+      v1[i] = s1[(i * G_QT + j) * G_THREADS];
+    }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        v0[4 * i + c] = s0[((i * G_QT + j) * 4 + c) * G_THREADS];
-        v1[4 * i + c] = s1[((i * G_QT + j) * 4 + c) * G_THREADS];
-      }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[i][4 * c + e] += v0[4 * i + c][e];
+    for (int i = 0; i < G_PT; ++i) a[i] += v0[i];
     if (w + 1 <= w_hi) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a[i][4 * c + e] += v1[4 * i + c][e];
+      for (int i = 0; i < G_PT; ++i) a[i] += v1[i];
     }
   }
-  rotate_store_block(a, lane, p_base + 128 * wp, q_base + 32 * G_QT * wq + 32 * j, P, Q, y, ldy, n0, sign_n);
+  rotate_store_block16(a, lane, p_base + 128 * wp, q_base + 16 * G_QT * wq + 16 * j, P, Q, y, ldy, n0, sign_n);
 }
 
 // Round plan: `full` tiles (whole rounds of 256) run whole; the `rem` tiles

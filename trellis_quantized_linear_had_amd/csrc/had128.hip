@@ -42,16 +42,21 @@ __global__ __launch_bounds__(256) void had128_kernel(const uint16_t* in, uint16_
   if (blk_raw < nblocks) *reinterpret_cast<u32x4*>(out + blk * 128 + 8 * q) = o;
 }
 
-// The prefill GEMM's B operand: the same rotation of x (M x K), stored in
-// MFMA fragment order for Mpad = ceil(M / 32) * 32 rows, rows past M zero.
-// Block (qb, t) of 32 rows x 16 k is 1 KiB at halves (qb * K/16 + t) * 512;
-// lane l = row % 32 + 32 * ((k % 16) / 8) of it holds k .. k + 7 of its row.
-// One workgroup per (32-row block qb, 128-column block b): 16 lanes per row
-// rotate as in had128_kernel, each lane two rows 16 apart (both loads in
-// flight together), the results meet in LDS in fragment order, and each of
-// the 4 waves then stores two whole 1 KiB fragment blocks, one contiguous
-// store instruction each.
-template <bool PRE>
+// The MFMA GEMMs' input operand: the same rotation of x (M x K), stored in
+// fragment order for Mpad = ceil(M / 32) * 32 rows, rows past M zero, each
+// fragment 1 KiB (64 lanes x 16 bytes, lane l at 16 l):
+//   32-row order (the B operand of v_mfma_f32_32x32x16_f16, the dequant-GEMM):
+//     block (qb, t) of 32 rows x 16 k at halves (qb * K/16 + t) * 512; lane
+//     l = row % 32 + 32 * ((k % 16) / 8) holds k .. k + 7 of its row;
+//   16-row order (the B operand of v_mfma_f32_16x16x32_f16, the prefill GEMM):
+//     block (qb, t) of 16 rows x 32 k at halves (qb * K/32 + t) * 512; lane
+//     l = row % 16 + 16 * ((k % 32) / 8) holds k .. k + 7 of its row.
+// One workgroup per (32-row block, 128-column block): 16 lanes per row rotate
+// as in had128_kernel, each lane two rows 16 apart (both loads in flight
+// together), the results meet in LDS in fragment order, and each of the 4
+// waves then stores two whole 1 KiB fragment blocks, one contiguous store
+// instruction each.
+template <bool PRE, bool ROWS16>
 __global__ __launch_bounds__(256) void had128_frag_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
                                                           int32_t M, int32_t K, const uint16_t* __restrict__ sign_pre) {
   __shared__ u32x4 frag[8 * 64];
@@ -79,25 +84,33 @@ __global__ __launch_bounds__(256) void had128_frag_kernel(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * EXL3_INV_SQRT128, v[2 * j + 1] * EXL3_INV_SQRT128);
     if (32 * qb + r >= M) o = (u32x4){0u, 0u, 0u, 0u};
-    frag[(q >> 1) * 64 + r + 32 * (q & 1)] = o;  // block t = 8 b + q / 2, lane r + 32 (q & 1)
+    if (ROWS16)  // block (r / 16, q / 4) of this 32 x 128 piece, lane r % 16 + 16 (q % 4)
+      frag[((r >> 4) * 4 + (q >> 2)) * 64 + (r & 15) + 16 * (q & 3)] = o;
+    else  // block q / 2, lane r + 32 (q & 1)
+      frag[(q >> 1) * 64 + r + 32 * (q & 1)] = o;
   }
   __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = 2 * w + h;
-    *reinterpret_cast<u32x4*>(out + (((int64_t)qb * (K / 16) + 8 * b + t) * 64 + lane) * 8) = frag[t * 64 + lane];
+    const int64_t blk = ROWS16 ? (int64_t)(2 * qb + (t >> 2)) * (K / 32) + 4 * b + (t & 3)
+                               : (int64_t)qb * (K / 16) + 8 * b + t;
+    *reinterpret_cast<u32x4*>(out + (blk * 64 + lane) * 8) = frag[t * 64 + lane];
   }
 }
 
 hipError_t launch_had128_frag(const uint16_t* in, uint16_t* out, int64_t M, int32_t K, const uint16_t* sign_pre,
-                              hipStream_t stream) {
+                              bool rows16, hipStream_t stream) {
   const int64_t blocks = (M + 31) / 32 * (K / 128);
   if (blocks == 0) return hipSuccess;
+#define EXL3_FRAG_LAUNCH(pre, r16) \
+  had128_frag_kernel<pre, r16><<<(unsigned)blocks, 256, 0, stream>>>(in, out, (int32_t)M, K, sign_pre)
   if (sign_pre)
-    had128_frag_kernel<true><<<(unsigned)blocks, 256, 0, stream>>>(in, out, (int32_t)M, K, sign_pre);
+    rows16 ? EXL3_FRAG_LAUNCH(true, true) : EXL3_FRAG_LAUNCH(true, false);
   else
-    had128_frag_kernel<false><<<(unsigned)blocks, 256, 0, stream>>>(in, out, (int32_t)M, K, sign_pre);
+    rows16 ? EXL3_FRAG_LAUNCH(false, true) : EXL3_FRAG_LAUNCH(false, false);
+#undef EXL3_FRAG_LAUNCH
   return hipGetLastError();
 }
 
