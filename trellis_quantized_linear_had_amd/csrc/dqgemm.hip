@@ -6,7 +6,7 @@
 //
 // Transposed product, as in the prefill GEMM: D[p][q] = sum_k W[k][p] Xr[q][k]
 // with v_mfma_f32_32x32x16_f16, A = 32 columns p x 16 k of W decoded in
-// registers, B = 32 rows q x 16 k of Xr in the MFMA fragment order the
+// registers, B = 32 rows q x 16 k of Xr in the 32-row fragment order the
 // rotation pass writes (1 KiB per fragment, one contiguous load).
 //
 // The cost is one random 16-bit codebook read from LDS per decoded weight,
