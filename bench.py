@@ -560,9 +560,9 @@ def sweep(bits: int = 4) -> str:
         return one
 
     names = {_measure.VARIANT_FUSED: "decode-GEMM", _measure.VARIANT_RECON_GEMM: "reconstruct+GEMM",
-             _measure.VARIANT_DEQUANT_GEMM: "dequant-GEMM"}
+             _measure.VARIANT_DEQUANT_GEMM: "dequant-GEMM", _measure.VARIANT_DEQUANT_GEMM8: "dequant-GEMM, 8 waves"}
     variants = [_measure.VARIANT_FUSED, _measure.VARIANT_RECON_GEMM] + (
-        [_measure.VARIANT_DEQUANT_GEMM] if bits == 4 else [])
+        [_measure.VARIANT_DEQUANT_GEMM, _measure.VARIANT_DEQUANT_GEMM8] if bits == 4 else [])
     out = ["| geometry | bits | M | " + " | ".join("%s µs" % names[v] for v in variants) +
            " | default dispatch µs | fastest | default TFLOP/s |",
            "|---|---|---|" + "---|" * len(variants) + "---|---|---|"]
@@ -721,11 +721,12 @@ def ceilings(log=None) -> dict:
 
 
 def dq_sweep() -> str:
-    """exl3_linear's three kernel sequences forced at the same shapes: the
-    fused decode-GEMM, reconstruct + GEMM, and the dequant-in-GEMM, over M
-    on both MLP geometries (6 rotating 4-bit weight sets, 267 MB of codes);
-    whole calls back to back between one event pair, and the dequant-GEMM
-    kernel alone (event pairs around its launch)."""
+    """exl3_linear's kernel sequences forced at the same shapes: the fused
+    decode-GEMM, reconstruct + GEMM, and both dequant-in-GEMM kernels (four
+    waves of 1..8 row fragments, eight waves of 256-row passes), over M on
+    both MLP geometries (6 rotating 4-bit weight sets, 267 MB of codes);
+    whole calls back to back between one event pair, and each dequant-GEMM
+    kernel alone (event pairs around its launches)."""
     import torch
 
     import trellis_quantized_linear_had_amd as X
@@ -735,30 +736,36 @@ def dq_sweep() -> str:
     sh = torch.cuda.current_stream().cuda_stream
     cb = W.codebook()
     out = ["| geometry | M | fused µs | reconstruct+GEMM µs | dequant-GEMM µs | same, whole units µs | its kernels µs | "
-           "call TFLOP/s | kernels GB/s of codes |", "|---|---|---|---|---|---|---|---|---|"]
+           "8-wave dequant-GEMM µs | its kernels µs | best dequant call TFLOP/s | best kernels GB/s of codes |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
     kt = _measure.KernelTimer(pairs=512, per_call=4)
     for g, (k, n) in enumerate(((5120, 17408), (17408, 5120))):
         layers = [X.Layer.from_numpy(W.layer(W.SEED_PREFILL, k, n, 2 * s), cb) for s in range(6)]
-        for M in (16, 32, 64, 128, 256, 512, 1024, 2048):
+        for M in (16, 32, 64, 128, 192, 256, 384, 512, 1024, 2048):
             x = _lib.to_device_u16(W.activations(W.SEED_PREFILL, M, k, g))
             y = torch.empty((M, n), dtype=torch.int16, device=dev)
-            scr = torch.empty(max(_measure.linear_scratch_bytes(k, n, M, v) for v in (1, 2, 3, 4)), dtype=torch.uint8,
-                              device=dev)
+            scr = torch.empty(max(_measure.linear_scratch_bytes(k, n, M, v) for v in (1, 2, 3, 4, 5)),
+                              dtype=torch.uint8, device=dev)
             def forced(var):
                 return lambda i: kt.linear_variant(layers[i % 6], x, M, y, scr, sh, var)
             vs = [v for v in (_measure.VARIANT_FUSED, _measure.VARIANT_RECON_GEMM, _measure.VARIANT_DEQUANT_GEMM,
-                              _measure.VARIANT_DEQUANT_WHOLE) if not (v == _measure.VARIANT_FUSED and M > 256)]
+                              _measure.VARIANT_DEQUANT_WHOLE, _measure.VARIANT_DEQUANT_GEMM8)
+                  if not (v == _measure.VARIANT_FUSED and M > 256)]
             row = interleaved_us({v: forced(v) for v in vs}, 12 if M <= 256 else 6)
             row.setdefault(_measure.VARIANT_FUSED, None)
-            for i in range(6):
-                kt.linear(layers[i % 6], x, M, y, scr, 128, sh, _measure.DECODE, _measure.VARIANT_DEQUANT_GEMM)
-            ms, cnt = kt.read(_measure.DECODE)
-            kus = ms / cnt * 1e3
-            out.append("| K%dxN%d | %d | %s | %.1f | %.1f | %.1f | %.1f | %.0f | %.0f |" % (
+            kus = {}
+            for v in (_measure.VARIANT_DEQUANT_GEMM, _measure.VARIANT_DEQUANT_GEMM8):
+                for i in range(6):
+                    kt.linear(layers[i % 6], x, M, y, scr, 128, sh, _measure.DECODE, v)
+                ms, cnt = kt.read(_measure.DECODE)
+                kus[v] = ms / cnt * 1e3
+            best = min((_measure.VARIANT_DEQUANT_GEMM, _measure.VARIANT_DEQUANT_GEMM8), key=lambda v: row[v])
+            out.append("| K%dxN%d | %d | %s | %.1f | %.1f | %.1f | %.1f | %.1f | %.1f | %.0f | %.0f |" % (
                 k, n, M, "—" if row[_measure.VARIANT_FUSED] is None else "%.1f" % row[_measure.VARIANT_FUSED],
                 row[_measure.VARIANT_RECON_GEMM], row[_measure.VARIANT_DEQUANT_GEMM],
-                row[_measure.VARIANT_DEQUANT_WHOLE], kus, 2 * M * k * n / row[_measure.VARIANT_DEQUANT_GEMM] / 1e6,
-                k * n / 2 / kus / 1e3))
+                row[_measure.VARIANT_DEQUANT_WHOLE], kus[_measure.VARIANT_DEQUANT_GEMM],
+                row[_measure.VARIANT_DEQUANT_GEMM8], kus[_measure.VARIANT_DEQUANT_GEMM8],
+                2 * M * k * n / row[best] / 1e6, k * n / 2 / kus[best] / 1e3))
             print("[bench] dq-sweep K%d N%d M=%d done" % (k, n, M), file=sys.stderr, flush=True)
             del x, y, scr
         del layers

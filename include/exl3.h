@@ -127,10 +127,13 @@ typedef struct exl3_layer {
  *   - dequant-GEMM (4 bits: 48 rows and up on the fused side, up to 1024 rows
  *     on the prefill side) [P316 follow-up item 4: dequantisation fused into
  *     the GEMM]: input rotation into scratch, then an MFMA GEMM that decodes
- *     each trellis tile into its operand registers once per pass of up to
- *     256 rows and applies scales, output rotation and sign_n in its
- *     epilogue; a K-split remainder of the work leaves fp32 partials that a
- *     fixup kernel sums in a fixed order before the same epilogue.
+ *     each trellis tile into its operand registers once per pass of rows --
+ *     below 192 rows a four-wave kernel with passes of 32 to 256 rows, from
+ *     192 rows an eight-wave kernel with 256-row passes whose rows of the
+ *     rotated input are staged in LDS -- and applies scales, output rotation
+ *     and sign_n in its epilogue; a K-split remainder of the work leaves fp32
+ *     partials that a fixup kernel sums in a fixed order before the same
+ *     epilogue.
  * All three give y within the fp16 rounding of the same sums, not
  * bit-identical to each other. M = 0 is a no-op returning EXL3_OK.
  * Limits (EXL3_ESHAPE otherwise): K, N positive multiples of 128, K < 65536,

@@ -69,16 +69,17 @@ def require_gpu():
 
 
 # exl3_linear's kernel sequences: the decode-GEMM ("fused"), reconstruct +
-# GEMM ("recon") and the dequant-GEMM ("dq", 4 bits only). At 4 bits the
-# dispatch takes the dequant-GEMM from 48 rows on the fused side and up to
-# 1024 rows on the prefill side.
-DQ_FUSED_MIN_ROWS, DQ_PREFILL_MAX_ROWS = 48, 1024
+# GEMM ("recon") and the dequant-GEMMs ("dq", four waves, and "dq8", eight
+# waves; 4 bits only). At 4 bits the dispatch takes a dequant-GEMM from 48
+# rows on the fused side and up to 1024 rows on the prefill side: the
+# eight-wave one from 192 rows on.
+DQ_FUSED_MIN_ROWS, DQ_PREFILL_MAX_ROWS, DQ8_MIN_ROWS = 48, 1024, 192
 
 
 def route(bits: int, M: int, pm: int) -> str:
     prefill = pm > 0 and M >= pm
     if bits == 4 and (M <= DQ_PREFILL_MAX_ROWS if prefill else M >= DQ_FUSED_MIN_ROWS):
-        return "dq"
+        return "dq8" if M >= DQ8_MIN_ROWS else "dq"
     return "recon" if prefill else "fused"
 
 
@@ -91,7 +92,8 @@ def linear_forced(lay, x, route_name: str, out=None, scratch=None, sync: bool = 
     from trellis_quantized_linear_had_amd import _lib, _measure
 
     variant = {"fused": _measure.VARIANT_FUSED, "recon": _measure.VARIANT_RECON_GEMM,
-               "dq": _measure.VARIANT_DEQUANT_GEMM, "dq_whole": _measure.VARIANT_DEQUANT_WHOLE}[route_name]
+               "dq": _measure.VARIANT_DEQUANT_GEMM, "dq_whole": _measure.VARIANT_DEQUANT_WHOLE,
+               "dq8": _measure.VARIANT_DEQUANT_GEMM8, "dq8_whole": _measure.VARIANT_DEQUANT8_WHOLE}[route_name]
     xd = x if isinstance(x, torch.Tensor) else _lib.to_device_u16(x)
     M = xd.shape[0]
     if out is None:

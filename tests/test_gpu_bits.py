@@ -88,7 +88,7 @@ def test_linear_both_paths(T, X, cb, bits, M):
     x = WL.activations(34, M, K)
     ref = O.exl3_linear(x, L, cb)
     lay = X.Layer.from_numpy(L, cb)
-    for r in ("fused", "recon") + (("dq",) if bits == 4 else ()):
+    for r in ("fused", "recon") + (("dq", "dq8") if bits == 4 else ()):
         H.assert_rows_close(H.linear_forced(lay, x, r), ref, what=r)
     for pm in (0, 1):  # the dispatch at this width
         want = H.linear_forced(lay, x, H.route(bits, M, pm))

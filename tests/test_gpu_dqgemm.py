@@ -2,7 +2,9 @@
 loop, exl3_linear's kernel sequence forced through the measurement library)
 against the oracle: within the per-row tolerance over row counts that take
 one to eight row fragments per pass and several passes, with split-K, and
-bit for bit on the decoded states (the inputs of tests/exact_decode.py)."""
+bit for bit on the decoded states (the inputs of tests/exact_decode.py).
+Both kernels: the four-wave one (1 to 8 row fragments of 32 per pass) and
+the eight-wave one (256-row passes, Xr staged in LDS)."""
 import numpy as np
 import pytest
 
@@ -43,28 +45,34 @@ def run_dq(T, X, lay, x, M, variant=None):
     return _lib.to_host_u16(y)
 
 
+def variant_of(eight, whole):
+    from trellis_quantized_linear_had_amd import _measure
+
+    return {(False, False): _measure.VARIANT_DEQUANT_GEMM, (False, True): _measure.VARIANT_DEQUANT_WHOLE,
+            (True, False): _measure.VARIANT_DEQUANT_GEMM8, (True, True): _measure.VARIANT_DEQUANT8_WHOLE}[eight, whole]
+
+
+@pytest.mark.parametrize("eight", [False, True])
 @pytest.mark.parametrize("whole", [False, True])
 @pytest.mark.parametrize("K,N", [(256, 256), (1024, 384), (512, 1152)])
 @pytest.mark.parametrize("M", [1, 17, 40, 100, 128, 200, 256, 300, 513])
-def test_dqgemm_matches_oracle(T, X, K, N, M, whole):
+def test_dqgemm_matches_oracle(T, X, K, N, M, whole, eight):
     """Both output stages: whole units (scales, rotation and signs in the
     kernel) and K-split tail pieces summed by the fixup."""
-    from trellis_quantized_linear_had_amd import _measure
-
-    H.announce("dqgemm K%d N%d M=%d whole=%d" % (K, N, M, whole))
+    H.announce("dqgemm K%d N%d M=%d whole=%d eight=%d" % (K, N, M, whole, eight))
     L = WL.layer(90, K, N)
     cb = WL.codebook()
     x = WL.activations(90, M, K)
-    var = _measure.VARIANT_DEQUANT_WHOLE if whole else _measure.VARIANT_DEQUANT_GEMM
-    y = run_dq(T, X, X.Layer.from_numpy(L, cb), x, M, var)
+    y = run_dq(T, X, X.Layer.from_numpy(L, cb), x, M, variant_of(eight, whole))
     H.assert_rows_close(y, O.exl3_linear(x, L, cb), what="dqgemm M=%d" % M)
 
 
+@pytest.mark.parametrize("eight", [False, True])
 @pytest.mark.parametrize("whole", [False, True])
 @pytest.mark.parametrize("M", [40, 256, 300])
-def test_dqgemm_states_bit_exact(T, X, M, whole):
+def test_dqgemm_states_bit_exact(T, X, M, whole, eight):
     K, N = 512, 768
-    H.announce("dqgemm exact decode K%d N%d M=%d" % (K, N, M))
+    H.announce("dqgemm exact decode K%d N%d M=%d whole=%d eight=%d" % (K, N, M, whole, eight))
     L = E.unit_layer(91, K, N, 4)
     st = O.trellis_states(L["codes"], K, N, 4)
     order = np.random.default_rng(M).permutation(K)
@@ -74,20 +82,21 @@ def test_dqgemm_states_bit_exact(T, X, M, whole):
             ks = order[c0:c0 + M]
             if len(ks) < M:
                 ks = np.concatenate([ks, order[:M - len(ks)]])
-            got = run_dq(T, X, lay, E.unit_rows(ks, K, L["sign_k"]), M, 4 if whole else 3)
+            got = run_dq(T, X, lay, E.unit_rows(ks, K, L["sign_k"]), M, variant_of(eight, whole))
             want = E.expected_y(st, ks, kind, L["sign_n"])
             assert np.array_equal(got, want), (kind, c0, int(np.count_nonzero(got != want)))
 
 
+@pytest.mark.parametrize("eight", [False, True])
 @pytest.mark.parametrize("M", [64, 256, 1024, 2048])
-def test_dqgemm_full_geometry_sampled(T, X, M):
+def test_dqgemm_full_geometry_sampled(T, X, M, eight):
     from tests.test_gpu_configs import sample_rows
 
     K, N = 5120, 17408
-    H.announce("dqgemm K%d N%d M=%d" % (K, N, M))
+    H.announce("dqgemm K%d N%d M=%d eight=%d" % (K, N, M, eight))
     L = WL.layer(WL.SEED_PREFILL, K, N, 0)
     cb = WL.codebook()
     x = WL.activations(WL.SEED_PREFILL, M, K, 0)
     rows = sample_rows(M)
-    y = run_dq(T, X, X.Layer.from_numpy(L, cb), x, M)
+    y = run_dq(T, X, X.Layer.from_numpy(L, cb), x, M, variant_of(eight, False))
     H.assert_rows_close(y[rows], O.exl3_linear(x, L, cb, rows), what="dqgemm full M=%d" % M)

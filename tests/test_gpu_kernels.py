@@ -136,7 +136,7 @@ def run_linear(X, L, cb, x, pm):
     return host16(X.linear(dev16(x), lay, prefill_min_m=pm))
 
 
-@pytest.mark.parametrize("M", [1, 5, 16, 17, 47, 48, 64, 127, 128, 130, 300, 1024, 1025])
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 47, 48, 64, 127, 128, 130, 191, 192, 300, 1024, 1025])
 def test_linear_tiny_every_route(T, X, cb, M):
     """Each kernel sequence (forced) against the oracle, and the dispatch:
     the default threshold, 0 (fused side only) and 1 (prefill side only)
@@ -147,7 +147,7 @@ def test_linear_tiny_every_route(T, X, cb, M):
     lay = X.Layer.from_numpy(L, cb)
     x = WL.activations(WL.SEED_TINY, M, K)
     ref = O.exl3_linear(x, L, cb)
-    out = {r: H.linear_forced(lay, x, r) for r in ("fused", "recon", "dq")}
+    out = {r: H.linear_forced(lay, x, r) for r in ("fused", "recon", "dq", "dq8")}
     for r, y in out.items():
         H.assert_rows_close(y, ref, what=r)
     H.assert_rows_close(out["fused"], out["recon"], what="fused vs recon")
@@ -256,7 +256,7 @@ def test_linear_zero_codes_rank_one(T, X, cb):
     for M in (3, 130):
         x = WL.activations(33, M, K)
         ref = O.exl3_linear(x, L, cb)
-        for r in ("fused", "recon", "dq"):
+        for r in ("fused", "recon", "dq", "dq8"):
             H.assert_rows_close(H.linear_forced(lay, x, r), ref, what="%s M=%d" % (r, M))
 
 

@@ -11,6 +11,7 @@ from . import _lib
 MEASURE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libexl3_measure.so")
 DECODE, GEMM, LOGITS, RECONSTRUCT = 0, 1, 2, 3
 VARIANT_AUTO, VARIANT_FUSED, VARIANT_RECON_GEMM, VARIANT_DEQUANT_GEMM, VARIANT_DEQUANT_WHOLE = 0, 1, 2, 3, 4
+VARIANT_DEQUANT_GEMM8, VARIANT_DEQUANT8_WHOLE = 5, 6  # the eight-wave dequant-GEMM (split tail, whole units)
 PROBE_WORKGROUPS = 256
 PROBE_SINK_BYTES = 256 * 32 * 256 * 4
 EXPORTS = (

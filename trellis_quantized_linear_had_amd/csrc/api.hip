@@ -46,6 +46,9 @@ hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, in
                            int64_t ldy, int32_t n0, const uint16_t* sign_n, float* partial, hipStream_t stream,
                            Marks* marks);
 size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K);
+hipError_t launch_dqgemm2(const uint16_t* xf16, const uint32_t* codes, const uint16_t* cb, const uint16_t* scale,
+                          const uint16_t* sign_n, uint16_t* y, int64_t ldy, float* partials, int32_t K, int32_t N,
+                          int32_t ldt, int32_t M, const DqPlan& plan, hipStream_t stream);
 hipError_t launch_dqgemm(const uint16_t* xf, const uint32_t* codes, const uint16_t* cb, const uint16_t* scale,
                          const uint16_t* sign_n, uint16_t* y, int64_t ldy, float* partials, int32_t K, int32_t N,
                          int32_t ldt, int32_t M, const DqPlan& plan, hipStream_t stream);
@@ -331,8 +334,12 @@ DqPlan plan_dq_rows(int32_t K, int32_t N, int64_t M, int nqb, bool whole, double
 
 // The least modelled time over the row-fragment counts that leave no whole
 // fragment of a pass empty (a pass of R rows serves M in ceil(M / R) passes).
-DqPlan plan_dq(int32_t K, int32_t N, int64_t M, bool whole = false) {
+DqPlan plan_dq(int32_t K, int32_t N, int64_t M, bool whole = false, bool eight_waves = false) {
   DqPlan best_plan{};
+  if (eight_waves) {
+    double t;
+    return plan_dq_rows(K, N, M, 8, whole, t);
+  }
   double best = 1e300;
   for (int nqb : {1, 2, 4, 8}) {
     if (nqb > 1 && 32 * (nqb / 2) >= M) break;
@@ -351,9 +358,9 @@ struct DqLayout {
   DqPlan plan;
 };
 
-DqLayout dq_layout(int32_t K, int32_t N, int64_t M, bool whole = false) {
+DqLayout dq_layout(int32_t K, int32_t N, int64_t M, bool whole = false, bool eight_waves = false) {
   DqLayout l;
-  l.plan = plan_dq(K, N, M, whole);
+  l.plan = plan_dq(K, N, M, whole, eight_waves);
   l.xf_off = 0;
   l.part_off = align256((size_t)((M + 31) / 32 * 32) * K * 2);
   l.total = l.part_off + align256(dq_partial_bytes(l.plan));
@@ -384,12 +391,21 @@ const char* exl3_strerror(int status) {
 
 namespace {
 
-// The kernel sequence of one call. At 4 bits the dequant-GEMM takes the row
-// counts where it measured fastest on both MLP geometries: from 48 rows on
+// The kernel sequence of one call. At 4 bits the dequant-GEMMs take the row
+// counts where they measured fastest on both MLP geometries: from 48 rows on
 // the fused side (the decode-GEMM below) and up to 1024 rows on the prefill
-// side (reconstruct + GEMM above). A forced variant overrides the choice.
-enum Route { kRouteDecode, kRouteReconstructGemm, kRouteDequantGemm, kRouteDequantGemmWhole };
-constexpr int64_t kDqFusedMinRows = 48, kDqPrefillMaxRows = 1024;
+// side (reconstruct + GEMM above); the four-wave kernel (passes of 32 to 256
+// rows) below 192 rows, the eight-wave one (256-row passes) from 192 rows on.
+// A forced variant overrides the choice.
+enum Route {
+  kRouteDecode,
+  kRouteReconstructGemm,
+  kRouteDequantGemm,
+  kRouteDequantGemmWhole,
+  kRouteDequantGemm8,
+  kRouteDequantGemm8Whole
+};
+constexpr int64_t kDqFusedMinRows = 48, kDqPrefillMaxRows = 1024, kDq8MinRows = 192;
 
 Route route_of(int32_t bits, int64_t M, int32_t prefill_min_m, int variant) {
   switch (variant) {
@@ -401,12 +417,17 @@ Route route_of(int32_t bits, int64_t M, int32_t prefill_min_m, int variant) {
       return kRouteDequantGemm;
     case kVariantDequantGemmWhole:
       return kRouteDequantGemmWhole;
+    case kVariantDequantGemm8:
+      return kRouteDequantGemm8;
+    case kVariantDequantGemm8Whole:
+      return kRouteDequantGemm8Whole;
     default:
       break;
   }
   const bool dq_ok = bits == 4;
-  if (use_prefill(M, prefill_min_m)) return dq_ok && M <= kDqPrefillMaxRows ? kRouteDequantGemm : kRouteReconstructGemm;
-  return dq_ok && M >= kDqFusedMinRows ? kRouteDequantGemm : kRouteDecode;
+  const Route dq = M >= kDq8MinRows ? kRouteDequantGemm8 : kRouteDequantGemm;
+  if (use_prefill(M, prefill_min_m)) return dq_ok && M <= kDqPrefillMaxRows ? dq : kRouteReconstructGemm;
+  return dq_ok && M >= kDqFusedMinRows ? dq : kRouteDecode;
 }
 
 size_t route_scratch_bytes(Route r, int32_t K, int32_t ncols, int64_t M, int32_t bits) {
@@ -415,7 +436,11 @@ size_t route_scratch_bytes(Route r, int32_t K, int32_t ncols, int64_t M, int32_t
       return prefill_layout(K, ncols, M).total;
     case kRouteDequantGemm:
     case kRouteDequantGemmWhole:
-      return dq_layout(K, ncols, M, r == kRouteDequantGemmWhole).total;
+    case kRouteDequantGemm8:
+    case kRouteDequantGemm8Whole:
+      return dq_layout(K, ncols, M, r == kRouteDequantGemmWhole || r == kRouteDequantGemm8Whole,
+                       r == kRouteDequantGemm8 || r == kRouteDequantGemm8Whole)
+          .total;
     default:
       return decode_layout(K, ncols, M, bits).total;
   }
@@ -436,16 +461,24 @@ int linear_cols(const exl3_layer* L, const uint16_t* x, int64_t M, uint16_t* y, 
                 char* sb, int32_t prefill_min_m, hipStream_t stream, Marks* marks) {
   const int32_t K = L->K, N = L->N;
   const Route route = route_of(L->bits, M, prefill_min_m, marks ? marks->variant : kVariantAuto);
-  if (route == kRouteDequantGemm || route == kRouteDequantGemmWhole) {
+  if (route == kRouteDequantGemm || route == kRouteDequantGemmWhole || route == kRouteDequantGemm8 ||
+      route == kRouteDequantGemm8Whole) {
     if (L->bits != 4) return fail(EXL3_ESHAPE, "the dequant-GEMM takes 4-bit codes only");
-    const DqLayout l = dq_layout(K, ncols, M, route == kRouteDequantGemmWhole);
+    const bool eight = route == kRouteDequantGemm8 || route == kRouteDequantGemm8Whole;
+    const DqLayout l =
+        dq_layout(K, ncols, M, route == kRouteDequantGemmWhole || route == kRouteDequantGemm8Whole, eight);
     uint16_t* xf = (uint16_t*)(sb + l.xf_off);
     float* part = (float*)(sb + l.part_off);
-    EXL3_TRY(launch_had128_frag(x, xf, M, K, L->sign_k, false, stream), "input rotation");
+    EXL3_TRY(launch_had128_frag(x, xf, M, K, L->sign_k, eight, stream), "input rotation");
     EXL3_TRY(mark_begin(marks, kMarkDecode, stream), "event record");
-    EXL3_TRY(launch_dqgemm(xf, L->codes, L->codebook, L->scale, L->sign_n, y, ldy, part, K, ncols, N / 16,
-                           (int32_t)M, l.plan, stream),
-             "dequant gemm");
+    if (eight)
+      EXL3_TRY(launch_dqgemm2(xf, L->codes, L->codebook, L->scale, L->sign_n, y, ldy, part, K, ncols, N / 16,
+                              (int32_t)M, l.plan, stream),
+               "dequant gemm");
+    else
+      EXL3_TRY(launch_dqgemm(xf, L->codes, L->codebook, L->scale, L->sign_n, y, ldy, part, K, ncols, N / 16,
+                             (int32_t)M, l.plan, stream),
+               "dequant gemm");
     EXL3_TRY(mark_end(marks, kMarkDecode, stream), "event record");
   } else if (route == kRouteReconstructGemm) {
     const PrefillLayout l = prefill_layout(K, ncols, M);

@@ -302,6 +302,246 @@ __global__ __launch_bounds__(DQ_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
   }
 }
 
+// ---- Eight-wave form: 32 columns per wave (two 16-column A fragments of
+// v_mfma_f32_16x16x32_f16), one pass of 256 rows, the pass's rows of Xr
+// staged once per workgroup in the LDS beside the codebook (16-row fragment
+// order, 16 KiB per 32-k step, two stages), so each wave reads them from LDS
+// instead of loading them itself, and two waves per SIMD hide each other's
+// waits. A lane of A fragment f holds 8 consecutive k of column p: k-tile
+// (lane >> 5) of the step, half (lane >> 4) & 1 of that tile's 16 steps.
+#define DQ2_THREADS 512
+#define DQ2_R 256
+#define DQ2_XSTAGE (16 * 512)  // halves per x stage: 16 fragments of 16 rows x 32 k
+
+template <bool TAIL>
+__global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void dqgemm2_kernel(
+    const uint16_t* __restrict__ xf, const uint32_t* __restrict__ codes, const uint16_t* __restrict__ cb,
+    const uint16_t* __restrict__ scale, const uint16_t* __restrict__ sign_n, uint16_t* __restrict__ y, int64_t ldy,
+    float* __restrict__ partials, int32_t K, int32_t N, int32_t ldt, int32_t M, DqPlan plan) {
+  // the codebook, then two x stages; after the last codebook read, the output stage's transpose buffer
+  __shared__ __align__(16) uint16_t lds[65536 + 2 * DQ2_XSTAGE];
+  uint16_t* cb_lds = lds;
+  uint16_t* xs = lds + 65536;
+
+  const int ks32 = K / 32;
+  int unit, s_begin, s_end;
+  if (!TAIL) {
+    unit = blockIdx.x;
+    s_begin = 0;
+    s_end = ks32;
+  } else {
+    const int t = blockIdx.x / plan.tail_ks, piece = blockIdx.x % plan.tail_ks;
+    unit = plan.full + t;
+    s_begin = piece * (plan.ksub_per_piece / 2);  // ksub_per_piece: 16-k steps, a multiple of 4
+    s_end = min(s_begin + plan.ksub_per_piece / 2, ks32);
+  }
+  const int pass = unit / plan.pblocks, pb = unit % plan.pblocks;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p0_raw = pb * DQ_COLS_WG + wave * 32;
+  const bool pvalid = p0_raw < N;          // N is a multiple of 128: valid waves come in groups of four
+  const int p0 = pvalid ? p0_raw : N - 32;  // idle waves re-read the last group, never store
+
+  // Codebook into LDS straight from global memory (1 KiB per wave instruction).
+  {
+    const char* src = reinterpret_cast<const char*>(cb) + threadIdx.x * 16;
+#pragma unroll 4
+    for (int i = 0; i < 65536 * 2 / (DQ2_THREADS * 16); ++i)
+      __builtin_amdgcn_global_load_lds(
+          src + i * DQ2_THREADS * 16,
+          (dq_lds_void*)(reinterpret_cast<char*>(cb_lds) + i * DQ2_THREADS * 16 + wave * 1024), 16, 0, 0);
+  }
+
+  // Code words: lane (column c, k-tile kt, half h) reads words 2c + h and
+  // 2c + h + 1 (mod 32) of tile (2 s + kt, (p0 + 16 f) / 16).
+  const int c = lane & 15, kt = lane >> 5, h = (lane >> 4) & 1;
+  const int d = 2 * c + h;
+  const uint32_t row_bytes = (uint32_t)ldt * 128;  // one k-tile row of codes
+  uint32_t voff[2][2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int nt = (p0 + 16 * f) / 16;
+    voff[f][0] = (uint32_t)(kt * row_bytes + nt * 128 + 4 * d);
+    voff[f][1] = (uint32_t)(kt * row_bytes + nt * 128 + 4 * ((d + 1) & 31));
+  }
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((int64_t)K * ldt * 8));
+  constexpr int kCodeLoads = 4;  // VMEM loads per call of load_codes
+  auto load_codes = [&](int s, uint32_t (&w)[2][2]) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) w[f][j] = buffer_load_u32(crs, voff[f][j], (uint32_t)(2 * s) * row_bytes);
+  };
+
+  // x stage of step s: the pass's 16 row fragments (16 rows x 32 k each),
+  // clamped to the last fragment of the padded rows (rows past M are zero
+  // or repeats and are never stored); wave w loads fragments 2 w and 2 w + 1.
+  // Buffer loads (a fixed lane offset, the step in the scalar offset): no
+  // 64-bit address registers to rebuild while code-word loads are in flight.
+  const int nq16 = (M + 31) / 32 * 2, q16_0 = pass * 16;
+  const __amdgpu_buffer_rsrc_t xrs =
+      make_rsrc(xf + (int64_t)q16_0 * ks32 * 512, (uint32_t)(min(16, nq16 - q16_0) * ks32 * 1024));
+  uint32_t xoff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) xoff[j] = (uint32_t)((min(q16_0 + 2 * wave + j, nq16 - 1) - q16_0) * ks32 * 1024 + 16 * lane);
+  auto load_x = [&](int s, int buf) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (dq_lds_void*)(xs + buf * DQ2_XSTAGE + (2 * wave + j) * 512), 16,
+                                               xoff[j], (uint32_t)s * 1024, 0, 0);
+  };
+  auto xfrag = [&](int buf, int qt) {
+    return *reinterpret_cast<const f16x8*>(xs + buf * DQ2_XSTAGE + qt * 512 + 8 * lane);
+  };
+
+  f32x4 acc[2][16];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int qt = 0; qt < 16; ++qt) acc[f][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  // Rings: code words of steps s .. s + 3; the codebook reads of step s + 1
+  // are issued during step s.
+  uint32_t wr[4][2][2];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) load_codes(min(s_begin + u, s_end - 1), wr[u]);
+  load_x(s_begin, 0);
+  load_x(min(s_begin + 1, s_end - 1), 1);
+  __builtin_amdgcn_s_waitcnt(0);  // the codebook, the first code words and both x stages have landed
+  __syncthreads();
+  uint32_t g[2][8];
+  dq_gather(cb_lds, wr[0][0], g[0]);
+  dq_gather(cb_lds, wr[0][1], g[1]);
+
+  // Step s (ring phase u = (s - s_begin) % 4, x buffer b = (s - s_begin) % 2):
+  // 16 slots, each the 2 MFMAs of one row fragment plus one piece of the next
+  // step's work in source order fenced by scheduling barriers: the x
+  // fragment kXAhead slots ahead, (slot 4) the code words of s + 4, and
+  // (slots 8..15) the codebook reads of s + 1. Measured at M = 256..2048 on
+  // both MLP geometries: fragments 6 ahead and the reads in the second half
+  // beat 2 ahead and the first half by 2-4 %; staggering the halves between
+  // the two waves of a SIMD, or one read pair per slot, did not help.
+  constexpr int kXAhead = 6, kCodeSlot = 4, kGatherSlot = 8;
+  static_assert(kGatherSlot + 8 <= 16, "all 8 codebook read pairs of the next step are issued inside the step");
+  static_assert(kCodeSlot < 16 && kXAhead < 16, "slot numbers");
+  auto step = [&](auto U, int s) {
+    constexpr int u = decltype(U)::value, b = u & 1;
+    const int s4 = min(s + 4, s_end - 1);
+    const f16x8 a0 = dq_pack(g[0]), a1 = dq_pack(g[1]);
+    uint32_t off[2][8];
+    window_offsets8(wr[(u + 1) & 3][0][0], wr[(u + 1) & 3][0][1], off[0]);
+    window_offsets8(wr[(u + 1) & 3][1][0], wr[(u + 1) & 3][1][1], off[1]);
+    f16x8 xq[kXAhead + 1];
+#pragma unroll
+    for (int i = 0; i < kXAhead; ++i) xq[i] = xfrag(b, i);
+#pragma unroll
+    for (int qt = 0; qt < 16; ++qt) {
+      if (qt + kXAhead < 16) xq[(qt + kXAhead) % (kXAhead + 1)] = xfrag(b, qt + kXAhead);
+      acc[0][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, xq[qt % (kXAhead + 1)], acc[0][qt], 0, 0, 0);
+      acc[1][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, xq[qt % (kXAhead + 1)], acc[1][qt], 0, 0, 0);
+      if (qt >= kGatherSlot && qt < kGatherSlot + 8) {
+        g[0][qt - kGatherSlot] = lds_cb(cb_lds, off[0][qt - kGatherSlot]);
+        g[1][qt - kGatherSlot] = lds_cb(cb_lds, off[1][qt - kGatherSlot]);
+      }
+      if (qt == kCodeSlot) load_codes(s4, wr[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // every wave is done with x buffer b and its loads of stage s + 1 (issued
+    // before this step's kCodeLoads code-word loads) have landed; then stage
+    // s + 2 goes into buffer b
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCodeLoads) : "memory");
+    __syncthreads();
+    load_x(min(s + 2, s_end - 1), b);
+  };
+  using U0 = std::integral_constant<int, 0>;
+  using U1 = std::integral_constant<int, 1>;
+  using U2 = std::integral_constant<int, 2>;
+  using U3 = std::integral_constant<int, 3>;
+  // every k range is a whole number of 2-step blocks here (the plan cuts K
+  // in multiples of 4 16-k steps) but not always of 4
+  int s = s_begin;
+  for (; s + 3 < s_end; s += 4) {
+    step(U0{}, s);
+    step(U1{}, s + 1);
+    step(U2{}, s + 2);
+    step(U3{}, s + 3);
+  }
+  if (s < s_end) {
+    step(U0{}, s);
+    step(U1{}, s + 1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last (repeated) loads land before the LDS is reused
+  __syncthreads();
+
+  // Lane holds D[p = p0 + 16 f + 4 (lane >> 4) + r][q = 16 qt + (lane & 15)].
+  const int pl = 16 * 0 + 4 * (lane >> 4), ql = lane & 15;
+  if (TAIL) {
+    // partials[w][q][p] over the unit's 256 rows and 256 columns
+    if (!pvalid) return;
+    float* base = partials + (int64_t)blockIdx.x * DQ2_R * DQ_COLS_WG + wave * 32 + pl;
+#pragma unroll
+    for (int qt = 0; qt < 16; ++qt)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+        *reinterpret_cast<f32x4*>(base + (16 * qt + ql) * DQ_COLS_WG + 16 * f) = acc[f][qt];
+    return;
+  }
+
+  // A whole unit: column scales into the accumulators, then two rounds of
+  // 128 rows through the LDS (fp32 [row][256 columns], 128 KiB, where the
+  // codebook was): 16 lanes per (row, 128-column block) read 8 consecutive
+  // columns, rotate (the arithmetic of the decode path's output stage),
+  // apply the signs and store fp16 y.
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const u32x2 sc = *reinterpret_cast<const u32x2*>(scale + p0 + 16 * f + pl);
+    const float s0 = bits_lo_f16(sc[0]), s1 = bits_hi_f16(sc[0]), s2 = bits_lo_f16(sc[1]), s3 = bits_hi_f16(sc[1]);
+#pragma unroll
+    for (int qt = 0; qt < 16; ++qt) {
+      acc[f][qt][0] *= s0;
+      acc[f][qt][1] *= s1;
+      acc[f][qt][2] *= s2;
+      acc[f][qt][3] *= s3;
+    }
+  }
+  float* tb = reinterpret_cast<float*>(lds);
+  const uint32_t smask = sign_n ? 0x80008000u : 0u;
+#pragma unroll
+  for (int rnd = 0; rnd < 2; ++rnd) {
+    if (pvalid)
+#pragma unroll
+      for (int qt = 0; qt < 8; ++qt)
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          *reinterpret_cast<f32x4*>(tb + (16 * qt + ql) * DQ_COLS_WG + wave * 32 + 16 * f + pl) = acc[f][8 * rnd + qt];
+    __syncthreads();
+    // 128 rows x 2 blocks x 16 lanes = 4096 lane tasks, 8 per thread
+    const int q16 = threadIdx.x & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int item = (threadIdx.x >> 4) + 32 * i;  // (row, block)
+      const int r = item >> 1, blk = item & 1;
+      const int row = pass * DQ2_R + 128 * rnd + r;
+      const int col0 = pb * DQ_COLS_WG + 128 * blk;
+      const f32x4* src = reinterpret_cast<const f32x4*>(tb + r * DQ_COLS_WG + 128 * blk + 8 * q16);
+      const f32x4 v0 = src[0], v1 = src[1];
+      float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      wht128_16(v, q16);
+      if (row < M && col0 < N) {  // uniform over the 16 lanes
+        const int col = col0 + 8 * q16;
+        const u32x4 sg = *reinterpret_cast<const u32x4*>((sign_n ? sign_n : scale) + col);
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * EXL3_INV_SQRT128, v[2 * j + 1] * EXL3_INV_SQRT128);
+        o ^= sg & smask;
+        *reinterpret_cast<u32x4*>(y + (int64_t)row * ldy + col) = o;
+      }
+    }
+    __syncthreads();  // the buffer is rewritten in the next round
+  }
+}
+
 // Sums the tail pieces of one unit in k order, applies the column scales,
 // the output rotation and the signs, and stores fp16 y: 16 lanes per (unit,
 // row, 128-column block), 8 columns per lane (the arithmetic of the decode
@@ -355,6 +595,24 @@ __global__ __launch_bounds__(256) void dq_fixup_kernel(const float* __restrict__
   for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * EXL3_INV_SQRT128, v[2 * j + 1] * EXL3_INV_SQRT128);
   o ^= sg & smask;
   if (ok) *reinterpret_cast<u32x4*>(y + (int64_t)row * ldy + col) = o;
+}
+
+hipError_t launch_dqgemm2(const uint16_t* xf16, const uint32_t* codes, const uint16_t* cb, const uint16_t* scale,
+                          const uint16_t* sign_n, uint16_t* y, int64_t ldy, float* partials, int32_t K, int32_t N,
+                          int32_t ldt, int32_t M, const DqPlan& plan, hipStream_t stream) {
+  if (plan.nqb != 8) return hipErrorInvalidValue;
+  if (plan.full > 0)
+    dqgemm2_kernel<false><<<plan.full, DQ2_THREADS, 0, stream>>>(xf16, codes, cb, scale, sign_n, y, ldy, partials, K,
+                                                                 N, ldt, M, plan);
+  if (plan.tail > 0)
+    dqgemm2_kernel<true><<<plan.tail * plan.tail_ks, DQ2_THREADS, 0, stream>>>(xf16, codes, cb, scale, sign_n, y, ldy,
+                                                                               partials, K, N, ldt, M, plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.tail == 0) return e;
+  const int64_t threads = (int64_t)plan.tail * DQ2_R * 2 * 16;
+  dq_fixup_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(partials, DQ2_R, plan, scale, sign_n, y,
+                                                                          ldy, M, N);
+  return hipGetLastError();
 }
 
 size_t dq_partial_bytes(const DqPlan& plan) {

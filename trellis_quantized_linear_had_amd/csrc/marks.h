@@ -28,7 +28,9 @@ enum KernelVariant {
   kVariantReconstructGemm = 2,
   kVariantDequantGemm = 3,
   kVariantDequantGemmWhole = 4,  // the dequant-GEMM with every unit over all of K (no split tail)
-  kVariantLast = 4
+  kVariantDequantGemm8 = 5,      // the eight-wave dequant-GEMM (256-row passes, Xr staged in LDS)
+  kVariantDequantGemm8Whole = 6,  // the eight-wave dequant-GEMM with every unit over all of K
+  kVariantLast = 6
 };
 
 inline hipError_t mark_begin(Marks* m, int kind, hipStream_t s) {

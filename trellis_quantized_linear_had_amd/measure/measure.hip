@@ -40,7 +40,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int make_marks(exl3::Marks& m, int kind, int capacity, void** start, void** stop, int* used, int variant = 0) {
   if (kind < 0 || kind >= exl3::kMarkKinds) return mfail(EXL3_EINVAL, "mark kind %d is not 0..3", kind);
-  if (variant < 0 || variant > exl3::kVariantLast) return mfail(EXL3_EINVAL, "variant %d is not 0..4", variant);
+  if (variant < 0 || variant > exl3::kVariantLast) return mfail(EXL3_EINVAL, "variant %d is not 0..%d", variant, (int)exl3::kVariantLast);
   if (capacity < 0 || (capacity > 0 && (!start || !stop)) || !used)
     return mfail(EXL3_EINVAL, "bad event arrays (capacity %d)", capacity);
   m = exl3::Marks{kind, capacity, 0, reinterpret_cast<hipEvent_t*>(start), reinterpret_cast<hipEvent_t*>(stop),
