@@ -388,9 +388,9 @@ PMC_KERNELS = {
                     ("reconstruct.hip", "trellis.h", "common.h")),
     # the down-projection geometry, where all 160 tiles run as stream-K pieces
     "gemm_tail": ("exl3::gemm_had_kernel<1>", "gemm_had_kernel<1> K17408xN5120 M=2048", ("gemm_f16.hip", "common.h")),
-    # the dequant-GEMM at M = 256 (the dispatch's choice there): 68 units of 256 rows x 256 columns, each
-    # split in three k pieces
-    "dq": ("exl3::dqgemm_kernel<8, true>", "dqgemm_kernel<8,true> K5120xN17408 M=256",
+    # the eight-wave dequant-GEMM at M = 256 (the dispatch's choice there): 68 units of 256 rows x 256
+    # columns, each split in three k pieces
+    "dq": ("exl3::dqgemm2_kernel<true>", "dqgemm2_kernel<true> K5120xN17408 M=256",
            ("dqgemm.hip", "dq_plan.h", "epilogue.h", "trellis.h", "common.h")),
 }
 
