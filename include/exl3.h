@@ -118,22 +118,21 @@ typedef struct exl3_layer {
  *     rotation into scratch; then, per slice of at most EXL3_MAX_CHUNK_COLS
  *     columns, reconstruct the slice to fp16 into scratch and run the MFMA
  *     GEMM whose epilogue applies the output rotation and sign_n;
- *   - fused, decode-GEMM (widths other than 4; 4 bits below 48 rows): a
+ *   - fused, decode-GEMM (widths other than 4; 4 bits up to 32 rows): a
  *     kernel that decodes every trellis tile once per pass of up to 64 rows
  *     and multiplies it with those rows -- for M <= 16 it also applies the
  *     input rotation itself, otherwise a rotation pass writes it to scratch
  *     first -- then an output-stage kernel that sums the split-K partials in
  *     a fixed order and applies the output rotation and sign_n;
- *   - dequant-GEMM (4 bits: 48 rows and up on the fused side, up to 1024 rows
+ *   - dequant-GEMM (4 bits: 33 rows and up on the fused side, up to 1024 rows
  *     on the prefill side) [P316 follow-up item 4: dequantisation fused into
- *     the GEMM]: input rotation into scratch, then an MFMA GEMM that decodes
- *     each trellis tile into its operand registers once per pass of rows --
- *     below 192 rows a four-wave kernel with passes of 32 to 256 rows, from
- *     192 rows an eight-wave kernel with 256-row passes whose rows of the
- *     rotated input are staged in LDS -- and applies scales, output rotation
- *     and sign_n in its epilogue; a K-split remainder of the work leaves fp32
- *     partials that a fixup kernel sums in a fixed order before the same
- *     epilogue.
+ *     the GEMM]: input rotation into scratch, then an MFMA GEMM of eight waves
+ *     that decodes each trellis tile into its operand registers once per pass
+ *     of 64, 128 or 256 rows (the shortest that covers M) while the pass's
+ *     rows of the rotated input are staged in LDS, and applies scales, output
+ *     rotation and sign_n in its epilogue; a K-split remainder of the work
+ *     leaves fp32 partials that a fixup kernel sums in a fixed order before
+ *     the same epilogue.
  * All three give y within the fp16 rounding of the same sums, not
  * bit-identical to each other. M = 0 is a no-op returning EXL3_OK.
  * Limits (EXL3_ESHAPE otherwise): K, N positive multiples of 128, K < 65536,

@@ -69,17 +69,17 @@ def require_gpu():
 
 
 # exl3_linear's kernel sequences: the decode-GEMM ("fused"), reconstruct +
-# GEMM ("recon") and the dequant-GEMMs ("dq", four waves, and "dq8", eight
-# waves; 4 bits only). At 4 bits the dispatch takes a dequant-GEMM from 48
-# rows on the fused side and up to 1024 rows on the prefill side: the
-# eight-wave one from 192 rows on.
-DQ_FUSED_MIN_ROWS, DQ_PREFILL_MAX_ROWS, DQ8_MIN_ROWS = 48, 1024, 192
+# GEMM ("recon") and the dequant-GEMMs ("dq8", eight waves, and "dq", four
+# waves, forced only; 4 bits only). At 4 bits the dispatch takes the
+# eight-wave dequant-GEMM from 33 rows on the fused side and up to 1024 rows
+# on the prefill side.
+DQ_FUSED_MIN_ROWS, DQ_PREFILL_MAX_ROWS = 33, 1024
 
 
 def route(bits: int, M: int, pm: int) -> str:
     prefill = pm > 0 and M >= pm
     if bits == 4 and (M <= DQ_PREFILL_MAX_ROWS if prefill else M >= DQ_FUSED_MIN_ROWS):
-        return "dq8" if M >= DQ8_MIN_ROWS else "dq"
+        return "dq8"
     return "recon" if prefill else "fused"
 
 

@@ -136,7 +136,7 @@ def run_linear(X, L, cb, x, pm):
     return host16(X.linear(dev16(x), lay, prefill_min_m=pm))
 
 
-@pytest.mark.parametrize("M", [1, 5, 16, 17, 47, 48, 64, 127, 128, 130, 191, 192, 300, 1024, 1025])
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 32, 33, 47, 48, 64, 65, 127, 128, 129, 130, 191, 192, 300, 1024, 1025])
 def test_linear_tiny_every_route(T, X, cb, M):
     """Each kernel sequence (forced) against the oracle, and the dispatch:
     the default threshold, 0 (fused side only) and 1 (prefill side only)

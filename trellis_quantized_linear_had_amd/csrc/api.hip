@@ -290,9 +290,13 @@ DecodeLayout decode_layout(int32_t K, int32_t N, int64_t M, int32_t bits) {
 // written and read back. The step costs (0.27, 0.32, 0.40 and 0.52 us for 1,
 // 2, 4 and 8 fragments) are the slopes of whole-unit runs over K at the MLP
 // geometries: the four waves' LDS gathers bound one fragment, the MFMAs and
-// the shared operand loads the larger passes.
-DqPlan plan_dq_rows(int32_t K, int32_t N, int64_t M, int nqb, bool whole, double& best) {
+// the shared operand loads the larger passes. The eight-wave kernel's step
+// costs (0.28, 0.32 and 0.55 us for passes of 64, 128 and 256 rows): the
+// 256-row slope of its whole-unit rounds at M = 2048, and the shorter passes
+// scaled by their measured calls.
+DqPlan plan_dq_rows(int32_t K, int32_t N, int64_t M, int nqb, bool whole, double& best, bool eight_waves = false) {
   static constexpr double kStepUs[9] = {0, 0.27, 0.32, 0, 0.40, 0, 0, 0, 0.52};
+  static constexpr double kStepUs8[9] = {0, 0, 0.28, 0, 0.32, 0, 0, 0, 0.55};
   DqPlan p;
   p.nqb = nqb;
   const int R = 32 * nqb;
@@ -300,7 +304,7 @@ DqPlan plan_dq_rows(int32_t K, int32_t N, int64_t M, int nqb, bool whole, double
   p.pblocks = (N + 255) / 256;
   const int ksub = K / 16;
   const int64_t units = (int64_t)p.passes * p.pblocks;
-  const double step_us = kStepUs[nqb], wg_us = 3.0;
+  const double step_us = (eight_waves ? kStepUs8 : kStepUs)[nqb], wg_us = 3.0;
   auto rounds = [](int64_t wgs) { return (double)((wgs + 255) / 256); };
   best = 1e300;
   p.full = (int32_t)units;
@@ -334,17 +338,22 @@ DqPlan plan_dq_rows(int32_t K, int32_t N, int64_t M, int nqb, bool whole, double
 
 // The least modelled time over the row-fragment counts that leave no whole
 // fragment of a pass empty (a pass of R rows serves M in ceil(M / R) passes).
+// The eight-wave kernel takes the shortest pass of 64, 128 or 256 rows that
+// covers M (256 above): its step is bound by the codebook gathers, which a
+// second pass repeats, more than by the MFMAs and Xr reads a taller pass
+// adds (K17408 x N5120, M = 256: one 256-row pass 74 us, two 128-row passes
+// 83 us).
 DqPlan plan_dq(int32_t K, int32_t N, int64_t M, bool whole = false, bool eight_waves = false) {
   DqPlan best_plan{};
-  if (eight_waves) {
-    double t;
-    return plan_dq_rows(K, N, M, 8, whole, t);
-  }
   double best = 1e300;
+  if (eight_waves) {
+    const int nqb = M <= 64 ? 2 : M <= 128 ? 4 : 8;
+    return plan_dq_rows(K, N, M, nqb, whole, best, true);
+  }
   for (int nqb : {1, 2, 4, 8}) {
     if (nqb > 1 && 32 * (nqb / 2) >= M) break;
     double t;
-    const DqPlan p = plan_dq_rows(K, N, M, nqb, whole, t);
+    const DqPlan p = plan_dq_rows(K, N, M, nqb, whole, t, eight_waves);
     if (t < best - 1e-9) {
       best = t;
       best_plan = p;
@@ -391,12 +400,13 @@ const char* exl3_strerror(int status) {
 
 namespace {
 
-// The kernel sequence of one call. At 4 bits the dequant-GEMMs take the row
-// counts where they measured fastest on both MLP geometries: from 48 rows on
-// the fused side (the decode-GEMM below) and up to 1024 rows on the prefill
-// side (reconstruct + GEMM above); the four-wave kernel (passes of 32 to 256
-// rows) below 192 rows, the eight-wave one (256-row passes) from 192 rows on.
-// A forced variant overrides the choice.
+// The kernel sequence of one call. At 4 bits the eight-wave dequant-GEMM
+// takes the row counts where it measured fastest on both MLP geometries:
+// from 33 rows on the fused side (the decode-GEMM below, whose cost steps up
+// past 32 rows) and up to 1024 rows on the prefill side (reconstruct + GEMM
+// above). The four-wave dequant-GEMM
+// is slower at every row count measured and runs only when forced, as do the
+// other sequences outside their ranges.
 enum Route {
   kRouteDecode,
   kRouteReconstructGemm,
@@ -405,7 +415,7 @@ enum Route {
   kRouteDequantGemm8,
   kRouteDequantGemm8Whole
 };
-constexpr int64_t kDqFusedMinRows = 48, kDqPrefillMaxRows = 1024, kDq8MinRows = 192;
+constexpr int64_t kDqFusedMinRows = 33, kDqPrefillMaxRows = 1024;
 
 Route route_of(int32_t bits, int64_t M, int32_t prefill_min_m, int variant) {
   switch (variant) {
@@ -425,7 +435,7 @@ Route route_of(int32_t bits, int64_t M, int32_t prefill_min_m, int variant) {
       break;
   }
   const bool dq_ok = bits == 4;
-  const Route dq = M >= kDq8MinRows ? kRouteDequantGemm8 : kRouteDequantGemm;
+  const Route dq = kRouteDequantGemm8;
   if (use_prefill(M, prefill_min_m)) return dq_ok && M <= kDqPrefillMaxRows ? dq : kRouteReconstructGemm;
   return dq_ok && M >= kDqFusedMinRows ? dq : kRouteDecode;
 }

@@ -303,23 +303,36 @@ __global__ __launch_bounds__(DQ_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
 }
 
 // ---- Eight-wave form: 32 columns per wave (two 16-column A fragments of
-// v_mfma_f32_16x16x32_f16), one pass of 256 rows, the pass's rows of Xr
-// staged once per workgroup in the LDS beside the codebook (16-row fragment
-// order, 16 KiB per 32-k step, two stages), so each wave reads them from LDS
-// instead of loading them itself, and two waves per SIMD hide each other's
-// waits. A lane of A fragment f holds 8 consecutive k of column p: k-tile
-// (lane >> 5) of the step, half (lane >> 4) & 1 of that tile's 16 steps.
+// v_mfma_f32_16x16x32_f16), one pass of R = 16 NQ rows (NQ = 4, 8 or 16 row
+// fragments), the pass's rows of Xr staged once per workgroup in the LDS
+// beside the codebook (16-row fragment order, NQ KiB per 32-k step, two
+// stages), so each wave reads them from LDS instead of loading them itself,
+// and two waves per SIMD hide each other's waits. A lane of A fragment f
+// holds 8 consecutive k of column p: k-tile (lane >> 5) of the step, half
+// (lane >> 4) & 1 of that tile's 16 steps.
 #define DQ2_THREADS 512
-#define DQ2_R 256
-#define DQ2_XSTAGE (16 * 512)  // halves per x stage: 16 fragments of 16 rows x 32 k
 
-template <bool TAIL>
+// One direct-to-LDS buffer load of 16 bytes per lane (lane i's bytes land at
+// dst + 16 i). A plain function: called with arguments that depend on a
+// kernel template's parameters, the builtin made the compiler drop that
+// template's instantiations without a diagnostic.
+__device__ __forceinline__ void dq_buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, dq_lds_void* dst, uint32_t voff,
+                                                     uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, soff, 0, 0);
+}
+
+template <int NQ, bool TAIL>
 __global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void dqgemm2_kernel(
     const uint16_t* __restrict__ xf, const uint32_t* __restrict__ codes, const uint16_t* __restrict__ cb,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ sign_n, uint16_t* __restrict__ y, int64_t ldy,
     float* __restrict__ partials, int32_t K, int32_t N, int32_t ldt, int32_t M, DqPlan plan) {
+  static_assert(NQ == 4 || NQ == 8 || NQ == 16, "row fragments per pass");
+  constexpr int R = 16 * NQ;          // rows per pass
+  constexpr int XSTAGE = NQ * 512;    // halves per x stage
+  constexpr int FPW = NQ >= 8 ? NQ / 8 : 1;  // x fragments each loading wave stages per step
+  constexpr int XWAVES = NQ / FPW;    // waves that stage x (the first XWAVES)
   // the codebook, then two x stages; after the last codebook read, the output stage's transpose buffer
-  __shared__ __align__(16) uint16_t lds[65536 + 2 * DQ2_XSTAGE];
+  __shared__ __align__(16) uint16_t lds[65536 + 2 * XSTAGE];
   uint16_t* cb_lds = lds;
   uint16_t* xs = lds + 65536;
 
@@ -374,32 +387,36 @@ __global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
       for (int j = 0; j < 2; ++j) w[f][j] = buffer_load_u32(crs, voff[f][j], (uint32_t)(2 * s) * row_bytes);
   };
 
-  // x stage of step s: the pass's 16 row fragments (16 rows x 32 k each),
+  // x stage of step s: the pass's NQ row fragments (16 rows x 32 k each),
   // clamped to the last fragment of the padded rows (rows past M are zero
-  // or repeats and are never stored); wave w loads fragments 2 w and 2 w + 1.
-  // Buffer loads (a fixed lane offset, the step in the scalar offset): no
-  // 64-bit address registers to rebuild while code-word loads are in flight.
-  const int nq16 = (M + 31) / 32 * 2, q16_0 = pass * 16;
+  // or repeats and are never stored); wave w < XWAVES loads fragments
+  // FPW w .. + FPW - 1. Buffer loads (a fixed lane offset, the step in the
+  // scalar offset): no 64-bit address registers to rebuild while code-word
+  // loads are in flight.
+  const int nq16 = (M + 31) / 32 * 2, q16_0 = pass * NQ;
   const __amdgpu_buffer_rsrc_t xrs =
-      make_rsrc(xf + (int64_t)q16_0 * ks32 * 512, (uint32_t)(min(16, nq16 - q16_0) * ks32 * 1024));
-  uint32_t xoff[2];
+      make_rsrc(xf + (int64_t)q16_0 * ks32 * 512, (uint32_t)(min(NQ, nq16 - q16_0) * ks32 * 1024));
+  uint32_t xoff[FPW];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) xoff[j] = (uint32_t)((min(q16_0 + 2 * wave + j, nq16 - 1) - q16_0) * ks32 * 1024 + 16 * lane);
+  for (int j = 0; j < FPW; ++j)
+    xoff[j] = (uint32_t)((min(q16_0 + FPW * wave + j, nq16 - 1) - q16_0) * ks32 * 1024 + 16 * lane);
   auto load_x = [&](int s, int buf) {
+    if (XWAVES == DQ2_THREADS / 64 || wave < XWAVES) {  // uniform per wave
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (dq_lds_void*)(xs + buf * DQ2_XSTAGE + (2 * wave + j) * 512), 16,
-                                               xoff[j], (uint32_t)s * 1024, 0, 0);
+      for (int j = 0; j < FPW; ++j)
+        dq_buffer_load_lds16(xrs, (dq_lds_void*)(xs + buf * XSTAGE + (FPW * wave + j) * 512), xoff[j],
+                             (uint32_t)s * 1024);
+    }
   };
   auto xfrag = [&](int buf, int qt) {
-    return *reinterpret_cast<const f16x8*>(xs + buf * DQ2_XSTAGE + qt * 512 + 8 * lane);
+    return *reinterpret_cast<const f16x8*>(xs + buf * XSTAGE + qt * 512 + 8 * lane);
   };
 
-  f32x4 acc[2][16];
+  f32x4 acc[2][NQ];
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int qt = 0; qt < 16; ++qt) acc[f][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < NQ; ++qt) acc[f][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   // Rings: code words of steps s .. s + 3; the codebook reads of step s + 1
   // are issued during step s.
@@ -415,16 +432,18 @@ __global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   dq_gather(cb_lds, wr[0][1], g[1]);
 
   // Step s (ring phase u = (s - s_begin) % 4, x buffer b = (s - s_begin) % 2):
-  // 16 slots, each the 2 MFMAs of one row fragment plus one piece of the next
-  // step's work in source order fenced by scheduling barriers: the x
-  // fragment kXAhead slots ahead, (slot 4) the code words of s + 4, and
-  // (slots 8..15) the codebook reads of s + 1. Measured at M = 256..2048 on
-  // both MLP geometries: fragments 6 ahead and the reads in the second half
-  // beat 2 ahead and the first half by 2-4 %; staggering the halves between
-  // the two waves of a SIMD, or one read pair per slot, did not help.
-  constexpr int kXAhead = 6, kCodeSlot = 4, kGatherSlot = 8;
-  static_assert(kGatherSlot + 8 <= 16, "all 8 codebook read pairs of the next step are issued inside the step");
-  static_assert(kCodeSlot < 16 && kXAhead < 16, "slot numbers");
+  // NQ slots, each the 2 MFMAs of one row fragment plus one piece of the
+  // next step's work in source order fenced by scheduling barriers: the x
+  // fragment kXAhead slots ahead, (slot kCodeSlot) the code words of s + 4,
+  // and (slots kGatherSlot..NQ - 1, evenly) the 8 codebook read pairs of
+  // s + 1. Measured at M = 256..2048 on both MLP geometries with 16
+  // fragments: fragments 6 ahead and the reads in the second half beat 2
+  // ahead and the first half by 2-4 %; staggering the halves between the two
+  // waves of a SIMD, or one read pair per slot, did not help.
+  constexpr int kXAhead = NQ < 6 ? NQ : 6, kCodeSlot = NQ >= 8 ? 4 : 1, kGatherSlot = NQ == 16 ? 8 : 0;
+  constexpr int kGatherPerSlot = 8 / (NQ - kGatherSlot);
+  static_assert(kGatherPerSlot * (NQ - kGatherSlot) == 8, "all 8 codebook read pairs of the next step are issued");
+  static_assert(kCodeSlot < NQ && kXAhead <= NQ, "slot numbers");
   auto step = [&](auto U, int s) {
     constexpr int u = decltype(U)::value, b = u & 1;
     const int s4 = min(s + 4, s_end - 1);
@@ -436,13 +455,17 @@ __global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int i = 0; i < kXAhead; ++i) xq[i] = xfrag(b, i);
 #pragma unroll
-    for (int qt = 0; qt < 16; ++qt) {
-      if (qt + kXAhead < 16) xq[(qt + kXAhead) % (kXAhead + 1)] = xfrag(b, qt + kXAhead);
+    for (int qt = 0; qt < NQ; ++qt) {
+      if (qt + kXAhead < NQ) xq[(qt + kXAhead) % (kXAhead + 1)] = xfrag(b, qt + kXAhead);
       acc[0][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, xq[qt % (kXAhead + 1)], acc[0][qt], 0, 0, 0);
       acc[1][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, xq[qt % (kXAhead + 1)], acc[1][qt], 0, 0, 0);
-      if (qt >= kGatherSlot && qt < kGatherSlot + 8) {
-        g[0][qt - kGatherSlot] = lds_cb(cb_lds, off[0][qt - kGatherSlot]);
-        g[1][qt - kGatherSlot] = lds_cb(cb_lds, off[1][qt - kGatherSlot]);
+      if (qt >= kGatherSlot) {
+#pragma unroll
+        for (int i = 0; i < kGatherPerSlot; ++i) {
+          const int j = (qt - kGatherSlot) * kGatherPerSlot + i;
+          g[0][j] = lds_cb(cb_lds, off[0][j]);
+          g[1][j] = lds_cb(cb_lds, off[1][j]);
+        }
       }
       if (qt == kCodeSlot) load_codes(s4, wr[u]);
       __builtin_amdgcn_sched_barrier(0);
@@ -475,30 +498,31 @@ __global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   __syncthreads();
 
   // Lane holds D[p = p0 + 16 f + 4 (lane >> 4) + r][q = 16 qt + (lane & 15)].
-  const int pl = 16 * 0 + 4 * (lane >> 4), ql = lane & 15;
+  const int pl = 4 * (lane >> 4), ql = lane & 15;
   if (TAIL) {
-    // partials[w][q][p] over the unit's 256 rows and 256 columns
+    // partials[w][q][p] over the unit's R rows and 256 columns
     if (!pvalid) return;
-    float* base = partials + (int64_t)blockIdx.x * DQ2_R * DQ_COLS_WG + wave * 32 + pl;
+    float* base = partials + (int64_t)blockIdx.x * R * DQ_COLS_WG + wave * 32 + pl;
 #pragma unroll
-    for (int qt = 0; qt < 16; ++qt)
+    for (int qt = 0; qt < NQ; ++qt)
 #pragma unroll
       for (int f = 0; f < 2; ++f)
         *reinterpret_cast<f32x4*>(base + (16 * qt + ql) * DQ_COLS_WG + 16 * f) = acc[f][qt];
     return;
   }
 
-  // A whole unit: column scales into the accumulators, then two rounds of
-  // 128 rows through the LDS (fp32 [row][256 columns], 128 KiB, where the
+  // A whole unit: column scales into the accumulators, then rounds of RR
+  // rows through the LDS (fp32 [row][256 columns], up to 128 KiB, where the
   // codebook was): 16 lanes per (row, 128-column block) read 8 consecutive
   // columns, rotate (the arithmetic of the decode path's output stage),
   // apply the signs and store fp16 y.
+  constexpr int RR = R < 128 ? R : 128, QR = RR / 16;
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const u32x2 sc = *reinterpret_cast<const u32x2*>(scale + p0 + 16 * f + pl);
     const float s0 = bits_lo_f16(sc[0]), s1 = bits_hi_f16(sc[0]), s2 = bits_lo_f16(sc[1]), s3 = bits_hi_f16(sc[1]);
 #pragma unroll
-    for (int qt = 0; qt < 16; ++qt) {
+    for (int qt = 0; qt < NQ; ++qt) {
       acc[f][qt][0] *= s0;
       acc[f][qt][1] *= s1;
       acc[f][qt][2] *= s2;
@@ -508,21 +532,22 @@ __global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   float* tb = reinterpret_cast<float*>(lds);
   const uint32_t smask = sign_n ? 0x80008000u : 0u;
 #pragma unroll
-  for (int rnd = 0; rnd < 2; ++rnd) {
+  for (int rnd = 0; rnd < R / RR; ++rnd) {
     if (pvalid)
 #pragma unroll
-      for (int qt = 0; qt < 8; ++qt)
+      for (int qt = 0; qt < QR; ++qt)
 #pragma unroll
         for (int f = 0; f < 2; ++f)
-          *reinterpret_cast<f32x4*>(tb + (16 * qt + ql) * DQ_COLS_WG + wave * 32 + 16 * f + pl) = acc[f][8 * rnd + qt];
+          *reinterpret_cast<f32x4*>(tb + (16 * qt + ql) * DQ_COLS_WG + wave * 32 + 16 * f + pl) =
+              acc[f][QR * rnd + qt];
     __syncthreads();
-    // 128 rows x 2 blocks x 16 lanes = 4096 lane tasks, 8 per thread
+    // RR rows x 2 blocks x 16 lanes = 32 RR lane tasks, RR / 16 per thread
     const int q16 = threadIdx.x & 15;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < RR / 16; ++i) {
       const int item = (threadIdx.x >> 4) + 32 * i;  // (row, block)
       const int r = item >> 1, blk = item & 1;
-      const int row = pass * DQ2_R + 128 * rnd + r;
+      const int row = pass * R + RR * rnd + r;
       const int col0 = pb * DQ_COLS_WG + 128 * blk;
       const f32x4* src = reinterpret_cast<const f32x4*>(tb + r * DQ_COLS_WG + 128 * blk + 8 * q16);
       const f32x4 v0 = src[0], v1 = src[1];
@@ -597,21 +622,37 @@ __global__ __launch_bounds__(256) void dq_fixup_kernel(const float* __restrict__
   if (ok) *reinterpret_cast<u32x4*>(y + (int64_t)row * ldy + col) = o;
 }
 
+// The eight-wave dequant-GEMM: passes of R = 32 * plan.nqb rows (nqb 2, 4 or
+// 8: NQ = 2 nqb row fragments of 16), whole units, then k-split pieces and
+// their fixup.
 hipError_t launch_dqgemm2(const uint16_t* xf16, const uint32_t* codes, const uint16_t* cb, const uint16_t* scale,
                           const uint16_t* sign_n, uint16_t* y, int64_t ldy, float* partials, int32_t K, int32_t N,
                           int32_t ldt, int32_t M, const DqPlan& plan, hipStream_t stream) {
-  if (plan.nqb != 8) return hipErrorInvalidValue;
-  if (plan.full > 0)
-    dqgemm2_kernel<false><<<plan.full, DQ2_THREADS, 0, stream>>>(xf16, codes, cb, scale, sign_n, y, ldy, partials, K,
-                                                                 N, ldt, M, plan);
-  if (plan.tail > 0)
-    dqgemm2_kernel<true><<<plan.tail * plan.tail_ks, DQ2_THREADS, 0, stream>>>(xf16, codes, cb, scale, sign_n, y, ldy,
-                                                                               partials, K, N, ldt, M, plan);
+  if (plan.nqb != 2 && plan.nqb != 4 && plan.nqb != 8) return hipErrorInvalidValue;
+#define EXL3_DQ2_LAUNCH(nq, tail, grid)                                                                         \
+  dqgemm2_kernel<nq, tail><<<(grid), DQ2_THREADS, 0, stream>>>(xf16, codes, cb, scale, sign_n, y, ldy, partials, K, \
+                                                               N, ldt, M, plan)
+#define EXL3_DQ2_LAUNCH_NQ(tail, grid)    \
+  switch (plan.nqb) {                      \
+    case 2:                                \
+      EXL3_DQ2_LAUNCH(4, tail, grid);      \
+      break;                               \
+    case 4:                                \
+      EXL3_DQ2_LAUNCH(8, tail, grid);      \
+      break;                               \
+    default:                               \
+      EXL3_DQ2_LAUNCH(16, tail, grid);     \
+  }
+  if (plan.full > 0) EXL3_DQ2_LAUNCH_NQ(false, plan.full)
+  if (plan.tail > 0) EXL3_DQ2_LAUNCH_NQ(true, plan.tail * plan.tail_ks)
+#undef EXL3_DQ2_LAUNCH_NQ
+#undef EXL3_DQ2_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.tail == 0) return e;
-  const int64_t threads = (int64_t)plan.tail * DQ2_R * 2 * 16;
-  dq_fixup_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(partials, DQ2_R, plan, scale, sign_n, y,
-                                                                          ldy, M, N);
+  const int R = 32 * plan.nqb;
+  const int64_t threads = (int64_t)plan.tail * R * 2 * 16;
+  dq_fixup_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(partials, R, plan, scale, sign_n, y, ldy, M,
+                                                                          N);
   return hipGetLastError();
 }
 
