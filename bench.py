@@ -568,7 +568,7 @@ def sweep(bits: int = 4) -> str:
            "|---|---|---|" + "---|" * len(variants) + "---|---|---|"]
     cross = {}
     geoms = ((5120, 17408), (17408, 5120)) if bits == 4 else ((5120, 17408), (17408, 5120), (5120, 5120))
-    Ms = (16, 32, 48, 64, 96, 128, 192, 256, 384, 512, 1024, 2048, 4096) if bits == 4 else (
+    Ms = (16, 32, 33, 48, 64, 96, 128, 192, 256, 384, 512, 1024, 2048, 4096) if bits == 4 else (
         16, 32, 64, 96, 128, 192, 256, 512, 1024)
     for gi, (Kg, Ng) in enumerate(geoms):
         layers = [X.Layer.from_numpy(W.layer(W.SEED_PREFILL, Kg, Ng, 2 * s + gi, bits), cb) for s in range(6)]
@@ -741,7 +741,7 @@ def dq_sweep() -> str:
     kt = _measure.KernelTimer(pairs=512, per_call=4)
     for g, (k, n) in enumerate(((5120, 17408), (17408, 5120))):
         layers = [X.Layer.from_numpy(W.layer(W.SEED_PREFILL, k, n, 2 * s), cb) for s in range(6)]
-        for M in (16, 32, 64, 128, 192, 256, 384, 512, 1024, 2048):
+        for M in (16, 32, 33, 48, 64, 96, 128, 192, 256, 384, 512, 1024, 2048):
             x = _lib.to_device_u16(W.activations(W.SEED_PREFILL, M, k, g))
             y = torch.empty((M, n), dtype=torch.int16, device=dev)
             scr = torch.empty(max(_measure.linear_scratch_bytes(k, n, M, v) for v in (1, 2, 3, 4, 5)),
