@@ -54,11 +54,13 @@ def variant_of(eight, whole):
 
 @pytest.mark.parametrize("eight", [False, True])
 @pytest.mark.parametrize("whole", [False, True])
-@pytest.mark.parametrize("K,N", [(256, 256), (1024, 384), (512, 1152)])
+@pytest.mark.parametrize("K,N", [(128, 128), (256, 256), (1024, 384), (512, 1152)])
 @pytest.mark.parametrize("M", [1, 17, 40, 100, 128, 200, 256, 300, 513])
 def test_dqgemm_matches_oracle(T, X, K, N, M, whole, eight):
     """Both output stages: whole units (scales, rotation and signs in the
-    kernel) and K-split tail pieces summed by the fixup."""
+    kernel) and K-split tail pieces summed by the fixup. K = 128: four 32-k
+    steps, split into pieces of two (the loop's two-step remainder); N = 128:
+    half of each workgroup's waves past the last column."""
     H.announce("dqgemm K%d N%d M=%d whole=%d eight=%d" % (K, N, M, whole, eight))
     L = WL.layer(90, K, N)
     cb = WL.codebook()
