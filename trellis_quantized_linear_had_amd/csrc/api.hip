@@ -314,9 +314,13 @@ DqPlan plan_dq_rows(int32_t K, int32_t N, int64_t M, int nqb, bool whole, double
   const int64_t fr = units / 256;
   for (int64_t nf = std::max<int64_t>(0, fr - 1); nf <= fr; ++nf) {
     const int64_t full = nf * 256, tail = units - full;
-    for (int ks = 1; ks <= (whole ? 1 : std::min(ksub / 4, 16)); ++ks) {
+    // k pieces are whole blocks of `align` 16-k steps: 4 (the kernels' loops
+    // run 32-k steps in pairs), 8 for the eight-wave kernel's 64-row passes
+    // (its x stages hold four 32-k steps); ksub is a multiple of 8
+    const int align = eight_waves && nqb == 2 ? 8 : 4;
+    for (int ks = 1; ks <= (whole ? 1 : std::min(ksub / align, 16)); ++ks) {
       if (tail == 0 && ks > 1) break;
-      const int per = ((ksub + ks - 1) / ks + 3) / 4 * 4;  // whole 4-step blocks (ksub is a multiple of 8)
+      const int per = ((ksub + ks - 1) / ks + align - 1) / align * align;
       const int ks_eff = (ksub + per - 1) / per;
       double t = rounds(full) * (ksub * step_us + wg_us);
       if (ks_eff == 1) {

@@ -327,10 +327,9 @@ __global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ sign_n, uint16_t* __restrict__ y, int64_t ldy,
     float* __restrict__ partials, int32_t K, int32_t N, int32_t ldt, int32_t M, DqPlan plan) {
   static_assert(NQ == 4 || NQ == 8 || NQ == 16, "row fragments per pass");
-  constexpr int R = 16 * NQ;          // rows per pass
-  constexpr int XSTAGE = NQ * 512;    // halves per x stage
-  constexpr int FPW = NQ >= 8 ? NQ / 8 : 1;  // x fragments each loading wave stages per step
-  constexpr int XWAVES = NQ / FPW;    // waves that stage x (the first XWAVES)
+  constexpr int R = 16 * NQ;     // rows per pass
+  constexpr int SPB = 16 / NQ;   // 32-k steps per x stage: every stage holds 16 fragments (16 KiB)
+  constexpr int XSTAGE = 16 * 512;  // halves per x stage
   // the codebook, then two x stages; after the last codebook read, the output stage's transpose buffer
   __shared__ __align__(16) uint16_t lds[65536 + 2 * XSTAGE];
   uint16_t* cb_lds = lds;
@@ -387,29 +386,29 @@ __global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
       for (int j = 0; j < 2; ++j) w[f][j] = buffer_load_u32(crs, voff[f][j], (uint32_t)(2 * s) * row_bytes);
   };
 
-  // x stage of step s: the pass's NQ row fragments (16 rows x 32 k each),
-  // clamped to the last fragment of the padded rows (rows past M are zero
-  // or repeats and are never stored); wave w < XWAVES loads fragments
-  // FPW w .. + FPW - 1. Buffer loads (a fixed lane offset, the step in the
-  // scalar offset): no 64-bit address registers to rebuild while code-word
-  // loads are in flight.
+  // x stage: SPB consecutive 32-k steps of the pass's NQ row fragments (16
+  // rows x 32 k each), fragment f = j NQ + qt for step j of the stage and row
+  // fragment qt, clamped to the last fragment of the padded rows (rows past M
+  // are zero or repeats and are never stored); wave w loads fragments 2 w
+  // and 2 w + 1, which belong to one step. Buffer loads (a fixed lane
+  // offset, the step in the scalar offset): no 64-bit address registers to
+  // rebuild while code-word loads are in flight.
   const int nq16 = (M + 31) / 32 * 2, q16_0 = pass * NQ;
   const __amdgpu_buffer_rsrc_t xrs =
       make_rsrc(xf + (int64_t)q16_0 * ks32 * 512, (uint32_t)(min(NQ, nq16 - q16_0) * ks32 * 1024));
-  uint32_t xoff[FPW];
+  const int xj = (2 * wave) / NQ;  // the step of the stage this wave's fragments belong to
+  uint32_t xoff[2];
 #pragma unroll
-  for (int j = 0; j < FPW; ++j)
-    xoff[j] = (uint32_t)((min(q16_0 + FPW * wave + j, nq16 - 1) - q16_0) * ks32 * 1024 + 16 * lane);
-  auto load_x = [&](int s, int buf) {
-    if (XWAVES == DQ2_THREADS / 64 || wave < XWAVES) {  // uniform per wave
+  for (int i = 0; i < 2; ++i)
+    xoff[i] = (uint32_t)((min(q16_0 + (2 * wave + i) % NQ, nq16 - 1) - q16_0) * ks32 * 1024 + 16 * lane);
+  auto load_x = [&](int s0, int buf) {  // the stage of steps s0 .. s0 + SPB - 1
 #pragma unroll
-      for (int j = 0; j < FPW; ++j)
-        dq_buffer_load_lds16(xrs, (dq_lds_void*)(xs + buf * XSTAGE + (FPW * wave + j) * 512), xoff[j],
-                             (uint32_t)s * 1024);
-    }
+    for (int i = 0; i < 2; ++i)
+      dq_buffer_load_lds16(xrs, (dq_lds_void*)(xs + buf * XSTAGE + (2 * wave + i) * 512), xoff[i],
+                           (uint32_t)(s0 + xj) * 1024);
   };
-  auto xfrag = [&](int buf, int qt) {
-    return *reinterpret_cast<const f16x8*>(xs + buf * XSTAGE + qt * 512 + 8 * lane);
+  auto xfrag = [&](int buf, int j, int qt) {
+    return *reinterpret_cast<const f16x8*>(xs + buf * XSTAGE + (j * NQ + qt) * 512 + 8 * lane);
   };
 
   f32x4 acc[2][NQ];
@@ -424,76 +423,88 @@ __global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int u = 0; u < 4; ++u) load_codes(min(s_begin + u, s_end - 1), wr[u]);
   load_x(s_begin, 0);
-  load_x(min(s_begin + 1, s_end - 1), 1);
+  load_x(min(s_begin + SPB, s_end - SPB), 1);
   __builtin_amdgcn_s_waitcnt(0);  // the codebook, the first code words and both x stages have landed
   __syncthreads();
   uint32_t g[2][8];
   dq_gather(cb_lds, wr[0][0], g[0]);
   dq_gather(cb_lds, wr[0][1], g[1]);
 
-  // Step s (ring phase u = (s - s_begin) % 4, x buffer b = (s - s_begin) % 2):
-  // NQ slots, each the 2 MFMAs of one row fragment plus one piece of the
-  // next step's work in source order fenced by scheduling barriers: the x
-  // fragment kXAhead slots ahead, (slot kCodeSlot) the code words of s + 4,
-  // and (slots kGatherSlot..NQ - 1, evenly) the 8 codebook read pairs of
-  // s + 1. Measured at M = 256..2048 on both MLP geometries with 16
+  // Step s, phase u = (s - s_begin) % UL: code-word ring slot u % 4, x
+  // buffer (u / SPB) % 2, step u % SPB of its stage. NQ slots, each the 2
+  // MFMAs of one row fragment plus one piece of the next step's work in
+  // source order fenced by scheduling barriers: the x fragment kXAhead slots
+  // ahead, (slot kCodeSlot) the code words of s + 4, and (slots
+  // kGatherSlot..NQ - 1, evenly) the 8 codebook read pairs of s + 1. After
+  // the last step of a stage, one barrier and the loads of the stage after
+  // next. Measured at M = 256..2048 on both MLP geometries with 16
   // fragments: fragments 6 ahead and the reads in the second half beat 2
   // ahead and the first half by 2-4 %; staggering the halves between the two
-  // waves of a SIMD, or one read pair per slot, did not help.
+  // waves of a SIMD, or one read pair per slot, did not help. Stages of
+  // several steps keep the barriers of the short passes (4 and 8 fragments)
+  // to one per 16 fragments.
   constexpr int kXAhead = NQ < 6 ? NQ : 6, kCodeSlot = NQ >= 8 ? 4 : 1, kGatherSlot = NQ == 16 ? 8 : 0;
   constexpr int kGatherPerSlot = 8 / (NQ - kGatherSlot);
+  constexpr int UL = SPB > 2 ? 2 * SPB : 4;  // steps per unrolled block: whole stages and ring turns
   static_assert(kGatherPerSlot * (NQ - kGatherSlot) == 8, "all 8 codebook read pairs of the next step are issued");
   static_assert(kCodeSlot < NQ && kXAhead <= NQ, "slot numbers");
+  static_assert(UL % 4 == 0 && UL % (2 * SPB) == 0, "an unrolled block is whole ring turns and stage pairs");
   auto step = [&](auto U, int s) {
-    constexpr int u = decltype(U)::value, b = u & 1;
+    constexpr int u = decltype(U)::value, b = (u / SPB) & 1, j = u % SPB, ur = u & 3;
     const int s4 = min(s + 4, s_end - 1);
     const f16x8 a0 = dq_pack(g[0]), a1 = dq_pack(g[1]);
     uint32_t off[2][8];
-    window_offsets8(wr[(u + 1) & 3][0][0], wr[(u + 1) & 3][0][1], off[0]);
-    window_offsets8(wr[(u + 1) & 3][1][0], wr[(u + 1) & 3][1][1], off[1]);
+    window_offsets8(wr[(ur + 1) & 3][0][0], wr[(ur + 1) & 3][0][1], off[0]);
+    window_offsets8(wr[(ur + 1) & 3][1][0], wr[(ur + 1) & 3][1][1], off[1]);
     f16x8 xq[kXAhead + 1];
 #pragma unroll
-    for (int i = 0; i < kXAhead; ++i) xq[i] = xfrag(b, i);
+    for (int i = 0; i < kXAhead; ++i) xq[i] = xfrag(b, j, i);
 #pragma unroll
     for (int qt = 0; qt < NQ; ++qt) {
-      if (qt + kXAhead < NQ) xq[(qt + kXAhead) % (kXAhead + 1)] = xfrag(b, qt + kXAhead);
+      if (qt + kXAhead < NQ) xq[(qt + kXAhead) % (kXAhead + 1)] = xfrag(b, j, qt + kXAhead);
       acc[0][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, xq[qt % (kXAhead + 1)], acc[0][qt], 0, 0, 0);
       acc[1][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, xq[qt % (kXAhead + 1)], acc[1][qt], 0, 0, 0);
       if (qt >= kGatherSlot) {
 #pragma unroll
         for (int i = 0; i < kGatherPerSlot; ++i) {
-          const int j = (qt - kGatherSlot) * kGatherPerSlot + i;
-          g[0][j] = lds_cb(cb_lds, off[0][j]);
-          g[1][j] = lds_cb(cb_lds, off[1][j]);
+          const int jj = (qt - kGatherSlot) * kGatherPerSlot + i;
+          g[0][jj] = lds_cb(cb_lds, off[0][jj]);
+          g[1][jj] = lds_cb(cb_lds, off[1][jj]);
         }
       }
-      if (qt == kCodeSlot) load_codes(s4, wr[u]);
+      if (qt == kCodeSlot) load_codes(s4, wr[ur]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // every wave is done with x buffer b and its loads of stage s + 1 (issued
-    // before this step's kCodeLoads code-word loads) have landed; then stage
-    // s + 2 goes into buffer b
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCodeLoads) : "memory");
-    __syncthreads();
-    load_x(min(s + 2, s_end - 1), b);
+    if (j == SPB - 1) {
+      // every wave is done with x buffer b and its loads of the next stage
+      // (issued before this stage's SPB x kCodeLoads code-word loads) have
+      // landed; then the stage after next goes into buffer b
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SPB * kCodeLoads) : "memory");
+      __syncthreads();
+      load_x(min(s + 1 + SPB, s_end - SPB), b);
+    }
   };
-  using U0 = std::integral_constant<int, 0>;
-  using U1 = std::integral_constant<int, 1>;
-  using U2 = std::integral_constant<int, 2>;
-  using U3 = std::integral_constant<int, 3>;
-  // every k range is a whole number of 2-step blocks here (the plan cuts K
-  // in multiples of 4 16-k steps) but not always of 4
+  // every k range is a whole number of half blocks (UL / 2 steps: the plan
+  // cuts K in multiples of 2 SPB 16-k steps, and K / 32 is a multiple of 4)
+  auto block = [&](int s, auto... us) { (step(us, s + decltype(us)::value), ...); };
+  auto half_block = [&](int s) {
+    if constexpr (UL == 4)
+      block(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+    else
+      block(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{},
+            std::integral_constant<int, 3>{});
+  };
   int s = s_begin;
-  for (; s + 3 < s_end; s += 4) {
-    step(U0{}, s);
-    step(U1{}, s + 1);
-    step(U2{}, s + 2);
-    step(U3{}, s + 3);
+  for (; s + UL - 1 < s_end; s += UL) {
+    if constexpr (UL == 4)
+      block(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{},
+            std::integral_constant<int, 3>{});
+    else
+      block(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{},
+            std::integral_constant<int, 3>{}, std::integral_constant<int, 4>{}, std::integral_constant<int, 5>{},
+            std::integral_constant<int, 6>{}, std::integral_constant<int, 7>{});
   }
-  if (s < s_end) {
-    step(U0{}, s);
-    step(U1{}, s + 1);
-  }
+  if (s < s_end) half_block(s);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last (repeated) loads land before the LDS is reused
   __syncthreads();
 
