@@ -311,6 +311,8 @@ DqPlan plan_dq_rows(int32_t K, int32_t N, int64_t M, int nqb, bool whole, double
   p.tail = 0;
   p.tail_ks = 1;
   p.ksub_per_piece = ksub;
+  p.sk_steps = 0;
+  p.sk_wgs = 0;
   const int64_t fr = units / 256;
   for (int64_t nf = std::max<int64_t>(0, fr - 1); nf <= fr; ++nf) {
     const int64_t full = nf * 256, tail = units - full;
@@ -334,6 +336,34 @@ DqPlan plan_dq_rows(int32_t K, int32_t N, int64_t M, int nqb, bool whole, double
         p.tail = (int32_t)(ks_eff == 1 ? 0 : tail);
         p.tail_ks = ks_eff;
         p.ksub_per_piece = ks_eff == 1 ? ksub : per;
+        p.sk_steps = 0;
+        p.sk_wgs = 0;
+      }
+    }
+    // The eight-wave kernel's stream-K tail: the tail units' 32-k steps dealt
+    // evenly to up to 256 workgroups (runs of whole blocks, at most one unit
+    // long, so a run touches at most two units), one fp32 partial per unit
+    // a run touches. Equal pieces per unit leave CUs idle when the tail units
+    // times the pieces fall short of 256 (68 units x 3 pieces = 204).
+    if (eight_waves && !whole && tail > 0 && tail <= 256) {
+      const int ks32 = ksub / 2, al = align / 2;  // in 32-k steps
+      const int64_t total = tail * ks32;
+      const int per32 = (int)(((total + 255) / 256 + al - 1) / al * al);
+      if (per32 <= ks32) {
+        const int64_t wgs = (total + per32 - 1) / per32;
+        // a run that crosses into a second unit refills its pipeline there:
+        // one more fixed cost
+        const double t = rounds(full) * (ksub * step_us + wg_us) + (2 * per32 * step_us + 2 * wg_us) +
+                         (double)(wgs + tail) * R * 256 * 8.0 / 4e6;
+        if (t < best - 1e-9) {
+          best = t;
+          p.full = (int32_t)full;
+          p.tail = (int32_t)tail;
+          p.tail_ks = 1;
+          p.ksub_per_piece = 2 * per32;
+          p.sk_steps = per32;
+          p.sk_wgs = (int32_t)wgs;
+        }
       }
     }
   }

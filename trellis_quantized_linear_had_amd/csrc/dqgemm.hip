@@ -336,24 +336,8 @@ __global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   uint16_t* xs = lds + 65536;
 
   const int ks32 = K / 32;
-  int unit, s_begin, s_end;
-  if (!TAIL) {
-    unit = blockIdx.x;
-    s_begin = 0;
-    s_end = ks32;
-  } else {
-    const int t = blockIdx.x / plan.tail_ks, piece = blockIdx.x % plan.tail_ks;
-    unit = plan.full + t;
-    s_begin = piece * (plan.ksub_per_piece / 2);  // ksub_per_piece: 16-k steps, a multiple of 4
-    s_end = min(s_begin + plan.ksub_per_piece / 2, ks32);
-  }
-  const int pass = unit / plan.pblocks, pb = unit % plan.pblocks;
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int p0_raw = pb * DQ_COLS_WG + wave * 32;
-  const bool pvalid = p0_raw < N;          // N is a multiple of 128: valid waves come in groups of four
-  const int p0 = pvalid ? p0_raw : N - 32;  // idle waves re-read the last group, never store
 
   // Codebook into LDS straight from global memory (1 KiB per wave instruction).
   {
@@ -365,217 +349,257 @@ __global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
           (dq_lds_void*)(reinterpret_cast<char*>(cb_lds) + i * DQ2_THREADS * 16 + wave * 1024), 16, 0, 0);
   }
 
-  // Code words: lane (column c, k-tile kt, half h) reads words 2c + h and
-  // 2c + h + 1 (mod 32) of tile (2 s + kt, (p0 + 16 f) / 16).
-  const int c = lane & 15, kt = lane >> 5, h = (lane >> 4) & 1;
-  const int d = 2 * c + h;
-  const uint32_t row_bytes = (uint32_t)ldt * 128;  // one k-tile row of codes
-  uint32_t voff[2][2];
-#pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    const int nt = (p0 + 16 * f) / 16;
-    voff[f][0] = (uint32_t)(kt * row_bytes + nt * 128 + 4 * d);
-    voff[f][1] = (uint32_t)(kt * row_bytes + nt * 128 + 4 * ((d + 1) & 31));
+  // This workgroup's work: one segment (a unit and a range of its 32-k steps),
+  // or two when a stream-K run crosses from one tail unit into the next.
+  int unit0, b0, e0, unit1 = 0, e1 = 0, nseg = 1;
+  if (!TAIL) {
+    unit0 = blockIdx.x;
+    b0 = 0;
+    e0 = ks32;
+  } else if (plan.sk_steps == 0) {
+    const int t = blockIdx.x / plan.tail_ks, piece = blockIdx.x % plan.tail_ks;
+    unit0 = plan.full + t;
+    b0 = piece * (plan.ksub_per_piece / 2);  // ksub_per_piece: 16-k steps, whole x stages
+    e0 = min(b0 + plan.ksub_per_piece / 2, ks32);
+  } else {
+    // steps [g0, g1) of the tail units' 32-k steps, unit-major
+    const int64_t total = (int64_t)plan.tail * ks32;
+    const int64_t g0 = (int64_t)blockIdx.x * plan.sk_steps, g1 = min(g0 + plan.sk_steps, total);
+    const int t0 = (int)(g0 / ks32);
+    unit0 = plan.full + t0;
+    b0 = (int)(g0 - (int64_t)t0 * ks32);
+    e0 = (int)min((int64_t)ks32, b0 + (g1 - g0));
+    if (g0 + (e0 - b0) < g1) {  // sk_steps <= K / 32: the run ends in the next unit
+      unit1 = unit0 + 1;
+      e1 = (int)(g1 - g0 - (e0 - b0));
+      nseg = 2;
+    }
   }
-  const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((int64_t)K * ldt * 8));
-  constexpr int kCodeLoads = 4;  // VMEM loads per call of load_codes
-  auto load_codes = [&](int s, uint32_t (&w)[2][2]) {
+
+  for (int seg = 0; seg < nseg; ++seg) {  // uniform
+    const int unit = seg ? unit1 : unit0, s_begin = seg ? 0 : b0, s_end = seg ? e1 : e0;
+    const int pass = unit / plan.pblocks, pb = unit % plan.pblocks;
+    const int p0_raw = pb * DQ_COLS_WG + wave * 32;
+    const bool pvalid = p0_raw < N;          // N is a multiple of 128: valid waves come in groups of four
+    const int p0 = pvalid ? p0_raw : N - 32;  // idle waves re-read the last group, never store
+
+    // Code words: lane (column c, k-tile kt, half h) reads words 2c + h and
+    // 2c + h + 1 (mod 32) of tile (2 s + kt, (p0 + 16 f) / 16).
+    const int c = lane & 15, kt = lane >> 5, h = (lane >> 4) & 1;
+    const int d = 2 * c + h;
+    const uint32_t row_bytes = (uint32_t)ldt * 128;  // one k-tile row of codes
+    uint32_t voff[2][2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int nt = (p0 + 16 * f) / 16;
+      voff[f][0] = (uint32_t)(kt * row_bytes + nt * 128 + 4 * d);
+      voff[f][1] = (uint32_t)(kt * row_bytes + nt * 128 + 4 * ((d + 1) & 31));
+    }
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, (uint32_t)((int64_t)K * ldt * 8));
+    constexpr int kCodeLoads = 4;  // VMEM loads per call of load_codes
+    auto load_codes = [&](int s, uint32_t (&w)[2][2]) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) w[f][j] = buffer_load_u32(crs, voff[f][j], (uint32_t)(2 * s) * row_bytes);
+    };
+
+    // x stage: SPB consecutive 32-k steps of the pass's NQ row fragments (16
+    // rows x 32 k each), fragment f = j NQ + qt for step j of the stage and row
+    // fragment qt, clamped to the last fragment of the padded rows (rows past M
+    // are zero or repeats and are never stored); wave w loads fragments 2 w
+    // and 2 w + 1, which belong to one step. Buffer loads (a fixed lane
+    // offset, the step in the scalar offset): no 64-bit address registers to
+    // rebuild while code-word loads are in flight.
+    const int nq16 = (M + 31) / 32 * 2, q16_0 = pass * NQ;
+    const __amdgpu_buffer_rsrc_t xrs =
+        make_rsrc(xf + (int64_t)q16_0 * ks32 * 512, (uint32_t)(min(NQ, nq16 - q16_0) * ks32 * 1024));
+    const int xj = (2 * wave) / NQ;  // the step of the stage this wave's fragments belong to
+    uint32_t xoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      xoff[i] = (uint32_t)((min(q16_0 + (2 * wave + i) % NQ, nq16 - 1) - q16_0) * ks32 * 1024 + 16 * lane);
+    auto load_x = [&](int s0, int buf) {  // the stage of steps s0 .. s0 + SPB - 1
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dq_buffer_load_lds16(xrs, (dq_lds_void*)(xs + buf * XSTAGE + (2 * wave + i) * 512), xoff[i],
+                             (uint32_t)(s0 + xj) * 1024);
+    };
+    auto xfrag = [&](int buf, int j, int qt) {
+      return *reinterpret_cast<const f16x8*>(xs + buf * XSTAGE + (j * NQ + qt) * 512 + 8 * lane);
+    };
+
+    f32x4 acc[2][NQ];
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) w[f][j] = buffer_load_u32(crs, voff[f][j], (uint32_t)(2 * s) * row_bytes);
-  };
+      for (int qt = 0; qt < NQ; ++qt) acc[f][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // x stage: SPB consecutive 32-k steps of the pass's NQ row fragments (16
-  // rows x 32 k each), fragment f = j NQ + qt for step j of the stage and row
-  // fragment qt, clamped to the last fragment of the padded rows (rows past M
-  // are zero or repeats and are never stored); wave w loads fragments 2 w
-  // and 2 w + 1, which belong to one step. Buffer loads (a fixed lane
-  // offset, the step in the scalar offset): no 64-bit address registers to
-  // rebuild while code-word loads are in flight.
-  const int nq16 = (M + 31) / 32 * 2, q16_0 = pass * NQ;
-  const __amdgpu_buffer_rsrc_t xrs =
-      make_rsrc(xf + (int64_t)q16_0 * ks32 * 512, (uint32_t)(min(NQ, nq16 - q16_0) * ks32 * 1024));
-  const int xj = (2 * wave) / NQ;  // the step of the stage this wave's fragments belong to
-  uint32_t xoff[2];
+    // Rings: code words of steps s .. s + 3; the codebook reads of step s + 1
+    // are issued during step s.
+    uint32_t wr[4][2][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    xoff[i] = (uint32_t)((min(q16_0 + (2 * wave + i) % NQ, nq16 - 1) - q16_0) * ks32 * 1024 + 16 * lane);
-  auto load_x = [&](int s0, int buf) {  // the stage of steps s0 .. s0 + SPB - 1
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dq_buffer_load_lds16(xrs, (dq_lds_void*)(xs + buf * XSTAGE + (2 * wave + i) * 512), xoff[i],
-                           (uint32_t)(s0 + xj) * 1024);
-  };
-  auto xfrag = [&](int buf, int j, int qt) {
-    return *reinterpret_cast<const f16x8*>(xs + buf * XSTAGE + (j * NQ + qt) * 512 + 8 * lane);
-  };
+    for (int u = 0; u < 4; ++u) load_codes(min(s_begin + u, s_end - 1), wr[u]);
+    load_x(s_begin, 0);
+    load_x(min(s_begin + SPB, s_end - SPB), 1);
+    __builtin_amdgcn_s_waitcnt(0);  // the codebook, the first code words and both x stages have landed
+    __syncthreads();
+    uint32_t g[2][8];
+    dq_gather(cb_lds, wr[0][0], g[0]);
+    dq_gather(cb_lds, wr[0][1], g[1]);
 
-  f32x4 acc[2][NQ];
+    // Step s, phase u = (s - s_begin) % UL: code-word ring slot u % 4, x
+    // buffer (u / SPB) % 2, step u % SPB of its stage. NQ slots, each the 2
+    // MFMAs of one row fragment plus one piece of the next step's work in
+    // source order fenced by scheduling barriers: the x fragment kXAhead slots
+    // ahead, (slot kCodeSlot) the code words of s + 4, and (slots
+    // kGatherSlot..NQ - 1, evenly) the 8 codebook read pairs of s + 1. After
+    // the last step of a stage, one barrier and the loads of the stage after
+    // next. Measured at M = 256..2048 on both MLP geometries with 16
+    // fragments: fragments 6 ahead and the reads in the second half beat 2
+    // ahead and the first half by 2-4 %; staggering the halves between the two
+    // waves of a SIMD, or one read pair per slot, did not help. Stages of
+    // several steps keep the barriers of the short passes (4 and 8 fragments)
+    // to one per 16 fragments.
+    constexpr int kXAhead = NQ < 6 ? NQ : 6, kCodeSlot = NQ >= 8 ? 4 : 1, kGatherSlot = NQ == 16 ? 8 : 0;
+    constexpr int kGatherPerSlot = 8 / (NQ - kGatherSlot);
+    constexpr int UL = SPB > 2 ? 2 * SPB : 4;  // steps per unrolled block: whole stages and ring turns
+    static_assert(kGatherPerSlot * (NQ - kGatherSlot) == 8, "all 8 codebook read pairs of the next step are issued");
+    static_assert(kCodeSlot < NQ && kXAhead <= NQ, "slot numbers");
+    static_assert(UL % 4 == 0 && UL % (2 * SPB) == 0, "an unrolled block is whole ring turns and stage pairs");
+    auto step = [&](auto U, int s) {
+      constexpr int u = decltype(U)::value, b = (u / SPB) & 1, j = u % SPB, ur = u & 3;
+      const int s4 = min(s + 4, s_end - 1);
+      const f16x8 a0 = dq_pack(g[0]), a1 = dq_pack(g[1]);
+      uint32_t off[2][8];
+      window_offsets8(wr[(ur + 1) & 3][0][0], wr[(ur + 1) & 3][0][1], off[0]);
+      window_offsets8(wr[(ur + 1) & 3][1][0], wr[(ur + 1) & 3][1][1], off[1]);
+      f16x8 xq[kXAhead + 1];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+      for (int i = 0; i < kXAhead; ++i) xq[i] = xfrag(b, j, i);
 #pragma unroll
-    for (int qt = 0; qt < NQ; ++qt) acc[f][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int qt = 0; qt < NQ; ++qt) {
+        if (qt + kXAhead < NQ) xq[(qt + kXAhead) % (kXAhead + 1)] = xfrag(b, j, qt + kXAhead);
+        acc[0][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, xq[qt % (kXAhead + 1)], acc[0][qt], 0, 0, 0);
+        acc[1][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, xq[qt % (kXAhead + 1)], acc[1][qt], 0, 0, 0);
+        if (qt >= kGatherSlot) {
+#pragma unroll
+          for (int i = 0; i < kGatherPerSlot; ++i) {
+            const int jj = (qt - kGatherSlot) * kGatherPerSlot + i;
+            g[0][jj] = lds_cb(cb_lds, off[0][jj]);
+            g[1][jj] = lds_cb(cb_lds, off[1][jj]);
+          }
+        }
+        if (qt == kCodeSlot) load_codes(s4, wr[ur]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j == SPB - 1) {
+        // every wave is done with x buffer b and its loads of the next stage
+        // (issued before this stage's SPB x kCodeLoads code-word loads) have
+        // landed; then the stage after next goes into buffer b
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SPB * kCodeLoads) : "memory");
+        __syncthreads();
+        load_x(min(s + 1 + SPB, s_end - SPB), b);
+      }
+    };
+    // every k range is a whole number of half blocks (UL / 2 steps: the plan
+    // cuts K in multiples of 2 SPB 16-k steps, and K / 32 is a multiple of 4)
+    auto block = [&](int s, auto... us) { (step(us, s + decltype(us)::value), ...); };
+    auto half_block = [&](int s) {
+      if constexpr (UL == 4)
+        block(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+      else
+        block(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{},
+              std::integral_constant<int, 3>{});
+    };
+    int s = s_begin;
+    for (; s + UL - 1 < s_end; s += UL) {
+      if constexpr (UL == 4)
+        block(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{},
+              std::integral_constant<int, 3>{});
+      else
+        block(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{},
+              std::integral_constant<int, 3>{}, std::integral_constant<int, 4>{}, std::integral_constant<int, 5>{},
+              std::integral_constant<int, 6>{}, std::integral_constant<int, 7>{});
+    }
+    if (s < s_end) half_block(s);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last (repeated) loads land before the LDS is reused
+    __syncthreads();
 
-  // Rings: code words of steps s .. s + 3; the codebook reads of step s + 1
-  // are issued during step s.
-  uint32_t wr[4][2][2];
+    // Lane holds D[p = p0 + 16 f + 4 (lane >> 4) + r][q = 16 qt + (lane & 15)].
+    const int pl = 4 * (lane >> 4), ql = lane & 15;
+    if (TAIL) {
+      // partials[slot][q][p] over the unit's R rows and 256 columns; slot: the
+      // workgroup, or (stream-K) workgroup + tail unit, distinct for every
+      // (run, unit) pair since consecutive runs move on by at least one in
+      // one of the two
+      if (pvalid) {
+        const int slot = (int)blockIdx.x + (plan.sk_steps ? unit - plan.full : 0);
+        float* base = partials + (int64_t)slot * R * DQ_COLS_WG + wave * 32 + pl;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) load_codes(min(s_begin + u, s_end - 1), wr[u]);
-  load_x(s_begin, 0);
-  load_x(min(s_begin + SPB, s_end - SPB), 1);
-  __builtin_amdgcn_s_waitcnt(0);  // the codebook, the first code words and both x stages have landed
-  __syncthreads();
-  uint32_t g[2][8];
-  dq_gather(cb_lds, wr[0][0], g[0]);
-  dq_gather(cb_lds, wr[0][1], g[1]);
+        for (int qt = 0; qt < NQ; ++qt)
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+            *reinterpret_cast<f32x4*>(base + (16 * qt + ql) * DQ_COLS_WG + 16 * f) = acc[f][qt];
+      }
+      continue;
+    }
 
-  // Step s, phase u = (s - s_begin) % UL: code-word ring slot u % 4, x
-  // buffer (u / SPB) % 2, step u % SPB of its stage. NQ slots, each the 2
-  // MFMAs of one row fragment plus one piece of the next step's work in
-  // source order fenced by scheduling barriers: the x fragment kXAhead slots
-  // ahead, (slot kCodeSlot) the code words of s + 4, and (slots
-  // kGatherSlot..NQ - 1, evenly) the 8 codebook read pairs of s + 1. After
-  // the last step of a stage, one barrier and the loads of the stage after
-  // next. Measured at M = 256..2048 on both MLP geometries with 16
-  // fragments: fragments 6 ahead and the reads in the second half beat 2
-  // ahead and the first half by 2-4 %; staggering the halves between the two
-  // waves of a SIMD, or one read pair per slot, did not help. Stages of
-  // several steps keep the barriers of the short passes (4 and 8 fragments)
-  // to one per 16 fragments.
-  constexpr int kXAhead = NQ < 6 ? NQ : 6, kCodeSlot = NQ >= 8 ? 4 : 1, kGatherSlot = NQ == 16 ? 8 : 0;
-  constexpr int kGatherPerSlot = 8 / (NQ - kGatherSlot);
-  constexpr int UL = SPB > 2 ? 2 * SPB : 4;  // steps per unrolled block: whole stages and ring turns
-  static_assert(kGatherPerSlot * (NQ - kGatherSlot) == 8, "all 8 codebook read pairs of the next step are issued");
-  static_assert(kCodeSlot < NQ && kXAhead <= NQ, "slot numbers");
-  static_assert(UL % 4 == 0 && UL % (2 * SPB) == 0, "an unrolled block is whole ring turns and stage pairs");
-  auto step = [&](auto U, int s) {
-    constexpr int u = decltype(U)::value, b = (u / SPB) & 1, j = u % SPB, ur = u & 3;
-    const int s4 = min(s + 4, s_end - 1);
-    const f16x8 a0 = dq_pack(g[0]), a1 = dq_pack(g[1]);
-    uint32_t off[2][8];
-    window_offsets8(wr[(ur + 1) & 3][0][0], wr[(ur + 1) & 3][0][1], off[0]);
-    window_offsets8(wr[(ur + 1) & 3][1][0], wr[(ur + 1) & 3][1][1], off[1]);
-    f16x8 xq[kXAhead + 1];
+    // A whole unit: column scales into the accumulators, then rounds of RR
+    // rows through the LDS (fp32 [row][256 columns], up to 128 KiB, where the
+    // codebook was): 16 lanes per (row, 128-column block) read 8 consecutive
+    // columns, rotate (the arithmetic of the decode path's output stage),
+    // apply the signs and store fp16 y.
+    constexpr int RR = R < 128 ? R : 128, QR = RR / 16;
 #pragma unroll
-    for (int i = 0; i < kXAhead; ++i) xq[i] = xfrag(b, j, i);
+    for (int f = 0; f < 2; ++f) {
+      const u32x2 sc = *reinterpret_cast<const u32x2*>(scale + p0 + 16 * f + pl);
+      const float s0 = bits_lo_f16(sc[0]), s1 = bits_hi_f16(sc[0]), s2 = bits_lo_f16(sc[1]), s3 = bits_hi_f16(sc[1]);
 #pragma unroll
-    for (int qt = 0; qt < NQ; ++qt) {
-      if (qt + kXAhead < NQ) xq[(qt + kXAhead) % (kXAhead + 1)] = xfrag(b, j, qt + kXAhead);
-      acc[0][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, xq[qt % (kXAhead + 1)], acc[0][qt], 0, 0, 0);
-      acc[1][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, xq[qt % (kXAhead + 1)], acc[1][qt], 0, 0, 0);
-      if (qt >= kGatherSlot) {
+      for (int qt = 0; qt < NQ; ++qt) {
+        acc[f][qt][0] *= s0;
+        acc[f][qt][1] *= s1;
+        acc[f][qt][2] *= s2;
+        acc[f][qt][3] *= s3;
+      }
+    }
+    float* tb = reinterpret_cast<float*>(lds);
+    const uint32_t smask = sign_n ? 0x80008000u : 0u;
 #pragma unroll
-        for (int i = 0; i < kGatherPerSlot; ++i) {
-          const int jj = (qt - kGatherSlot) * kGatherPerSlot + i;
-          g[0][jj] = lds_cb(cb_lds, off[0][jj]);
-          g[1][jj] = lds_cb(cb_lds, off[1][jj]);
+    for (int rnd = 0; rnd < R / RR; ++rnd) {
+      if (pvalid)
+#pragma unroll
+        for (int qt = 0; qt < QR; ++qt)
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+            *reinterpret_cast<f32x4*>(tb + (16 * qt + ql) * DQ_COLS_WG + wave * 32 + 16 * f + pl) =
+                acc[f][QR * rnd + qt];
+      __syncthreads();
+      // RR rows x 2 blocks x 16 lanes = 32 RR lane tasks, RR / 16 per thread
+      const int q16 = threadIdx.x & 15;
+#pragma unroll
+      for (int i = 0; i < RR / 16; ++i) {
+        const int item = (threadIdx.x >> 4) + 32 * i;  // (row, block)
+        const int r = item >> 1, blk = item & 1;
+        const int row = pass * R + RR * rnd + r;
+        const int col0 = pb * DQ_COLS_WG + 128 * blk;
+        const f32x4* src = reinterpret_cast<const f32x4*>(tb + r * DQ_COLS_WG + 128 * blk + 8 * q16);
+        const f32x4 v0 = src[0], v1 = src[1];
+        float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        wht128_16(v, q16);
+        if (row < M && col0 < N) {  // uniform over the 16 lanes
+          const int col = col0 + 8 * q16;
+          const u32x4 sg = *reinterpret_cast<const u32x4*>((sign_n ? sign_n : scale) + col);
+          u32x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * EXL3_INV_SQRT128, v[2 * j + 1] * EXL3_INV_SQRT128);
+          o ^= sg & smask;
+          *reinterpret_cast<u32x4*>(y + (int64_t)row * ldy + col) = o;
         }
       }
-      if (qt == kCodeSlot) load_codes(s4, wr[ur]);
-      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();  // the buffer is rewritten in the next round
     }
-    if (j == SPB - 1) {
-      // every wave is done with x buffer b and its loads of the next stage
-      // (issued before this stage's SPB x kCodeLoads code-word loads) have
-      // landed; then the stage after next goes into buffer b
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SPB * kCodeLoads) : "memory");
-      __syncthreads();
-      load_x(min(s + 1 + SPB, s_end - SPB), b);
-    }
-  };
-  // every k range is a whole number of half blocks (UL / 2 steps: the plan
-  // cuts K in multiples of 2 SPB 16-k steps, and K / 32 is a multiple of 4)
-  auto block = [&](int s, auto... us) { (step(us, s + decltype(us)::value), ...); };
-  auto half_block = [&](int s) {
-    if constexpr (UL == 4)
-      block(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-    else
-      block(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{},
-            std::integral_constant<int, 3>{});
-  };
-  int s = s_begin;
-  for (; s + UL - 1 < s_end; s += UL) {
-    if constexpr (UL == 4)
-      block(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{},
-            std::integral_constant<int, 3>{});
-    else
-      block(s, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{},
-            std::integral_constant<int, 3>{}, std::integral_constant<int, 4>{}, std::integral_constant<int, 5>{},
-            std::integral_constant<int, 6>{}, std::integral_constant<int, 7>{});
-  }
-  if (s < s_end) half_block(s);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last (repeated) loads land before the LDS is reused
-  __syncthreads();
-
-  // Lane holds D[p = p0 + 16 f + 4 (lane >> 4) + r][q = 16 qt + (lane & 15)].
-  const int pl = 4 * (lane >> 4), ql = lane & 15;
-  if (TAIL) {
-    // partials[w][q][p] over the unit's R rows and 256 columns
-    if (!pvalid) return;
-    float* base = partials + (int64_t)blockIdx.x * R * DQ_COLS_WG + wave * 32 + pl;
-#pragma unroll
-    for (int qt = 0; qt < NQ; ++qt)
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-        *reinterpret_cast<f32x4*>(base + (16 * qt + ql) * DQ_COLS_WG + 16 * f) = acc[f][qt];
-    return;
-  }
-
-  // A whole unit: column scales into the accumulators, then rounds of RR
-  // rows through the LDS (fp32 [row][256 columns], up to 128 KiB, where the
-  // codebook was): 16 lanes per (row, 128-column block) read 8 consecutive
-  // columns, rotate (the arithmetic of the decode path's output stage),
-  // apply the signs and store fp16 y.
-  constexpr int RR = R < 128 ? R : 128, QR = RR / 16;
-#pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    const u32x2 sc = *reinterpret_cast<const u32x2*>(scale + p0 + 16 * f + pl);
-    const float s0 = bits_lo_f16(sc[0]), s1 = bits_hi_f16(sc[0]), s2 = bits_lo_f16(sc[1]), s3 = bits_hi_f16(sc[1]);
-#pragma unroll
-    for (int qt = 0; qt < NQ; ++qt) {
-      acc[f][qt][0] *= s0;
-      acc[f][qt][1] *= s1;
-      acc[f][qt][2] *= s2;
-      acc[f][qt][3] *= s3;
-    }
-  }
-  float* tb = reinterpret_cast<float*>(lds);
-  const uint32_t smask = sign_n ? 0x80008000u : 0u;
-#pragma unroll
-  for (int rnd = 0; rnd < R / RR; ++rnd) {
-    if (pvalid)
-#pragma unroll
-      for (int qt = 0; qt < QR; ++qt)
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-          *reinterpret_cast<f32x4*>(tb + (16 * qt + ql) * DQ_COLS_WG + wave * 32 + 16 * f + pl) =
-              acc[f][QR * rnd + qt];
-    __syncthreads();
-    // RR rows x 2 blocks x 16 lanes = 32 RR lane tasks, RR / 16 per thread
-    const int q16 = threadIdx.x & 15;
-#pragma unroll
-    for (int i = 0; i < RR / 16; ++i) {
-      const int item = (threadIdx.x >> 4) + 32 * i;  // (row, block)
-      const int r = item >> 1, blk = item & 1;
-      const int row = pass * R + RR * rnd + r;
-      const int col0 = pb * DQ_COLS_WG + 128 * blk;
-      const f32x4* src = reinterpret_cast<const f32x4*>(tb + r * DQ_COLS_WG + 128 * blk + 8 * q16);
-      const f32x4 v0 = src[0], v1 = src[1];
-      float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      wht128_16(v, q16);
-      if (row < M && col0 < N) {  // uniform over the 16 lanes
-        const int col = col0 + 8 * q16;
-        const u32x4 sg = *reinterpret_cast<const u32x4*>((sign_n ? sign_n : scale) + col);
-        u32x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = pack_f16x2(v[2 * j] * EXL3_INV_SQRT128, v[2 * j + 1] * EXL3_INV_SQRT128);
-        o ^= sg & smask;
-        *reinterpret_cast<u32x4*>(y + (int64_t)row * ldy + col) = o;
-      }
-    }
-    __syncthreads();  // the buffer is rewritten in the next round
-  }
+  }  // segments
 }
 
 // Sums the tail pieces of one unit in k order, applies the column scales,
@@ -585,7 +609,7 @@ __global__ __launch_bounds__(DQ2_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
 __global__ __launch_bounds__(256) void dq_fixup_kernel(const float* __restrict__ partials, int32_t R, DqPlan plan,
                                                        const uint16_t* __restrict__ scale,
                                                        const uint16_t* __restrict__ sign_n, uint16_t* __restrict__ y,
-                                                       int64_t ldy, int32_t M, int32_t N) {
+                                                       int64_t ldy, int32_t M, int32_t N, int32_t K) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int q = (int)(gid & 15);
   const int64_t item = gid >> 4;  // (tail unit, row, block)
@@ -600,11 +624,21 @@ __global__ __launch_bounds__(256) void dq_fixup_kernel(const float* __restrict__
   const u32x4 sc = *reinterpret_cast<const u32x4*>(scale + col);
   const u32x4 sg = *reinterpret_cast<const u32x4*>((sign_n ? sign_n : scale) + col);
   const uint32_t smask = sign_n ? 0x80008000u : 0u;
-  const f32x4* src = reinterpret_cast<const f32x4*>(partials + ((int64_t)t * plan.tail_ks * R + r) * DQ_COLS_WG +
-                                                    128 * b + 8 * q);
-  const int64_t piece = (int64_t)R * DQ_COLS_WG / 4;  // f32x4 per piece
+  // the unit's pieces in k order: slots t tail_ks .. + tail_ks - 1, or
+  // (stream-K) the runs v that overlap the unit's steps [t ks32, (t + 1)
+  // ks32), slot v + t
+  const int64_t piece = (int64_t)R * DQ_COLS_WG / 4;  // f32x4 per slot
+  const f32x4* src0 = reinterpret_cast<const f32x4*>(partials + (int64_t)r * DQ_COLS_WG + 128 * b + 8 * q);
+  const int ks32 = K / 32;
+  int v_lo = t * plan.tail_ks, v_hi = v_lo + plan.tail_ks - 1;
+  if (plan.sk_steps) {
+    v_lo = (int)((int64_t)t * ks32 / plan.sk_steps);
+    v_hi = (int)(((int64_t)(t + 1) * ks32 - 1) / plan.sk_steps);
+  }
+  auto slot = [&](int v) { return plan.sk_steps ? v + t : v; };
   float v[8];
   {
+    const f32x4* src = src0 + slot(v_lo) * piece;
     const f32x4 p0 = src[0], p1 = src[1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -612,8 +646,9 @@ __global__ __launch_bounds__(256) void dq_fixup_kernel(const float* __restrict__
       v[4 + j] = p1[j];
     }
   }
-  for (int k = 1; k < plan.tail_ks; ++k) {
-    const f32x4 p0 = src[k * piece], p1 = src[k * piece + 1];
+  for (int w = v_lo + 1; w <= v_hi; ++w) {
+    const f32x4* src = src0 + slot(w) * piece;
+    const f32x4 p0 = src[0], p1 = src[1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v[j] += p0[j];
@@ -655,7 +690,7 @@ hipError_t launch_dqgemm2(const uint16_t* xf16, const uint32_t* codes, const uin
       EXL3_DQ2_LAUNCH(16, tail, grid);     \
   }
   if (plan.full > 0) EXL3_DQ2_LAUNCH_NQ(false, plan.full)
-  if (plan.tail > 0) EXL3_DQ2_LAUNCH_NQ(true, plan.tail * plan.tail_ks)
+  if (plan.tail > 0) EXL3_DQ2_LAUNCH_NQ(true, plan.sk_steps ? plan.sk_wgs : plan.tail * plan.tail_ks)
 #undef EXL3_DQ2_LAUNCH_NQ
 #undef EXL3_DQ2_LAUNCH
   hipError_t e = hipGetLastError();
@@ -663,12 +698,13 @@ hipError_t launch_dqgemm2(const uint16_t* xf16, const uint32_t* codes, const uin
   const int R = 32 * plan.nqb;
   const int64_t threads = (int64_t)plan.tail * R * 2 * 16;
   dq_fixup_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(partials, R, plan, scale, sign_n, y, ldy, M,
-                                                                          N);
+                                                                          N, K);
   return hipGetLastError();
 }
 
 size_t dq_partial_bytes(const DqPlan& plan) {
-  return (size_t)plan.tail * plan.tail_ks * 32 * plan.nqb * DQ_COLS_WG * sizeof(float);
+  const size_t slots = plan.sk_steps ? (size_t)plan.sk_wgs + plan.tail - 1 : (size_t)plan.tail * plan.tail_ks;
+  return slots * 32 * plan.nqb * DQ_COLS_WG * sizeof(float);
 }
 
 hipError_t launch_dqgemm(const uint16_t* xf, const uint32_t* codes, const uint16_t* cb, const uint16_t* scale,
@@ -697,7 +733,7 @@ hipError_t launch_dqgemm(const uint16_t* xf, const uint32_t* codes, const uint16
   const int R = 32 * plan.nqb;
   const int64_t threads = (int64_t)plan.tail * R * 2 * 16;
   dq_fixup_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(partials, R, plan, scale, sign_n, y, ldy, M,
-                                                                          N);
+                                                                          N, K);
   return hipGetLastError();
 }
 
