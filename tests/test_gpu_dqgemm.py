@@ -90,8 +90,11 @@ def test_dqgemm_states_bit_exact(T, X, M, whole, eight):
 
 
 @pytest.mark.parametrize("eight", [False, True])
-@pytest.mark.parametrize("M", [64, 256, 1024, 2048])
+@pytest.mark.parametrize("M", [64, 256, 384, 512, 1024, 2048])
 def test_dqgemm_full_geometry_sampled(T, X, M, eight):
+    """K5120 x N17408 on sampled rows (every 256-row pass). At M = 384 and 512
+    the eight-wave kernel's 136 units of 256 rows take the stream-K tail
+    (runs crossing unit boundaries, one partial per unit a run touches)."""
     from tests.test_gpu_configs import sample_rows
 
     K, N = 5120, 17408
