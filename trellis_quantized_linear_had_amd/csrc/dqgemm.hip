@@ -305,11 +305,12 @@ __global__ __launch_bounds__(DQ_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
 // ---- Eight-wave form: 32 columns per wave (two 16-column A fragments of
 // v_mfma_f32_16x16x32_f16), one pass of R = 16 NQ rows (NQ = 4, 8 or 16 row
 // fragments), the pass's rows of Xr staged once per workgroup in the LDS
-// beside the codebook (16-row fragment order, NQ KiB per 32-k step, two
-// stages), so each wave reads them from LDS instead of loading them itself,
-// and two waves per SIMD hide each other's waits. A lane of A fragment f
-// holds 8 consecutive k of column p: k-tile (lane >> 5) of the step, half
-// (lane >> 4) & 1 of that tile's 16 steps.
+// beside the codebook (16-row fragment order, two stages of 16 fragments:
+// one, two or four 32-k steps each), so each wave reads them from LDS
+// instead of loading them itself, and two waves per SIMD hide each other's
+// waits. A lane of A fragment f holds 8 consecutive k of column p: k-tile
+// (lane >> 5) of the step, half (lane >> 4) & 1 of that tile's 16 steps. The
+// tail is split into equal pieces per unit or dealt stream-K (DqPlan).
 #define DQ2_THREADS 512
 
 // One direct-to-LDS buffer load of 16 bytes per lane (lane i's bytes land at
