@@ -390,7 +390,7 @@ PMC_KERNELS = {
     "gemm_tail": ("exl3::gemm_had_kernel<1>", "gemm_had_kernel<1> K17408xN5120 M=2048", ("gemm_f16.hip", "common.h")),
     # the eight-wave dequant-GEMM at M = 256 (the dispatch's choice there): 68 units of 256 rows x 256
     # columns, each split in three k pieces
-    "dq": ("exl3::dqgemm2_kernel<true>", "dqgemm2_kernel<true> K5120xN17408 M=256",
+    "dq": ("exl3::dqgemm2_kernel<16, true>", "dqgemm2_kernel<16,true> K5120xN17408 M=256",
            ("dqgemm.hip", "dq_plan.h", "epilogue.h", "trellis.h", "common.h")),
 }
 
