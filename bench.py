@@ -37,10 +37,10 @@ RECON_BYTES = K * N // 2 + K * N * 2 + N * 2
 HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 # Secondary roof of the trellis kernels: one random 16-bit codebook read from
-# LDS per weight. The gather probe's rate per CU per clock (measured in every
-# run; 11.66 on the last boxes) times 256 CUs at the 2.4 GHz peak clock gives
-# the weights per second, and 0.5 byte of packed 4-bit codes per weight the
-# GB/s (3.58 TB/s at 11.66).
+# LDS per weight. The gather probe's rate per CU per clock for addresses
+# independent across lanes (measured in every run; 9.06 on the last boxes)
+# times 256 CUs at the 2.4 GHz peak clock gives the weights per second, and
+# 0.5 byte of packed 4-bit codes per weight the GB/s (2.78 TB/s at 9.06).
 PEAK_CLOCK_HZ = 2.4e9
 
 

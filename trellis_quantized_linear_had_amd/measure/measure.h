@@ -66,7 +66,9 @@ int exl3m_logits_marked(const uint16_t *x, int64_t M, int32_t K, const uint16_t 
 /* Probes. Each launches EXL3M_PROBE_WORKGROUPS workgroups on `stream` and
  * returns at once.
  *   exl3m_probe_lds_gather: every lane issues `iters` x 16 random 16-bit reads
- *     from a 128 KiB LDS table (the codebook gathers of the trellis kernels);
+ *     from a 128 KiB LDS table at addresses independent across lanes (the
+ *     codebook gathers of the trellis kernels, whose states come from a
+ *     random bitstream);
  *   exl3m_probe_mfma: 8 waves per workgroup each issue `iters` x 8 independent
  *     v_mfma_f32_32x32x16_f16 (32768 FLOP each);
  *   exl3m_probe_stream: write = 0 reads `bytes` of src in 16-byte accesses,

@@ -12,24 +12,40 @@ namespace exl3 {
 
 #define PROBE_CUS 256
 
-// Random u16 gathers: each lane walks its own linear congruential sequence
-// (Numerical Recipes constants) and reads tab[state >> 16]; 16 reads are
-// issued before their sum is formed, as in the decode kernel.
+// Random u16 gathers: every lane reads 16 entries at independent uniform
+// addresses (a murmur3-style finalizer of its thread index and the read
+// number), issued before their sum is formed, as in the decode kernel. Each
+// iteration XORs every address with one constant, which permutes the banks
+// alike for all lanes (a read instruction keeps its bank-conflict pattern)
+// and keeps the reads inside the loop. (Per-lane linear congruential
+// sequences started at an arithmetic progression of seeds, as an earlier
+// version used, stay an arithmetic progression across the lanes of one
+// instruction: evenly spaced addresses with few bank conflicts, 11.66 reads
+// per CU per clock against 9.06 for independent random ones.)
 __global__ __launch_bounds__(1024) void probe_lds_gather_kernel(int64_t iters, uint32_t* __restrict__ sink,
                                                                 uint64_t* __restrict__ clocks) {
   __shared__ uint16_t tab[65536];
   for (int i = threadIdx.x; i < 65536; i += 1024) tab[i] = (uint16_t)(i * 40503u);
   __syncthreads();
+  uint32_t a[16];  // byte offsets of 16-bit entries
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    uint32_t h = (blockIdx.x * 1024u + threadIdx.x) * 16u + (uint32_t)j + 0x9E3779B9u;
+    h ^= h >> 16;
+    h *= 0x85EBCA6Bu;
+    h ^= h >> 13;
+    h *= 0xC2B2AE35u;
+    h ^= h >> 16;
+    a[j] = (h >> 16) << 1;
+  }
   const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
-  uint32_t s = (blockIdx.x * 1024u + threadIdx.x) * 2654435761u + 12345u;
   uint32_t acc = 0;
   for (int64_t it = 0; it < iters; ++it) {
+    const uint32_t c = ((uint32_t)it * 40503u & 0xFFFFu) << 1;  // even, below 2^17: stays inside the table
     uint32_t g[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      s = s * 1664525u + 1013904223u;
-      g[j] = tab[s >> 16];
-    }
+    for (int j = 0; j < 16; ++j)
+      g[j] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(tab) + (a[j] ^ c));
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc += g[j];
   }
