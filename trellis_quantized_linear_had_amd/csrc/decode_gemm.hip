@@ -28,10 +28,11 @@ namespace exl3 {
 
 // Code words per tile and lane: a lane's 8 windows (steps 16c + 8h .. + 7)
 // span BITS * 7 + 16 bits from bit BITS (16c + 8h) of the tile; at 4 bits
-// that is words d = 2c + h and d + 1 (mod 32).
+// that is words d = 2c + h and d + 1 (mod 32), and the lane loads only word
+// d: word d + 1 is the one another lane loaded (next_tile_word).
 template <int BITS>
 struct DecWidth {
-  static constexpr int kWords = BITS == 4 ? 2 : TrellisWidth<BITS>::words(8, 8);
+  static constexpr int kWords = BITS == 4 ? 1 : TrellisWidth<BITS>::words(8, 8);
 };
 
 // Loads the code words of NT tiles of one k-step, NW per lane. The tile
@@ -81,7 +82,7 @@ __device__ __forceinline__ void gather_tile(const uint16_t* cb_lds, const uint32
                                             uint32_t (&g)[8]) {
   uint32_t off[8];
   if constexpr (BITS == 4)
-    window_offsets8(w[0], w[1], off);
+    window_offsets8(w[0], next_tile_word(w[0]), off);  // word d + 1 from its lane
   else
     window_offsets_any<BITS, 8, NW>(w, woff, off);
 #pragma unroll

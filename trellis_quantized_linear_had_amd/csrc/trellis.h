@@ -43,6 +43,18 @@ __device__ __forceinline__ void window_offsets8(uint32_t lo, uint32_t hi, uint32
   off[7] = twice_hi16(a3, one);
 }
 
+// At 4 bits a 32-k MFMA step's B-fragment lanes hold word 2 i + (r & 1) of
+// their k-tile's 32 code words in lane 16 r + i (rows r = 0, 1 of the first
+// k-tile, 2, 3 of the second). The word after a lane's own sits in the same
+// lane of the paired row (rows 0, 2) or one lane further in it, lane 15
+// wrapping to word 0 (rows 1, 3): one row swap and one in-row rotation, with
+// every lane active.
+__device__ __forceinline__ uint32_t next_tile_word(uint32_t w) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  // rows 1, 3 take sw[0] rotated one lane down (row_ror:15); rows 0, 2 keep sw[1]
+  return __builtin_amdgcn_update_dpp(sw[1], sw[0], 0x12F, 0xA, 0xF, false);
+}
+
 __device__ __forceinline__ void window_states8(uint32_t lo, uint32_t hi, uint32_t (&s)[8]) {
   const uint32_t a1 = __builtin_amdgcn_alignbit(hi, lo, 4);
   const uint32_t a2 = __builtin_amdgcn_alignbit(hi, lo, 8);
