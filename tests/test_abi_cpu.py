@@ -275,30 +275,34 @@ def test_missing_library_fails_loudly():
 
 @pytest.mark.parametrize("K,N,M", [
     (17408, 5120, 2048),  # 160 tiles, pieces of 170 k-steps straddling tiles of 272
-    (5120, 17408, 2048),  # 32 tail tiles, 8 pieces per tile
+    (5120, 17408, 2048),  # 32 tail tiles as 64 halves, 4 pieces of 20 k-steps per half
     (2560, 3328, 200),    # 13 tiles, pieces of 3 k-steps over 40
     (1024, 4608, 300),    # 36 tiles, pieces of 3 k-steps over 16
-    (5120, 5120, 128),    # 20 tiles, 229 pieces of 7 k-steps over 80
+    (5120, 5120, 128),    # 20 tiles as 40 halves, 247 pieces of 13 k-steps over 80
     (1024, 4352, 4096),   # one whole round + 16 tiles split along K
     (5120, 17408, 4096),  # 1024 whole tiles + 64 split
     (256, 256, 128),      # one tile in 4 pieces of one k-step
 ])
 def test_prefill_scratch_counts_every_piece_tile_pair(K, N, M):
-    """The GEMM tail's partial region holds one 256x256 fp32 tile per (piece,
-    tile) pair; the pairs are counted here by walking each piece's k-step run,
-    independently of the library's closed-form slot count."""
+    """The GEMM tail's partial region holds one fp32 accumulator tile per
+    (piece, tail item) pair; the pairs are counted here by walking each
+    piece's k-step run, independently of the library's closed-form slot
+    count. Tail items are the 256x256 tail tiles, or their 256x128 halves when
+    a piece over whole tiles would be at most an eighth of a tile's k-steps."""
     import math
 
     tiles = math.ceil(N / 256) * math.ceil(M / 256)
     rem = tiles % 256
     nk = K // 64
-    pairs = 0
+    pairs, split = 0, 1
     if 0 < rem <= 224 and nk >= 2:
-        total = rem * nk
+        if 2 * rem <= 256 and 8 * math.ceil(rem * nk / 256) <= nk:
+            split = 2
+        total = rem * split * nk
         units = math.ceil(total / 256)
         for v in range(math.ceil(total / units)):
             lo, hi = v * units, min((v + 1) * units, total)
             pairs += len({u // nk for u in range(lo, hi)})
     a256 = lambda b: (b + 255) // 256 * 256
     base = a256(math.ceil(M / 32) * 32 * K * 2) + a256(N * K * 2)
-    assert X.lib().exl3_linear_scratch_bytes(K, N, M, 1) == base + pairs * 256 * 256 * 4
+    assert X.lib().exl3_linear_scratch_bytes(K, N, M, 1) == base + pairs * 256 * (256 // split) * 4

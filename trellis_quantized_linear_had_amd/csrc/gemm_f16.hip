@@ -37,7 +37,9 @@
 // spread evenly over (up to) 256 workgroups, stream-K style, each writing an
 // fp32 accumulator tile (in register order) per tile it touches, and a fixup
 // kernel sums each tile's pieces in k order and runs the same rotation
-// epilogue.
+// epilogue. Where those pieces would be short (at most an eighth of a tile's
+// k-steps) the tail is dealt as 256 x 128 halves of its tiles (two 16-wide q
+// tiles per wave): twice the k-steps per piece and half the partial bytes.
 //
 // Workgroup order is XCD-aware: workgroups are dispatched round-robin over
 // the 8 XCDs, so workgroup w is given tile (w % 8) * ceil(T / 8) + w / 8. Each
@@ -104,44 +106,53 @@ __device__ __forceinline__ f16x8 load_frag(const uint16_t* p) {
 }
 
 // Vector-memory loads one wave issues per k step, in issue order: B slot 0
-// (the next k step's first k32 sub-step, G_QT fragments), the 4 direct-to-LDS
-// loads of the A stage after next (32 rows per wave, 8 rows per instruction),
-// B slot 1 (its second k32 sub-step).
-constexpr int kBLoads = G_QT;
-constexpr int kALoads = 4;
-constexpr int kLoadsPerStep = 2 * kBLoads + kALoads;
-// Before half-step 0 slot 0 must have landed: issued after it, the A stage and
-// slot 1. Before half-step 2 slot 1 must have landed: issued after it, this
-// k step's refill of slot 0.
-constexpr int kWaitSlot0 = kALoads + kBLoads;
-constexpr int kWaitSlot1 = kBLoads;
-// Before the barrier the A stage (issued before slot 1's refill of the
-// previous k step) must have landed: issued after it, that refill and this
-// k step's refill of slot 0.
-constexpr int kWaitStage = 2 * kBLoads;
-// Prologue, issued in steady-state order (A stage 0, slot 0, A stage 1,
-// slot 1): A stage 0 has landed once the loads after it are outstanding.
-constexpr int kWaitPrologue = kBLoads + kALoads + kBLoads;
-static_assert(kWaitPrologue < 64 && kWaitSlot0 < kLoadsPerStep && kWaitSlot1 < kWaitSlot0 && kWaitStage < kLoadsPerStep,
-              "vmcnt counts out of range (6 bits)");
-static_assert(kWaitPrologue == kLoadsPerStep, "the prologue issues one k step's loads after A stage 0");
+// (the next k step's first k32 sub-step, QT fragments: QT 16-wide q tiles per
+// wave), the 4 direct-to-LDS loads of the A stage after next (32 rows per
+// wave, 8 rows per instruction), B slot 1 (its second k32 sub-step).
+template <int QT>
+struct GemmWaits {
+  static constexpr int kBLoads = QT;
+  static constexpr int kALoads = 4;
+  static constexpr int kLoadsPerStep = 2 * kBLoads + kALoads;
+  // Before half-step 0 slot 0 must have landed: issued after it, the A stage
+  // and slot 1. Before half-step 2 slot 1 must have landed: issued after it,
+  // this k step's refill of slot 0.
+  static constexpr int kWaitSlot0 = kALoads + kBLoads;
+  static constexpr int kWaitSlot1 = kBLoads;
+  // Before the barrier the A stage (issued before slot 1's refill of the
+  // previous k step) must have landed: issued after it, that refill and this
+  // k step's refill of slot 0.
+  static constexpr int kWaitStage = 2 * kBLoads;
+  // Prologue, issued in steady-state order (A stage 0, slot 0, A stage 1,
+  // slot 1): A stage 0 has landed once the loads after it are outstanding.
+  static constexpr int kWaitPrologue = kBLoads + kALoads + kBLoads;
+  static_assert(kWaitPrologue < 64 && kWaitSlot0 < kLoadsPerStep && kWaitSlot1 < kWaitSlot0 &&
+                    kWaitStage < kLoadsPerStep,
+                "vmcnt counts out of range (6 bits)");
+  static_assert(kWaitPrologue == kLoadsPerStep, "the prologue issues one k step's loads after A stage 0");
+};
 
 // Waits until at most N vector-memory loads are outstanding. The slot's
 // registers are named as read and written by the wait, so the compiler can
 // neither move the MFMAs that read them above it nor reuse them while their
 // load may still be in flight.
-template <int N>
-__device__ __forceinline__ void wait_slot(f16x8 (&slot)[G_QT]) {
-  static_assert(G_QT == 4, "one operand per fragment of the slot");
-  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(slot[0]), "+v"(slot[1]), "+v"(slot[2]), "+v"(slot[3]) : "n"(N) : "memory");
+template <int N, int QT>
+__device__ __forceinline__ void wait_slot(f16x8 (&slot)[QT]) {
+  static_assert(QT == 4 || QT == 2, "one operand per fragment of the slot");
+  if constexpr (QT == 4)
+    asm volatile("s_waitcnt vmcnt(%4)" : "+v"(slot[0]), "+v"(slot[1]), "+v"(slot[2]), "+v"(slot[3]) : "n"(N)
+                 : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(slot[0]), "+v"(slot[1]) : "n"(N) : "memory");
 }
 
-// Epilogue of one wave's 128 x 64 block: four 16-wide q blocks.
-__device__ __forceinline__ void rotate_store(f32x4 (&acc)[G_PT][G_QT], int lane, int pw, int qw, int P, int Q,
+// Epilogue of one wave's 128 x 16 QT block: QT 16-wide q blocks.
+template <int QT>
+__device__ __forceinline__ void rotate_store(f32x4 (&acc)[G_PT][QT], int lane, int pw, int qw, int P, int Q,
                                              uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
                                              const uint16_t* __restrict__ sign_n) {
 #pragma unroll
-  for (int j = 0; j < G_QT; ++j) {
+  for (int j = 0; j < QT; ++j) {
     f32x4 blk[G_PT];
 #pragma unroll
     for (int i = 0; i < G_PT; ++i) blk[i] = acc[i][j];
@@ -149,13 +160,14 @@ __device__ __forceinline__ void rotate_store(f32x4 (&acc)[G_PT][G_QT], int lane,
   }
 }
 
-// One accumulator tile in scratch: 512 threads x 128 floats, stored as 32
-// float4 columns of 512 (coalesced in both the writer and the fixup).
-__device__ __forceinline__ void store_partial(const f32x4 (&acc)[G_PT][G_QT], f32x4* __restrict__ dst) {
+// One accumulator tile in scratch: 512 threads x 32 QT floats, stored as
+// 8 QT float4 columns of 512 (coalesced in both the writer and the fixup).
+template <int QT>
+__device__ __forceinline__ void store_partial(const f32x4 (&acc)[G_PT][QT], f32x4* __restrict__ dst) {
 #pragma unroll
   for (int i = 0; i < G_PT; ++i)
 #pragma unroll
-    for (int j = 0; j < G_QT; ++j) dst[(i * G_QT + j) * G_THREADS + threadIdx.x] = acc[i][j];
+    for (int j = 0; j < QT; ++j) dst[(i * QT + j) * G_THREADS + threadIdx.x] = acc[i][j];
 }
 
 // Slot of the partial of piece v for tail tile t: the (piece, tile) pairs in
@@ -187,15 +199,17 @@ __device__ __forceinline__ int tail_tile(int t, int tile_base, int tiles_q, int 
 // round-robin over the 8 XCDs, so pieces v and v + 8 j share an XCD, and
 // with a phase period nk / gcd(nk, units) that is a multiple of 8 the pieces
 // in one phase (the same k offsets at every step) all run on one XCD.
-template <int MODE>
-__global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __restrict__ A,
-                                                             const uint16_t* __restrict__ B,
-                                                             uint16_t* __restrict__ y, int32_t P, int32_t Q,
-                                                             int32_t K, int64_t ldy, int32_t n0,
-                                                             const uint16_t* __restrict__ sign_n, int32_t tile_base,
-                                                             int32_t count, int32_t units, int32_t sdiv,
-                                                             int32_t grp, f32x4* __restrict__ partial) {
+template <int MODE, int QT>
+__device__ __forceinline__ void gemm_had_body(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                              uint16_t* __restrict__ y, int32_t P, int32_t Q, int32_t K, int64_t ldy,
+                                              int32_t n0, const uint16_t* __restrict__ sign_n, int32_t tile_base,
+                                              int32_t count, int32_t units, int32_t sdiv, int32_t grp,
+                                              f32x4* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * G_STAGE];
+  using W = GemmWaits<QT>;
+  constexpr int BQ = 64 * QT;          // q extent of this launch's tiles
+  constexpr int SPLIT = G_BQ / BQ;     // tail sub-tiles per whole tile (q halves at QT = 2)
+  static_assert(MODE == 1 || QT == 4, "whole tiles are 256 x 256");
 
   const int tiles_q = (Q + G_BQ - 1) / G_BQ;
   const int nk_all = K / G_BK;
@@ -204,11 +218,11 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
   const int wp = wave & 1, wq = wave >> 1;
   const int lrow = lane & 15, lchunk = lane >> 4;
 
-  f32x4 acc[G_PT][G_QT];
+  f32x4 acc[G_PT][QT];
   // A fragments of one half-step (4 p tiles), two register sets; B fragments
   // of the two k32 sub-steps of one k step: slot t is refilled with the next
   // k step's sub-step t once this k step's last MFMAs reading it are issued
-  f16x8 af[2][4], bq[2][G_QT];
+  f16x8 af[2][4], bq[2][QT];
   // A fragments of half-step h of stage `stage`: p tiles 4 (h % 2) .. + 3,
   // k32 sub-step h / 2 (chunks 4 (h / 2) .. + 3, one per 16-lane group)
   auto read_frags = [&](int stage, int h, int set) {
@@ -222,7 +236,7 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < G_QT; ++j) {
+      for (int j = 0; j < QT; ++j) {
         f32x4& d = acc[4 * (h & 1) + i][j];
         d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[set][i], bq[h >> 1][j], d, 0, 0, 0);
       }
@@ -235,9 +249,9 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * G_QT - 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * QT - 4, 0);
   };
-  // ... and with a slot refill in the half-step: its G_QT B loads go out
+  // ... and with a slot refill in the half-step: its QT B loads go out
   // between the next MFMAs.
   auto interleave_loads = [&]() {
 #pragma unroll
@@ -246,11 +260,11 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
 #pragma unroll
-    for (int k = 0; k < G_QT; ++k) {
+    for (int k = 0; k < QT; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * G_QT - 4 - G_QT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * QT - 4 - QT, 0);
   };
 
   // acc = sum over k-steps [kb0, kb1) of one tile. Schedule per k step kb
@@ -269,21 +283,21 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
 #pragma unroll
     for (int i = 0; i < G_PT; ++i)
 #pragma unroll
-      for (int j = 0; j < G_QT; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < QT; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
     uint32_t offa[4];
     lane_offsets(K, p_base, P, 32 * wave, lane, offa);
     // this wave's B blocks: q rows q_base + 64 wq + 16 j (clamped to the last
     // block; rows past Q are never stored)
     const int nqb = (Q + 15) / 16, kt32 = K / 32;
-    const uint16_t* bsrc[G_QT];
+    const uint16_t* bsrc[QT];
 #pragma unroll
-    for (int j = 0; j < G_QT; ++j) {
-      const int qb = min((q_base + 16 * G_QT * wq + 16 * j) / 16, nqb - 1);
+    for (int j = 0; j < QT; ++j) {
+      const int qb = min((q_base + 16 * QT * wq + 16 * j) / 16, nqb - 1);
       bsrc[j] = B + ((int64_t)qb * kt32 * 64 + lane) * 8;
     }
     auto load_b = [&](int kb, int t) {
 #pragma unroll
-      for (int j = 0; j < G_QT; ++j) bq[t][j] = load_frag(bsrc[j] + (int64_t)(2 * kb + t) * G_FRAG);
+      for (int j = 0; j < QT; ++j) bq[t][j] = load_frag(bsrc[j] + (int64_t)(2 * kb + t) * G_FRAG);
     };
     auto issue_loads = [&](int stage, int k0) { load_rows_lds(A, k0, offa, smem + stage * G_STAGE, 32 * wave); };
     const int nk = kb1 - kb0;
@@ -297,13 +311,13 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
     issue_loads(1, (kb0 + min(1, nk - 1)) * G_BK);
     load_b(kb0, 1);
     // stage 0 landed (the loads after it may not have)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitPrologue) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W::kWaitPrologue) : "memory");
     __syncthreads();
     read_frags(0, 0, 0);
     for (int kk = 0; kk < nk; ++kk) {
       const int b = kk & 1;
       const int kn = kb0 + min(kk + 1, nk - 1);  // the k step the B slots are refilled with
-      wait_slot<kWaitSlot0>(bq[0]);
+      wait_slot<W::kWaitSlot0>(bq[0]);
       read_frags(b, 1, 1);
       mfmas(0, 0);
       interleave();
@@ -313,7 +327,7 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
       load_b(kn, 0);
       interleave_loads();
       __builtin_amdgcn_sched_barrier(0);
-      wait_slot<kWaitSlot1>(bq[1]);
+      wait_slot<W::kWaitSlot1>(bq[1]);
       read_frags(b, 3, 1);
       mfmas(0, 2);
       interleave();
@@ -321,7 +335,7 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
       // only slot 1's refill of the previous k step and slot 0's refill of
       // this one may be outstanding: this wave's A loads of stage kk+1 (issued
       // before them) have landed
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitStage) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W::kWaitStage) : "memory");
       __syncthreads();
       issue_loads(b, (kb0 + min(kk + 2, nk - 1)) * G_BK);
       if (kk + 1 < nk) read_frags(b ^ 1, 0, 0);
@@ -342,7 +356,7 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
     const int tile = tile_base + t;
     const int p_base = (tile / tiles_q) * G_BP, q_base = (tile % tiles_q) * G_BQ;
     run_tile(p_base, q_base, 0, nk_all);
-    rotate_store(acc, lane, p_base + 128 * wp, q_base + 16 * G_QT * wq, P, Q, y, ldy, n0, sign_n);
+    rotate_store(acc, lane, p_base + 128 * wp, q_base + 16 * QT * wq, P, Q, y, ldy, n0, sign_n);
   } else {
     const int total = count * nk_all;
     const int pieces = (total + units - 1) / units;
@@ -352,28 +366,49 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __r
     const int end = min(unit + units, total);
     for (int seg = 0; seg < 2 && unit < end; ++seg) {
       const int t = unit / nk_all, kb0 = unit - t * nk_all, kb1 = min(nk_all, kb0 + (end - unit));
-      const int tile = tail_tile(t, tile_base, tiles_q, grp);
-      run_tile((tile / tiles_q) * G_BP, (tile % tiles_q) * G_BQ, kb0, kb1);
-      store_partial(acc, partial + (int64_t)partial_slot(v, t, sdiv) * (G_BP * G_BQ / 4));
+      const int tile = tail_tile(t / SPLIT, tile_base, tiles_q, grp);
+      run_tile((tile / tiles_q) * G_BP, (tile % tiles_q) * G_BQ + (t % SPLIT) * BQ, kb0, kb1);
+      store_partial(acc, partial + (int64_t)partial_slot(v, t, sdiv) * (G_BP * BQ / 4));
       unit += kb1 - kb0;
     }
   }
+}
+
+// Whole 256 x 256 tiles (MODE 0) and the stream-K tail over whole tiles (MODE 1).
+template <int MODE>
+__global__ __launch_bounds__(G_THREADS) void gemm_had_kernel(const uint16_t* __restrict__ A,
+                                                             const uint16_t* __restrict__ B,
+                                                             uint16_t* __restrict__ y, int32_t P, int32_t Q,
+                                                             int32_t K, int64_t ldy, int32_t n0,
+                                                             const uint16_t* __restrict__ sign_n, int32_t tile_base,
+                                                             int32_t count, int32_t units, int32_t sdiv,
+                                                             int32_t grp, f32x4* __restrict__ partial) {
+  gemm_had_body<MODE, 4>(A, B, y, P, Q, K, ldy, n0, sign_n, tile_base, count, units, sdiv, grp, partial);
+}
+
+// The stream-K tail over 256 x 128 halves of the tail tiles (count = 2 rem).
+__global__ __launch_bounds__(G_THREADS) void gemm_had_tail_half_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ y, int32_t P, int32_t Q,
+    int32_t K, int64_t ldy, int32_t n0, const uint16_t* __restrict__ sign_n, int32_t tile_base, int32_t count,
+    int32_t units, int32_t sdiv, int32_t grp, f32x4* __restrict__ partial) {
+  gemm_had_body<1, 2>(A, B, y, P, Q, K, ldy, n0, sign_n, tile_base, count, units, sdiv, grp, partial);
 }
 
 // Sums the k-pieces of one 128 (p) x 16 (q) block of a tail tile in piece
 // order and runs the rotation epilogue. One single-wave workgroup per (tail
 // tile, wave, 16-wide q block) spreads the partial reads over the CUs; the
 // loads of two pieces are in flight together.
-__global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict__ partial, int32_t units,
-                                                        int32_t sdiv, int32_t grp, int32_t tile_base, int32_t P,
-                                                        int32_t Q, int32_t K,
-                                                        uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
-                                                        const uint16_t* __restrict__ sign_n) {
-  const int per_tile = (G_THREADS / 64) * G_QT;
-  const int item = blockIdx.x / per_tile, wave = (blockIdx.x % per_tile) / G_QT, j = blockIdx.x % G_QT;
+template <int QT>
+__device__ __forceinline__ void gemm_fixup_body(const f32x4* __restrict__ partial, int32_t units, int32_t sdiv,
+                                                int32_t grp, int32_t tile_base, int32_t P, int32_t Q, int32_t K,
+                                                uint16_t* __restrict__ y, int64_t ldy, int32_t n0,
+                                                const uint16_t* __restrict__ sign_n) {
+  constexpr int BQ = 64 * QT, SPLIT = G_BQ / BQ;
+  const int per_tile = (G_THREADS / 64) * QT;
+  const int item = blockIdx.x / per_tile, wave = (blockIdx.x % per_tile) / QT, j = blockIdx.x % QT;
   const int tiles_q = (Q + G_BQ - 1) / G_BQ;
-  const int tile = tail_tile(item, tile_base, tiles_q, grp);
-  const int p_base = (tile / tiles_q) * G_BP, q_base = (tile % tiles_q) * G_BQ;
+  const int tile = tail_tile(item / SPLIT, tile_base, tiles_q, grp);
+  const int p_base = (tile / tiles_q) * G_BP, q_base = (tile % tiles_q) * G_BQ + (item % SPLIT) * BQ;
   const int lane = threadIdx.x;
   const int tid = 64 * wave + lane;  // the thread of the k-piece workgroup this lane stands for
   const int wp = wave & 1, wq = wave >> 1;
@@ -381,12 +416,12 @@ __global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict_
   // [item nk, (item + 1) nk), in k order
   const int nk = K / G_BK;
   const int w_lo = item * nk / units, w_hi = ((item + 1) * nk - 1) / units;
-  auto piece = [&](int w) { return partial + (int64_t)partial_slot(w, item, sdiv) * (G_BP * G_BQ / 4) + tid; };
+  auto piece = [&](int w) { return partial + (int64_t)partial_slot(w, item, sdiv) * (G_BP * BQ / 4) + tid; };
   f32x4 a[G_PT];
   {
     const f32x4* src = piece(w_lo);
 #pragma unroll
-    for (int i = 0; i < G_PT; ++i) a[i] = src[(i * G_QT + j) * G_THREADS];
+    for (int i = 0; i < G_PT; ++i) a[i] = src[(i * QT + j) * G_THREADS];
   }
   for (int w = w_lo + 1; w <= w_hi; w += 2) {
     const f32x4* s0 = piece(w);
@@ -394,8 +429,8 @@ __global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict_
     f32x4 v0[G_PT], v1[G_PT];
 #pragma unroll
     for (int i = 0; i < G_PT; ++i) {
-      v0[i] = s0[(i * G_QT + j) * G_THREADS];
-      v1[i] = s1[(i * G_QT + j) * G_THREADS];
+      v0[i] = s0[(i * QT + j) * G_THREADS];
+      v1[i] = s1[(i * QT + j) * G_THREADS];
     }
 #pragma unroll
     for (int i = 0; i < G_PT; ++i) a[i] += v0[i];
@@ -404,16 +439,37 @@ __global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict_
       for (int i = 0; i < G_PT; ++i) a[i] += v1[i];
     }
   }
-  rotate_store_block16(a, lane, p_base + 128 * wp, q_base + 16 * G_QT * wq + 16 * j, P, Q, y, ldy, n0, sign_n);
+  rotate_store_block16(a, lane, p_base + 128 * wp, q_base + 16 * QT * wq + 16 * j, P, Q, y, ldy, n0, sign_n);
+}
+
+__global__ __launch_bounds__(64) void gemm_fixup_kernel(const f32x4* __restrict__ partial, int32_t units,
+                                                        int32_t sdiv, int32_t grp, int32_t tile_base, int32_t P,
+                                                        int32_t Q, int32_t K, uint16_t* __restrict__ y, int64_t ldy,
+                                                        int32_t n0, const uint16_t* __restrict__ sign_n) {
+  gemm_fixup_body<4>(partial, units, sdiv, grp, tile_base, P, Q, K, y, ldy, n0, sign_n);
+}
+
+// The fixup of the half-tile tail: one item per 256 x 128 half.
+__global__ __launch_bounds__(64) void gemm_fixup_half_kernel(const f32x4* __restrict__ partial, int32_t units,
+                                                             int32_t sdiv, int32_t grp, int32_t tile_base, int32_t P,
+                                                             int32_t Q, int32_t K, uint16_t* __restrict__ y,
+                                                             int64_t ldy, int32_t n0,
+                                                             const uint16_t* __restrict__ sign_n) {
+  gemm_fixup_body<2>(partial, units, sdiv, grp, tile_base, P, Q, K, y, ldy, n0, sign_n);
 }
 
 // Round plan: `full` tiles (whole rounds of 256) run whole; the `rem` tiles
 // after them are spread stream-K style, `units` k-steps per workgroup over
 // `pieces` workgroups, when that beats one more whole round with idle CUs
 // (rem <= 224); otherwise they also run whole. grp > 0 selects the grouped
-// tail order (tail_tile).
+// tail order (tail_tile). split = 2: when a piece would be at most an eighth
+// of a whole tile's k-steps, the tail tiles are dealt as 256 x 128 halves
+// instead (twice the k-steps per piece, half the partial bytes per piece):
+// the partials' round trip is then what the tail costs beyond its MFMAs, and
+// halving it outweighs the half tile's lower MFMA rate, which decides at
+// longer pieces.
 struct GemmPlan {
-  int tiles, full, rem, units, pieces, sdiv, slots, grp;
+  int tiles, full, rem, split, units, pieces, sdiv, slots, grp;
 };
 
 static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
@@ -421,6 +477,7 @@ static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
   g.tiles = ((P + G_BP - 1) / G_BP) * ((Q + G_BQ - 1) / G_BQ);
   g.full = g.tiles / G_CUS * G_CUS;
   g.rem = g.tiles - g.full;
+  g.split = 1;
   g.units = 0;
   g.pieces = 0;
   g.sdiv = 1;
@@ -428,8 +485,11 @@ static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
   g.grp = 0;
   const int nk = K / G_BK;
   if (g.rem > 0 && g.rem <= 224 && nk >= 2) {
-    const int64_t total = (int64_t)g.rem * nk;
-    g.units = (int)((total + G_CUS - 1) / G_CUS);  // <= nk because rem < G_CUS
+    const int64_t units_whole = ((int64_t)g.rem * nk + G_CUS - 1) / G_CUS;
+    if (2 * g.rem <= G_CUS && 8 * units_whole <= nk) g.split = 2;
+    const int sub = g.rem * g.split;  // tail items (tiles or halves)
+    const int64_t total = (int64_t)sub * nk;
+    g.units = (int)((total + G_CUS - 1) / G_CUS);  // <= nk because sub <= G_CUS
     g.pieces = (int)((total + g.units - 1) / g.units);
     int a = nk, b = g.units;  // gcd
     while (b) {
@@ -438,10 +498,10 @@ static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
       b = r;
     }
     g.sdiv = g.units / a;
-    const int t_last = g.rem - 1;
+    const int t_last = sub - 1;
     g.slots = g.pieces + t_last - t_last / g.sdiv;  // one past the last slot
     const int tiles_q = (Q + G_BQ - 1) / G_BQ;
-    if (g.full % tiles_q == 0 && g.rem % (tiles_q * g.sdiv) == 0) g.grp = g.sdiv;
+    if (g.split == 1 && g.full % tiles_q == 0 && g.rem % (tiles_q * g.sdiv) == 0) g.grp = g.sdiv;
   } else {
     g.full = g.tiles;
     g.rem = 0;
@@ -451,7 +511,7 @@ static GemmPlan gemm_plan(int32_t P, int32_t Q, int32_t K) {
 
 size_t gemm_partial_bytes(int32_t P, int32_t Q, int32_t K) {
   const GemmPlan g = gemm_plan(P, Q, K);
-  return (size_t)g.slots * G_BP * G_BQ * sizeof(float);
+  return (size_t)g.slots * G_BP * (G_BQ / g.split) * sizeof(float);
 }
 
 hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, int32_t P, int32_t Q, int32_t K,
@@ -470,10 +530,19 @@ hipError_t launch_gemm_had(const uint16_t* A, const uint16_t* B, uint16_t* y, in
     if (e != hipSuccess) return e;
   }
   if (g.rem > 0) {
-    gemm_had_kernel<1><<<8 * ((g.pieces + 7) / 8), G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, g.full,
-                                                                           g.rem, g.units, g.sdiv, g.grp, part);
-    gemm_fixup_kernel<<<g.rem * (G_THREADS / 64) * G_QT, 64, 0, stream>>>(part, g.units, g.sdiv, g.grp, g.full, P,
-                                                                          Q, K, y, ldy, n0, sign_n);
+    const unsigned grid = 8 * ((g.pieces + 7) / 8);
+    // fixup: one single-wave workgroup per (tail item, wave, 16-wide q block)
+    const unsigned fix = (unsigned)(g.rem * g.split) * (G_THREADS / 64) * (G_QT / g.split);
+    if (g.split == 1) {
+      gemm_had_kernel<1><<<grid, G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, g.full, g.rem, g.units,
+                                                         g.sdiv, g.grp, part);
+      gemm_fixup_kernel<<<fix, 64, 0, stream>>>(part, g.units, g.sdiv, g.grp, g.full, P, Q, K, y, ldy, n0, sign_n);
+    } else {
+      gemm_had_tail_half_kernel<<<grid, G_THREADS, 0, stream>>>(A, B, y, P, Q, K, ldy, n0, sign_n, g.full,
+                                                                2 * g.rem, g.units, g.sdiv, g.grp, part);
+      gemm_fixup_half_kernel<<<fix, 64, 0, stream>>>(part, g.units, g.sdiv, g.grp, g.full, P, Q, K, y, ldy, n0,
+                                                     sign_n);
+    }
   }
   return hipGetLastError();
 }
