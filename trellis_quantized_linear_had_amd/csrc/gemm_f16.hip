@@ -192,10 +192,11 @@ __device__ __forceinline__ int tail_tile(int t, int tile_base, int tiles_q, int 
 
 // MODE 0: workgroup w computes tile tile_base + t (t in XCD order, t < count)
 // over all of K and runs the rotation epilogue. MODE 1 (stream-K tail): the
-// count tiles' k-steps, tile-major, are dealt in runs of `units` to the
-// workgroups; piece v covers [v units, (v + 1) units), at most two tiles
-// (units <= K / G_BK), and writes one partial per tile it touches (slot
-// partial_slot(v, tile)). Piece v is workgroup v: workgroups are dealt
+// count items' k-steps, item-major, are dealt in runs of `units` to the
+// workgroups (an item is a tail tile, or at QT = 2 one of its two 256 x 128
+// halves: item t is half t % SPLIT of tail tile t / SPLIT); piece v covers
+// [v units, (v + 1) units), at most two items (units <= K / G_BK), and writes
+// one partial per item it touches (slot partial_slot(v, item)). Piece v is workgroup v: workgroups are dealt
 // round-robin over the 8 XCDs, so pieces v and v + 8 j share an XCD, and
 // with a phase period nk / gcd(nk, units) that is a multiple of 8 the pieces
 // in one phase (the same k offsets at every step) all run on one XCD.
@@ -394,10 +395,11 @@ __global__ __launch_bounds__(G_THREADS) void gemm_had_tail_half_kernel(
   gemm_had_body<1, 2>(A, B, y, P, Q, K, ldy, n0, sign_n, tile_base, count, units, sdiv, grp, partial);
 }
 
-// Sums the k-pieces of one 128 (p) x 16 (q) block of a tail tile in piece
-// order and runs the rotation epilogue. One single-wave workgroup per (tail
-// tile, wave, 16-wide q block) spreads the partial reads over the CUs; the
-// loads of two pieces are in flight together.
+// Sums the k-pieces of one 128 (p) x 16 (q) block of a tail item (a tail
+// tile, or at QT = 2 one of its 256 x 128 halves) in piece order and runs the
+// rotation epilogue. One single-wave workgroup per (item, wave, 16-wide q
+// block) spreads the partial reads over the CUs; the loads of two pieces are
+// in flight together.
 template <int QT>
 __device__ __forceinline__ void gemm_fixup_body(const f32x4* __restrict__ partial, int32_t units, int32_t sdiv,
                                                 int32_t grp, int32_t tile_base, int32_t P, int32_t Q, int32_t K,
