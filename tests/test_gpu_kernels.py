@@ -204,6 +204,8 @@ def test_linear_two_slices(T, X, cb):
 @pytest.mark.parametrize("K,N,M", [
     (2560, 3328, 200),    # 13 tiles < 256 CUs: the tail as 26 256x128 halves, pieces of 5 k-steps over 40
                           # straddling halves; each tile's second half is ragged (rows 128..199 of 256)
+    (2560, 3328, 100),    # the same split with every second half past the last row (q 128..255, M = 100):
+                          # those pieces read clamped rows and their fixup stores nothing
     (1024, 4352, 4096),   # 272 tiles: one whole round + 16 tiles as 32 halves split along K
     (1024, 4608, 300),    # 36 tiles in two column blocks, the last ragged: grouped tail order (3-strip groups)
 ])
