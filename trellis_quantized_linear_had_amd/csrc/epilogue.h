@@ -1,12 +1,36 @@
 // Output stage shared by the MFMA kernels that compute the transposed
-// product D[p][q] (p = output column, q = input row) with
-// v_mfma_f32_32x32x16_f16 tiles: the 128-point output rotation along p, the
-// sign vector, the 1/sqrt(128) scaling and the fp16 store of y[q][p].
+// product D[p][q] (p = output column, q = input row) in the accumulator
+// layouts of v_mfma_f32_32x32x16_f16 and v_mfma_f32_16x16x32_f16: the
+// 128-point output rotation along p, the sign vector, the 1/sqrt(128) scaling
+// and the fp16 store of y[q][p].
 #pragma once
 
 #include "common.h"
 
 namespace exl3 {
+
+// The butterfly between lanes M apart (M = 16 or 32) without the LDS: a
+// permlane swap of the value with itself leaves, in every lane of a pair of
+// M-lane rows, the lower row's value in its first result and the upper row's
+// in its second. With s = +1 in the lower row and -1 in the upper one this
+// gives lower + upper and lower - upper, the same roundings as adding the
+// partner's value from a shuffle. Every lane of the wave must be active.
+template <int M>
+__device__ __forceinline__ float xor_butterfly(float v, float s) {
+  static_assert(M == 16 || M == 32, "rows of 16 or 32 lanes");
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  uint32_t lo, hi;
+  if constexpr (M == 16) {
+    const auto w = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    lo = w[0];
+    hi = w[1];
+  } else {
+    const auto w = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = w[0];
+    hi = w[1];
+  }
+  return __builtin_fmaf(s, __builtin_bit_cast(float, hi), __builtin_bit_cast(float, lo));
+}
 
 // Output rotation + signs + fp16 store of one 128 (p) x 32 (q) block of a
 // wave. a[i][r] holds D[p][q] with (inside the 128-row rotation block)
@@ -57,10 +81,7 @@ __device__ __forceinline__ void rotate_store_block(f32x16 (&a)[4], int lane, int
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float partner = __shfl_xor(a[i][r], 32);
-      a[i][r] = __builtin_fmaf(s, a[i][r], partner);
-    }
+    for (int r = 0; r < 16; ++r) a[i][r] = xor_butterfly<32>(a[i][r], s);
   if (pw >= P) return;
   const int q = q0 + lrow;
   if (q >= Q) return;
@@ -118,16 +139,16 @@ __device__ __forceinline__ void rotate_store_block16(f32x4 (&a)[8], int lane, in
           a[i][r] = u + v;
           a[i + h][r] = u - v;
         }
-#pragma unroll
-  for (int m = 16; m <= 32; m <<= 1) {  // lane bits 4, 5: the partner m lanes away
-    const float s = (lane & m) ? -1.f : 1.f;
+  {  // lane bits 4, 5: the partner 16, then 32 lanes away
+    const float s16 = (lane & 16) ? -1.f : 1.f, s32 = (lane & 32) ? -1.f : 1.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float partner = __shfl_xor(a[i][r], m);
-        a[i][r] = __builtin_fmaf(s, a[i][r], partner);
-      }
+      for (int r = 0; r < 4; ++r) a[i][r] = xor_butterfly<16>(a[i][r], s16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[i][r] = xor_butterfly<32>(a[i][r], s32);
   }
   if (pw >= P) return;
   const int q = q0 + lq;
@@ -169,10 +190,7 @@ __device__ __forceinline__ void wht64_half(f32x16 (&t)[2], int lane) {
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float partner = __shfl_xor(t[f][r], 32);
-      t[f][r] = __builtin_fmaf(s, t[f][r], partner);
-    }
+    for (int r = 0; r < 16; ++r) t[f][r] = xor_butterfly<32>(t[f][r], s);
 }
 
 // ... and the wave that stores a block combines the halves (bit 6: lo + hi
