@@ -381,13 +381,14 @@ CSRC = os.path.join(ROOT, "trellis_quantized_linear_had_amd", "csrc")
 # sources whose change makes a stored traffic figure stale
 PMC_KERNELS = {
     "logits": ("exl3::logits_kernel", "logits_kernel M=16", ("logits.hip", "common.h")),
-    "gemm": ("exl3::gemm_had_kernel<0>", "gemm_had_kernel<0> M=2048", ("gemm_f16.hip", "common.h")),
+    "gemm": ("exl3::gemm_had_kernel<0>", "gemm_had_kernel<0> M=2048", ("gemm_f16.hip", "epilogue.h", "common.h")),
     "decode": ("exl3::decode_gemm_kernel<6, true, 1, 4>", "decode_gemm_kernel M=16",
                ("decode_gemm.hip", "decode_plan.h", "trellis.h", "common.h")),
     "reconstruct": ("exl3::reconstruct_nk_kernel<4>", "reconstruct_nk_kernel K5120xN17408",
                     ("reconstruct.hip", "trellis.h", "common.h")),
     # the down-projection geometry, where all 160 tiles run as stream-K pieces
-    "gemm_tail": ("exl3::gemm_had_kernel<1>", "gemm_had_kernel<1> K17408xN5120 M=2048", ("gemm_f16.hip", "common.h")),
+    "gemm_tail": ("exl3::gemm_had_kernel<1>", "gemm_had_kernel<1> K17408xN5120 M=2048",
+                  ("gemm_f16.hip", "epilogue.h", "common.h")),
     # the eight-wave dequant-GEMM at M = 256 (the dispatch's choice there): 68 units of 256 rows x 256
     # columns, each split in three k pieces
     "dq": ("exl3::dqgemm2_kernel<16, true>", "dqgemm2_kernel<16,true> K5120xN17408 M=256",
