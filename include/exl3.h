@@ -204,7 +204,8 @@ int had_r_128(const uint16_t *in, uint16_t *out, int64_t rows, int64_t cols, con
  * x: M x K row-major fp16; w: w_rows x K row-major fp16 (only rows < n_pad are
  * read; the GEMM runs over whole 128-row tiles up to n_pad); fp32 accumulation.
  * The GEMM and the mask are one call: there is no way to obtain padded logits
- * without the mask. K must be a multiple of 128. scratch: at least
+ * without the mask. K must be a positive multiple of 128, at most 8388608
+ * (else EXL3_ESHAPE). scratch: at least
  * logits_scratch_bytes(M, K, n_valid, w_rows) bytes. M = 0 is a no-op. */
 int logits_pad_mask_argmax(const uint16_t *x, int64_t M, int32_t K, const uint16_t *w, int64_t w_rows,
                            int64_t n_valid, uint16_t *logits, int64_t ld_logits, int64_t *argmax,

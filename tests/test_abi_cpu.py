@@ -139,6 +139,7 @@ def test_logits_validation():
     assert call(n_valid=301) == X.EXL3_EWIDTH
     assert call(ld=299) == X.EXL3_EWIDTH
     assert call(K=200) == X.EXL3_ESHAPE
+    assert call(K=(1 << 23) + 128) == X.EXL3_ESHAPE  # a wave's 128 rows past a 32-bit buffer range
     assert call(M=-1) == X.EXL3_EINVAL
     assert call(x=0) == X.EXL3_EINVAL
     assert call(nbytes=0) == X.EXL3_ESCRATCH

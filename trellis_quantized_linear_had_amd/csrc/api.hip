@@ -655,7 +655,8 @@ int logits_entry(const uint16_t* x, int64_t M, int32_t K, const uint16_t* w, int
   g_msg[0] = 0;
   if (M < 0 || w_rows < 0) return fail(EXL3_EINVAL, "M = %lld, w_rows = %lld", (long long)M, (long long)w_rows);
   if (M > 0x7FFFFFFF || w_rows > 0x7FFFFFFF) return fail(EXL3_EINVAL, "M or w_rows too large");
-  if (K <= 0 || K % 128) return fail(EXL3_ESHAPE, "K = %d must be a positive multiple of 128", K);
+  if (K <= 0 || K % 128 || K > (1 << 23))
+    return fail(EXL3_ESHAPE, "K = %d must be a positive multiple of 128, at most 8388608", K);
   const int64_t n_pad = logits_padded_width(n_valid, w_rows);
   if (n_pad < 0)
     return fail(EXL3_EWIDTH, "n_valid = %lld must be in [1, w_rows = %lld]", (long long)n_valid, (long long)w_rows);

@@ -10,12 +10,13 @@
 // feeds them to v_mfma_f32_16x16x32_f16 as the A operand, with 16 rows of x as
 // the B operand. Inside a 64-wide k chunk, MFMA step s takes the k slice
 // 32 s + 8 g .. + 8 in lane group g on both operands (a permutation of k, which
-// leaves the dot products unchanged), so each 16-byte load instruction reads
-// 64 contiguous bytes of each of 16 weight rows. A pre-pass stores x in that
-// fragment order (rows past M zero), so each B-fragment load reads 1 KiB of
-// contiguous memory instead of 16 rows 2K bytes apart, which measured ~40 us
-// slower per call at M = 16 (the row-strided lines crowd a few L2 channels).
-// The loads of the next chunk are issued before the MFMAs of the current one.
+// leaves the dot products unchanged). The weights reach the MFMAs through a
+// two-slot LDS ring per wave: whole-line non-temporal direct-to-LDS loads fill
+// one slot while the MFMAs read their fragments from the other. A pre-pass
+// stores x in fragment order (rows past M zero), so each B-fragment load reads
+// 1 KiB of contiguous memory instead of 16 rows 2K bytes apart, which measured
+// ~40 us slower per call at M = 16 (the row-strided lines crowd a few L2
+// channels).
 #include "common.h"
 #include "marks.h"
 
@@ -43,34 +44,38 @@ __global__ __launch_bounds__(256) void logits_xperm_kernel(const uint16_t* __res
   *reinterpret_cast<u32x4*>(xp + c * 8) = v;
 }
 
-// Loads one LG_KC-wide chunk: LG_TILES x LG_STEPS weight fragments and the
-// LG_STEPS x fragments.
-__device__ __forceinline__ void logits_load_chunk(const uint16_t* const (&wrow)[LG_TILES], const uint16_t* xfrag,
-                                                  int kc, u32x4 (&av)[LG_TILES][LG_STEPS], u32x4 (&bv)[LG_STEPS]) {
-#pragma unroll
-  for (int t = 0; t < LG_TILES; ++t)
-#pragma unroll
-    for (int s = 0; s < LG_STEPS; ++s) av[t][s] = *reinterpret_cast<const u32x4*>(wrow[t] + kc + 32 * s);
-#pragma unroll
-  for (int s = 0; s < LG_STEPS; ++s) bv[s] = *reinterpret_cast<const u32x4*>(xfrag + (int64_t)(kc / 32 + s) * 64 * 8);
+// Chunk c of a wave (LG_KC k of its LG_ROWS weight rows, then the chunk's
+// LG_STEPS x fragments) goes from global memory straight into the wave's ring
+// slot c % 2 by direct-to-LDS loads. Each weight load instruction reads whole
+// 128-byte lines, 8 rows x 128 bytes (lane l: row 8 i + l / 8, 16-byte piece
+// l % 8), non-temporal: the weights are read once, and a stream of whole
+// lines without cache allocation measured 7.0 TB/s against 6.2 with ordinary
+// loads (half lines, which the MFMA register layout would need, lose the
+// other half without the cache). The piece a lane fetches is XOR-swizzled by
+// its row, (row >> 1) & 7, so the fragment reads below (16 consecutive rows,
+// one piece) fall on 16 distinct bank groups.
+typedef __attribute__((address_space(3))) void lg_lds_void;
+#define LG_SLOT_BYTES (LG_ROWS * LG_KC * 2 + LG_STEPS * 1024)  // weights, then x fragments
+#define LG_LOADS (LG_ROWS / 8 + LG_STEPS)                      // load instructions per chunk
+
+__device__ __forceinline__ void lg_load_lds16(__amdgpu_buffer_rsrc_t rs, lg_lds_void* dst, uint32_t voff, uint32_t soff,
+                                              bool nt) {
+  if (nt)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, soff, 0, 2);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, soff, 0, 0);
 }
 
-__device__ __forceinline__ void logits_mfma_chunk(const u32x4 (&av)[LG_TILES][LG_STEPS], const u32x4 (&bv)[LG_STEPS],
-                                                  f32x4 (&acc)[LG_TILES]) {
-#pragma unroll
-  for (int s = 0; s < LG_STEPS; ++s)
-#pragma unroll
-    for (int t = 0; t < LG_TILES; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av[t][s]),
-                                                      __builtin_bit_cast(f16x8, bv[s]), acc[t], 0, 0, 0);
-}
+__device__ __forceinline__ int lg_swz(int row) { return (row >> 1) & 7; }
 
 __global__ __launch_bounds__(64 * LG_WAVES) void logits_kernel(const uint16_t* __restrict__ xp, int32_t M, int32_t K,
                                                                const uint16_t* __restrict__ w, int64_t n_valid,
                                                                int64_t n_pad, uint16_t* __restrict__ logits,
                                                                int64_t ld, bool vec_store, int32_t* __restrict__ pk,
                                                                int32_t* __restrict__ pi, int64_t n_items, int32_t m0) {
-  const int64_t item = (int64_t)blockIdx.x * LG_WAVES + (threadIdx.x >> 6);
+  __shared__ __attribute__((aligned(16))) char ring[LG_WAVES][2][LG_SLOT_BYTES];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar resources below
+  const int64_t item = (int64_t)blockIdx.x * LG_WAVES + wv;
   if (item >= n_items) return;  // whole wave; no workgroup barriers below
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, pl = lane & 15;
@@ -81,27 +86,68 @@ __global__ __launch_bounds__(64 * LG_WAVES) void logits_kernel(const uint16_t* _
 #pragma unroll
   for (int t = 0; t < LG_TILES; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // Rows past the padded width read row 0 instead (valid memory, no branch
-  // in the loop); their sums are never stored or ranked.
-  const uint16_t* wrow[LG_TILES];
+  // The wave's rows as one buffer (at most LG_ROWS x K x 2 bytes, below 4 GiB
+  // for the entry point's K <= 2^23); rows past
+  // the padded width read the wave's first row instead (never stored or
+  // ranked), so every load stays inside it.
+  const int64_t rows_here = n_pad - p0 < LG_ROWS ? n_pad - p0 : LG_ROWS;
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(w + p0 * (int64_t)K, (uint32_t)(rows_here * K * 2));
+  uint32_t voff[LG_ROWS / 8];  // bytes: row 8 i + lane / 8, piece (lane % 8) ^ swz
 #pragma unroll
-  for (int t = 0; t < LG_TILES; ++t) {
-    const int64_t row = p0 + 16 * t + pl;
-    wrow[t] = w + (row < n_pad ? row : 0) * (int64_t)K + 8 * g;
+  for (int i = 0; i < LG_ROWS / 8; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    voff[i] = (uint32_t)(r < rows_here ? r : 0) * (uint32_t)K * 2u + 16u * (uint32_t)((lane & 7) ^ lg_swz(r));
   }
-  const uint16_t* xfrag = xp + ((int64_t)(m0 / 16) * (K / 32) * 64 + lane) * 8;
+  // this row group's fragments, K / 32 KiB
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xp + (int64_t)(m0 / 16) * 16 * K, (uint32_t)(K / 32) * 1024u);
+  char* my = ring[wv][0];
+  auto issue = [&](int c) {  // chunk c into slot c % 2
+    char* slot = my + (c & 1) * LG_SLOT_BYTES;
+    const uint32_t kb = (uint32_t)c * LG_KC * 2;  // the chunk's byte offset in a row
+#pragma unroll
+    for (int i = 0; i < LG_ROWS / 8; ++i) lg_load_lds16(wrs, (lg_lds_void*)(slot + i * 1024), voff[i], kb, true);
+#pragma unroll
+    for (int st = 0; st < LG_STEPS; ++st)
+      lg_load_lds16(xrs, (lg_lds_void*)(slot + LG_ROWS * LG_KC * 2 + st * 1024), (uint32_t)lane * 16,
+                    (uint32_t)(c * LG_STEPS + st) * 1024u, false);
+  };
+  // fragment reads: tile t, step s: row 16 t + pl, piece 4 s + g
+  uint32_t aoff[LG_TILES][LG_STEPS];
+#pragma unroll
+  for (int t = 0; t < LG_TILES; ++t)
+#pragma unroll
+    for (int st = 0; st < LG_STEPS; ++st) {
+      const int r = 16 * t + pl;
+      aoff[t][st] = (uint32_t)(r * LG_KC * 2 + 16 * ((4 * st + g) ^ lg_swz(r)));
+    }
 
-  // Two chunk buffers: chunk c + 1 is in flight while the MFMAs of chunk c
-  // run (K is a multiple of 128, so chunks come in pairs).
-  u32x4 av0[LG_TILES][LG_STEPS], bv0[LG_STEPS], av1[LG_TILES][LG_STEPS], bv1[LG_STEPS];
-  logits_load_chunk(wrow, xfrag, 0, av0, bv0);
-  for (int kc = 0; kc < K; kc += 2 * LG_KC) {
-    logits_load_chunk(wrow, xfrag, kc + LG_KC, av1, bv1);
-    __builtin_amdgcn_sched_barrier(0);
-    logits_mfma_chunk(av0, bv0, acc);
-    if (kc + 2 * LG_KC < K) logits_load_chunk(wrow, xfrag, kc + 2 * LG_KC, av0, bv0);  // uniform
-    __builtin_amdgcn_sched_barrier(0);
-    logits_mfma_chunk(av1, bv1, acc);
+  const int nc = K / LG_KC;
+  issue(0);
+  if (nc > 1) issue(1);
+  for (int c = 0; c < nc; ++c) {
+    // chunk c has landed: only chunk c + 1's loads (issued after it) may be
+    // outstanding; on the last chunk none
+    if (c + 1 < nc)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LG_LOADS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const char* slot = my + (c & 1) * LG_SLOT_BYTES;
+    u32x4 bv[LG_STEPS];
+#pragma unroll
+    for (int st = 0; st < LG_STEPS; ++st)
+      bv[st] = *reinterpret_cast<const u32x4*>(slot + LG_ROWS * LG_KC * 2 + st * 1024 + lane * 16);
+#pragma unroll
+    for (int st = 0; st < LG_STEPS; ++st)
+#pragma unroll
+      for (int t = 0; t < LG_TILES; ++t) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(slot + aoff[t][st]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av), __builtin_bit_cast(f16x8, bv[st]),
+                                                        acc[t], 0, 0, 0);
+      }
+    // every read of the slot has returned (the MFMAs above consumed them)
+    // before chunk c + 2's loads overwrite it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (c + 2 < nc) issue(c + 2);
   }
 
   // Epilogue: lane holds D[p = p0 + 16t + 4g + r][q]; round to fp16, mask the

@@ -73,8 +73,9 @@ int exl3m_logits_marked(const uint16_t *x, int64_t M, int32_t K, const uint16_t 
  *     v_mfma_f32_32x32x16_f16 (32768 FLOP each);
  *   exl3m_probe_stream: write = 0 reads `bytes` of src in 16-byte accesses,
  *     1 fills `bytes` of dst, 2 reads src as rows of 10240 bytes in the
- *     padded-logits GEMM's pattern (each 16-byte load instruction reads 64
- *     bytes of each of 16 rows; whole groups of 128 rows only, so
+ *     padded-logits GEMM's pattern (each 16-byte load instruction reads a
+ *     whole 128-byte line of each of 8 rows, non-temporal; whole groups of
+ *     128 rows only, so
  *     floor(bytes / 1310720) * 1310720 bytes); bytes a multiple of 16.
  * sink: device buffer of EXL3M_PROBE_SINK_BYTES that keeps the results live.
  * clocks (compute probes): device buffer of 4 x EXL3M_PROBE_WORKGROUPS uint64:

@@ -129,15 +129,13 @@ __global__ __launch_bounds__(256) void probe_stream_kernel(const u32x4* __restri
 
 // Row-pattern read: the buffer as rows of PROBE_ROW_BYTES; a wave owns 128
 // rows and walks them in 128-byte column chunks, each 16-byte load
-// instruction reading 64 contiguous bytes of each of 16 rows (the access
-// pattern of the padded-logits GEMM's weight stream), with the next chunk's
-// 16 loads issued before the current chunk is consumed.
+// instruction reading whole 128-byte lines of 8 rows (lane l: row 8 i + l / 8,
+// piece l % 8), non-temporal: the weight stream of the padded-logits GEMM.
+// The next chunk's 16 loads are issued before the current chunk is consumed.
 #define PROBE_ROW_BYTES 10240
-__device__ __forceinline__ void probe_rows_chunk(const char* const (&rp)[8], int kc, u32x4 (&v)[8][2]) {
+__device__ __forceinline__ void probe_rows_chunk(const char* const (&rp)[16], int kc, u32x4 (&v)[16]) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) v[t][s] = *reinterpret_cast<const u32x4*>(rp[t] + kc + 64 * s);
+  for (int i = 0; i < 16; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp[i] + kc));
 }
 
 __global__ __launch_bounds__(256) void probe_rows_kernel(const char* __restrict__ src, int64_t waves,
@@ -145,18 +143,18 @@ __global__ __launch_bounds__(256) void probe_rows_kernel(const char* __restrict_
   const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= waves) return;
   const int lane = threadIdx.x & 63;
-  const char* rp[8];
+  const char* rp[16];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) rp[t] = src + (w * 128 + 16 * t + (lane & 15)) * PROBE_ROW_BYTES + 16 * (lane >> 4);
-  u32x4 acc = {0, 0, 0, 0}, v0[8][2], v1[8][2];
+  for (int i = 0; i < 16; ++i) rp[i] = src + (w * 128 + 8 * i + (lane >> 3)) * PROBE_ROW_BYTES + 16 * (lane & 7);
+  u32x4 acc = {0, 0, 0, 0}, v0[16], v1[16];
   probe_rows_chunk(rp, 0, v0);
   for (int kc = 0; kc < PROBE_ROW_BYTES; kc += 256) {
     probe_rows_chunk(rp, kc + 128, v1);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc ^= v0[t][0] ^ v0[t][1];
+    for (int i = 0; i < 16; ++i) acc ^= v0[i];
     if (kc + 256 < PROBE_ROW_BYTES) probe_rows_chunk(rp, kc + 256, v0);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc ^= v1[t][0] ^ v1[t][1];
+    for (int i = 0; i < 16; ++i) acc ^= v1[i];
   }
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
