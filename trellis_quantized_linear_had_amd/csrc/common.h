@@ -27,12 +27,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 __device__ __forceinline__ uint32_t buffer_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff_bytes, uint32_t soff_bytes) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff_bytes, soff_bytes, 0);
 }
-// The same, non-temporal (cache policy bit 1): for streams read once in whole
-// 128-byte lines, which then bypass cache allocation.
-__device__ __forceinline__ uint32_t buffer_load_u32_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff_bytes,
-                                                       uint32_t soff_bytes) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff_bytes, soff_bytes, 2);
-}
 
 __device__ __forceinline__ float bits_lo_f16(uint32_t w) {
   return (float)__builtin_bit_cast(f16, (uint16_t)(w & 0xFFFFu));

@@ -35,6 +35,12 @@ struct DecWidth {
   static constexpr int kWords = BITS == 4 ? 1 : TrellisWidth<BITS>::words(8, 8);
 };
 
+// An ordinary 32-bit buffer load with cache policy bit 1 set: non-temporal.
+__device__ __forceinline__ uint32_t buffer_load_u32_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff_bytes,
+                                                       uint32_t soff_bytes) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff_bytes, soff_bytes, 2);
+}
+
 // Loads the code words of NT tiles of one k-step, NW per lane. The tile
 // bases are wave-uniform (scalar registers); each lane adds a 32-bit offset
 // (its k-tile row and word). With 8 or more tiles per wave the loads are
